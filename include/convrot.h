@@ -1,0 +1,233 @@
+/*
+ * convrot.h -- C ABI of libconvrot.so: the ConvRot W8A8 INT8 linear layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (what every entry point computes):
+ *   - Linear layers of the INT8 package are W8A8: INT8 activations times INT8
+ *     weights, placed behind a block-diagonal Hadamard rotation (lehuy.net
+ *     article on HyperFlow H3 Flash, "Cach nen hoat dong", second bullet).
+ *   - The activation row is rotated and then quantised row-wise to INT8 right
+ *     in front of the projection (MiniMax-H3-Rung-Omega README, "Technical
+ *     Architecture Overview", Floor 1, where rotation and rowwise quantise are
+ *     fused ahead of MLP.fc2).
+ *   - Weights are stored pre-rotated as INT8 codes with one F32 scale per
+ *     output channel, source layout [output, input], and an exact transpose
+ *     [input, output] exists (PulpCut MiniMax H3 INT8 ConvRot input-major
+ *     README, "Input-major checkpoint").  Dequantising and undoing the
+ *     rotation recovers the weights (HyperFlow H3 Flash MLX card, "Where the
+ *     weights come from"), so the stored codes approximate W . R^T with R
+ *     orthogonal.
+ *   - Low-rank factorised linears sit beside the INT8 ones, with ranks padded
+ *     to a multiple of 64 (HyperFlow H3 Flash card, "Choose a Weight Format"
+ *     and "Standalone Transformer (AutoModel)").
+ *
+ * Arithmetic fixed by this library (readings where the pages are silent):
+ *   R = blockdiag(H_b) / sqrt(b), H_b the Sylvester Hadamard in natural order
+ *   (H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]]), b in {64, 128, 256}.
+ *   Rotation: fp32 butterflies with strides h = 1, 2, 4, ..., b/2 in that
+ *   order (bf16 inputs widen exactly).
+ *   Row quantise: amax = max|v|; codes = rint(v * (127/amax)) in [-127, 127]
+ *   (fp32, correctly rounded division, round half to even); scale =
+ *   (amax/127) * fp32(1/sqrt(b)).  A zero row gives codes 0 and scale 0.
+ *   Contraction: exact int32 acc = sum_k qx[m,k] * qw[n,k].
+ *   Epilogue: y = ((float)acc * s_x[m]) * s_w[n], then y += bias[n]; no fused
+ *   multiply-add; bf16 outputs round to nearest even.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.  It is re-entrant:
+ *     calls on different streams may overlap if they use separate workspaces.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous on that stream; the host never synchronises.
+ *   - Matrices are row-major and dense.  bf16 tensors hold raw bfloat16 bits.
+ *     Every pointer must be 16-byte aligned.
+ *   - Arguments are validated before anything is launched.  A call that
+ *     returns an error has launched nothing and written nothing.  Device
+ *     faults surface at the caller's next synchronisation.
+ *   - Non-finite inputs give unspecified (but memory-safe) results.
+ *   - Shape limits: K % 128 == 0, N % 16 == 0, K <= 65536, M*K < 2^31,
+ *     N*K < 2^31 (EUNSUPPORTED otherwise).  M == 0 is a no-op returning OK.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ */
+/* status codes, dtypes, layouts                                       */
+/* ------------------------------------------------------------------ */
+
+typedef enum convrot_status {
+    CONVROT_OK = 0,
+    CONVROT_EINVAL = -1,       /* null pointer, bad shape, K % b != 0, bad b */
+    CONVROT_EALIGN = -2,       /* a pointer is not 16-byte aligned */
+    CONVROT_EWORKSPACE = -3,   /* workspace NULL or smaller than the query */
+    CONVROT_ELAYOUT = -4,      /* weight descriptor magic/version/shape mismatch */
+    CONVROT_EUNSUPPORTED = -5, /* outside the shape limits, or dtype combination */
+    CONVROT_EHIP = -6          /* a HIP launch failed; see convrot_last_hip_error */
+} convrot_status;
+
+typedef enum convrot_dtype {
+    CONVROT_F32 = 0,
+    CONVROT_BF16 = 1,
+    CONVROT_I8 = 2,
+    CONVROT_I32 = 3
+} convrot_dtype;
+
+typedef enum convrot_layout {
+    CONVROT_OUT_MAJOR = 0,     /* W stored [N, K]: [output, input] */
+    CONVROT_IN_MAJOR = 1       /* W stored [K, N]: [input, output] */
+} convrot_layout;
+
+#define CONVROT_WEIGHTS_MAGIC 0x38545243u /* "CRT8" little-endian */
+#define CONVROT_WEIGHTS_VERSION 1u
+
+/* Prepared (pre-rotated, quantised, packed) weights of one linear layer.
+ * A host struct holding caller-owned device pointers.  `codes` and `scale`
+ * must be allocated by the caller before convrot_linear_prepare_weights
+ * (sizes: convrot_weights_packed_bytes(N, K, block) and 4*N bytes); the
+ * prepare call fills every other field.  The packed code layout is private to
+ * this library and tagged by magic/version: forward calls reject a descriptor
+ * whose tag does not match (CONVROT_ELAYOUT), the way a runtime validates a
+ * versioned layout marker before building its pipeline (PulpCut input-major
+ * README, "Input-major checkpoint"). */
+typedef struct convrot_weights {
+    uint32_t magic;            /* CONVROT_WEIGHTS_MAGIC once prepared */
+    uint32_t version;          /* CONVROT_WEIGHTS_VERSION */
+    int64_t N;                 /* output channels */
+    int64_t K;                 /* input channels */
+    int32_t block;             /* Hadamard block b the codes were rotated with */
+    int32_t flags;             /* reserved, 0 */
+    int8_t *codes;             /* device, packed INT8 codes of W . R^T */
+    float *scale;              /* device, [N] per-output F32 scales */
+} convrot_weights;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *convrot_status_string(int status);
+
+/* The hipError_t of the most recent CONVROT_EHIP on this thread (0 if none). */
+int convrot_last_hip_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int convrot_version(void);
+
+/* ------------------------------------------------------------------ */
+/* sizing queries (host only, no HIP calls)                            */
+/* ------------------------------------------------------------------ */
+
+/* Bytes of packed codes for an [N, K] weight (0 for invalid shapes). */
+size_t convrot_weights_packed_bytes(int64_t N, int64_t K, int block);
+
+/* Workspace for convrot_linear_prepare_weights (0 is a valid answer). */
+size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block,
+                                       int w_dtype, int layout);
+
+/* Workspace for convrot_linear_forward: INT8 codes [M, K] and F32 row scales
+ * [M] of the rotated activations, each region 256-byte aligned. */
+size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block);
+
+/* Workspace for lowrank_convrot_forward (codes of X, bf16 intermediate
+ * H [M, r], codes of H, and row scales). */
+size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r,
+                                       int64_t N, int block);
+
+/* Workspace for convrot_mlp_forward (codes of X, bf16 activation g [M, F],
+ * codes of g, row scales). */
+size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
+                                   int block);
+
+/* ------------------------------------------------------------------ */
+/* weight preparation (load time)                                      */
+/* ------------------------------------------------------------------ */
+
+/* Rotate, quantise and pack one weight matrix.
+ *   W         device; F32 or BF16 float weights, or I8 codes that are already
+ *             rotated (import mode).  Layout per `layout`:
+ *             CONVROT_OUT_MAJOR -> [N, K], CONVROT_IN_MAJOR -> [K, N].
+ *   src_scale I8 import only: device [N] per-output scales, copied unchanged;
+ *             must be NULL for float weights.
+ *   block     Hadamard block b in {64, 128, 256}; K % block == 0.
+ *   out       host struct; out->codes and out->scale must point to caller
+ *             allocations of convrot_weights_packed_bytes(N, K, block) and 4*N
+ *             bytes.  On success every other field is filled in.
+ *   ws        device workspace of convrot_prepare_workspace_bytes(...) bytes
+ *             (may be NULL when that query returns 0).
+ * Float weights: row n of W becomes codes/scale of FWHT_b(W[n, :]) quantised
+ * per output channel, i.e. the INT8 image of W . R^T.  Import mode copies the
+ * codes (transposing IN_MAJOR input) and scales without changing any value,
+ * as the input-major repack does. */
+int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
+                                   const float *src_scale, int64_t N, int64_t K,
+                                   int block, convrot_weights *out, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* forward entry points                                                */
+/* ------------------------------------------------------------------ */
+
+/* Y = dequant(Q(R x) . Q(W R^T)^T) (+ bias) for every row x of X.
+ *   X       device bf16 [M, W->K] activations.
+ *   W       prepared weights (host struct).
+ *   bias    device F32 [W->N] or NULL.
+ *   Y       device [M, W->N], y_dtype CONVROT_BF16 or CONVROT_F32.
+ *   ws      device workspace of convrot_linear_workspace_bytes(M, K, N, b).
+ * Rows are independent: forward on a row slice equals the same slice of the
+ * full forward, bit for bit. */
+int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
+                           const float *bias, void *Y, int y_dtype, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* Low-rank ConvRot linear: h = bf16(linear(X; A)) with A [r, K] and no bias,
+ * then Y = linear(h; B) with B [N, r] and the bias; h is re-rotated along r
+ * with the same block and requantised per token.  Requires A->N == B->K (= r),
+ * A->block == B->block and r % 128 == 0 (pad the rank with zero rows of A and
+ * zero columns of B, which leaves the product unchanged). */
+int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
+                            const convrot_weights *B, const float *bias,
+                            void *Y, int y_dtype, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* MLP pair: u = bf16(linear(X; W_up) + bias_up); g = bf16(GELU(u)) with the
+ * erf form of GELU evaluated in fp32; Y = linear(g; W_down) + bias_down.
+ * Requires W_up->N == W_down->K (= F).  GELU is applied in the epilogue of the
+ * up projection, so u is never written. */
+int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
+                        const float *bias_up, const convrot_weights *W_down,
+                        const float *bias_down, void *Y, int y_dtype, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* test hooks: the stages of the forward path, exported for parity     */
+/* tests.  Same validation and error behaviour as the entry points.    */
+/* ------------------------------------------------------------------ */
+
+/* Rotate and quantise rows: X [M, K] (x_dtype F32 or BF16) -> q [M, K] int8
+ * and s [M] F32.  flags must be 0. */
+int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K,
+                            int block, uint32_t flags, int8_t *q, float *s,
+                            void *stream);
+
+/* Exact INT32 contraction acc[M, N] = q_x [M, K] . codes(W)^T. */
+int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W,
+                     int32_t *acc, void *stream);
+
+/* Contraction plus the dequant epilogue from given codes and row scales:
+ * Y = ((float)(q_x . codes(W)^T) * s_x) * s_w (+ bias).  With
+ * CONVROT_FLAG_GELU (y_dtype must be BF16) the epilogue writes
+ * bf16(GELU(float(bf16(Y)))), the activation the MLP entry point feeds to its
+ * down projection. */
+#define CONVROT_FLAG_GELU 1u
+int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
+                         const convrot_weights *W, const float *bias, void *Y,
+                         int y_dtype, uint32_t flags, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

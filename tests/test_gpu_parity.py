@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path (called through the C ABI) against the CPU oracle
+on the same seeded inputs.  Codes, scales and INT32 accumulators must match
+bit for bit; outputs within the normwise tolerances of gpu_util."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w8a8_int8_rotated_amd import workloads as wl
+from gpu_util import (announce, assert_output_parity, bf16_bits, host, sample_rows,
+                      to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cr():
+    from w8a8_int8_rotated_amd import convrot
+    convrot.library()
+    return convrot
+
+
+def _x(M, K, seed=0, outliers=0, gain=1.0, dist="normal"):
+    w = wl.Workload("t", "linear", M=M, K=K, N=16, block=128, out="bf16", x_dist=dist,
+                    outlier_count=outliers, outlier_gain=gain, seed=seed)
+    return w.activations()
+
+
+# ------------------------------------------------------------ rotquant ----
+
+@pytest.mark.parametrize("b", [64, 128, 256])
+@pytest.mark.parametrize("M,K", [(1, 512), (37, 512), (300, 5376), (5, 21504), (9, 1024),
+                                 (3, 2560), (2, 65536), (130, 768)])
+def test_rotquant_codes_bitexact(cr, b, M, K):
+    if K % b:
+        pytest.skip("K not a multiple of b")
+    announce(f"rotquant b={b} M={M} K={K}")
+    x = _x(M, K, seed=M + K, outliers=3, gain=30.0)
+    q, s = cr.convrot_rotate_quantize(to_dev_bf16(x), b)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.rotate_quantize(x, b, "bf16")
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(s), s_ref)
+
+
+@pytest.mark.parametrize("b", [64, 128, 256])
+def test_rotquant_f32_rows_bitexact(cr, b):
+    announce(f"rotquant f32 b={b}")
+    rng = np.random.default_rng(b)
+    W = (rng.standard_normal((200, 1536)) * 0.02).astype(np.float32)
+    W[7] = 0.0                                   # zero row
+    W[9, 100] = 5.0                              # lone spike
+    q, s = cr.convrot_rotate_quantize(to_dev(W), b)
+    q_ref, s_ref = oracle.rotate_quantize(W, b, "f32")
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(s), s_ref)
+    assert not host(q)[7].any() and host(s)[7] == 0
+
+
+def test_rotquant_special_rows(cr):
+    """Zero rows, one-hot rows, rows of equal magnitude, a heavy outlier."""
+    announce("rotquant special rows")
+    K = 5376
+    x = np.zeros((6, K), np.float32)
+    x[1, 77] = 1.0
+    x[2] = 1.0
+    x[3, :] = -2.5
+    x[4] = np.random.default_rng(1).standard_normal(K)
+    x[4, 1000] = 2.0e5
+    x[5, ::2] = 3.0
+    xb = wl.f32_to_bf16_bits(x)
+    q, s = cr.convrot_rotate_quantize(to_dev_bf16(xb), 128)
+    q_ref, s_ref = oracle.rotate_quantize(xb, 128, "bf16")
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(s), s_ref)
+
+
+# -------------------------------------------------------- weight prep ----
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["out_major", "in_major"])
+def test_prepare_weights_bitexact(cr, dtype, layout):
+    announce(f"prepare {dtype} {layout}")
+    rng = np.random.default_rng(3)
+    N, K, b = 272, 1024, 128
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    src = W if dtype == "f32" else wl.f32_to_bf16_bits(W)
+    if layout == "in_major":
+        src = np.ascontiguousarray(src.T)
+    t = to_dev(src) if dtype == "f32" else to_dev_bf16(src)
+    pw = cr.convrot_linear_prepare_weights(t, b, cr.IN_MAJOR if layout == "in_major" else cr.OUT_MAJOR)
+    q_ref, s_ref = oracle.prepare_weights(src, b, dtype=dtype, layout=layout)
+    assert np.array_equal(host(pw.codes).reshape(N, K), q_ref)
+    assert np.array_equal(host(pw.scale), s_ref)
+
+
+@pytest.mark.parametrize("layout", ["out_major", "in_major"])
+def test_prepare_import_int8_unchanged(cr, layout):
+    """Import mode copies codes and scales without changing a value."""
+    announce(f"prepare import {layout}")
+    rng = np.random.default_rng(4)
+    N, K = 48, 512
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    s = rng.uniform(1e-4, 1e-2, N).astype(np.float32)
+    src = q if layout == "out_major" else np.ascontiguousarray(q.T)
+    pw = cr.convrot_linear_prepare_weights(
+        to_dev(src), 128, cr.IN_MAJOR if layout == "in_major" else cr.OUT_MAJOR,
+        src_scale=to_dev(s))
+    assert np.array_equal(host(pw.codes).reshape(N, K), q)
+    assert np.array_equal(host(pw.scale), s)
+
+
+# ---------------------------------------------------------- GEMM INT32 ----
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 272, 384), (1, 16, 512),
+                                   (513, 528, 1024), (64, 784, 5376), (257, 1040, 256)])
+def test_gemm_i32_bitexact(cr, M, N, K):
+    announce(f"gemm_i32 M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 7 + N)
+    qx = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    qx[0] = 127
+    qw[0] = -127                                 # extreme accumulator
+    pw = cr.convrot_linear_prepare_weights(to_dev(qw), 128, src_scale=to_dev(
+        np.ones(N, np.float32)))
+    acc = cr.convrot_gemm_i32(to_dev(qx), pw)
+    ref = oracle.gemm_i32(qx, qw)
+    assert np.array_equal(host(acc), ref)
+
+
+# ----------------------------------------------------- whole linear ----
+
+def _prepare_pair(cr, W, b):
+    pw = cr.convrot_linear_prepare_weights(to_dev(W), b)
+    q_ref, s_ref = oracle.prepare_weights(W, b)
+    assert np.array_equal(host(pw.codes).reshape(q_ref.shape), q_ref)
+    assert np.array_equal(host(pw.scale), s_ref)
+    return pw, q_ref, s_ref
+
+
+def test_linear_tiny_config(cr):
+    """The tiny workload (M=256, K=512, N=512, b=128, fp32 out): codes, INT32
+    accumulators and outputs, all rows."""
+    w = wl.WORKLOADS["tiny"]
+    announce(w.description)
+    x, W = w.activations(), w.weight()
+    pw, qw, sw = _prepare_pair(cr, W, w.block)
+    X = to_dev_bf16(x)
+    y = cr.convrot_linear_forward(X, pw, out_dtype=torch.float32)
+    qx, sx = cr.convrot_rotate_quantize(X, w.block)
+    acc = cr.convrot_gemm_i32(qx, pw)
+    qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
+    assert np.array_equal(host(qx), qx_ref) and np.array_equal(host(sx), sx_ref)
+    assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref, qw))
+    y_ref = oracle.linear_forward(x, qw, sw, w.block, out="f32")
+    mism = assert_output_parity(host(y), y_ref, "f32", "tiny fp32")
+    assert mism == 0
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_ragged_shapes(cr, out, with_bias):
+    """Ragged M and N (several tiles and partial ones), bias on and off."""
+    M, K, N, b = 600, 1280, 784, 128
+    announce(f"linear ragged M={M} K={K} N={N} out={out} bias={with_bias}")
+    w = wl.Workload("r", "linear", M=M, K=K, N=N, block=b, out=out, x_dist="normal",
+                    outlier_frac=0.01, outlier_gain=30, bias_std=0.01 if with_bias else None,
+                    seed=11)
+    x, W, bias = w.activations(), w.weight(), w.bias()
+    pw, qw, sw = _prepare_pair(cr, W, b)
+    y = cr.convrot_linear_forward(to_dev_bf16(x), pw,
+                                  bias=None if bias is None else to_dev(bias),
+                                  out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    y_ref = oracle.linear_forward(x, qw, sw, b, bias=bias, out=out)
+    yh = host(y) if out == "f32" else bf16_bits(y)
+    mism = assert_output_parity(yh, y_ref, out, "ragged")
+    assert mism == 0
+
+
+def test_linear_4096_config_sampled(cr):
+    """M=4096, K=N=5376, b=128, bias, bf16 out: codes and scales on every
+    row; outputs on sampled rows (first/last, tile edges, random)."""
+    w = wl.WORKLOADS["linear_4096"]
+    announce(w.description)
+    x, W, bias = w.activations(), w.weight(), w.bias()
+    pw, qw, sw = _prepare_pair(cr, W, w.block)
+    X = to_dev_bf16(x)
+    y = cr.convrot_linear_forward(X, pw, bias=to_dev(bias))
+    qx, sx = cr.convrot_rotate_quantize(X, w.block)
+    qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
+    assert np.array_equal(host(qx), qx_ref) and np.array_equal(host(sx), sx_ref)
+    rows = sample_rows(w.M, 96)
+    y_ref = oracle.linear_forward(x[rows], qw, sw, w.block, bias=bias, out="bf16")
+    mism = assert_output_parity(bf16_bits(y)[rows], y_ref, "bf16", "linear_4096 sampled")
+    assert mism == 0
+    acc = cr.convrot_gemm_i32(qx, pw)
+    assert np.array_equal(host(acc)[rows], oracle.gemm_i32(qx_ref[rows], qw))
+
+
+def test_row_chunk_invariance(cr):
+    """forward(X[a:b]) equals forward(X)[a:b] bit for bit (rows independent)."""
+    announce("row chunk invariance")
+    M, K, N = 700, 1024, 512
+    w = wl.Workload("c", "linear", M=M, K=K, N=N, block=128, out="bf16", x_dist="student_t4",
+                    seed=5)
+    x, W = w.activations(), w.weight()
+    pw = cr.convrot_linear_prepare_weights(to_dev(W), 128)
+    X = to_dev_bf16(x)
+    y = bf16_bits(cr.convrot_linear_forward(X, pw))
+    for a, b_ in [(0, 1), (3, 259), (256, 700), (511, 512)]:
+        ys = bf16_bits(cr.convrot_linear_forward(X[a:b_].contiguous(), pw))
+        assert np.array_equal(ys, y[a:b_])
+
+
+def test_deterministic_and_m0(cr):
+    announce("determinism and M=0")
+    w = wl.scaled("tiny", M=300)
+    x, W = w.activations(), w.weight()
+    pw = cr.convrot_linear_prepare_weights(to_dev(W), 128)
+    X = to_dev_bf16(x)
+    y1 = host(cr.convrot_linear_forward(X, pw, out_dtype=torch.float32))
+    y2 = host(cr.convrot_linear_forward(X, pw, out_dtype=torch.float32))
+    assert np.array_equal(y1, y2)
+    empty = torch.empty((0, w.K), dtype=torch.bfloat16, device="cuda")
+    out = cr.convrot_linear_forward(empty, pw)
+    assert out.shape == (0, w.N)
+
+
+def test_output_guard_band(cr):
+    """Nothing is written outside Y: a canary pattern around the output stays."""
+    announce("guard band")
+    M, K, N = 300, 512, 272
+    w = wl.Workload("g", "linear", M=M, K=K, N=N, block=128, out="bf16", x_dist="normal", seed=2)
+    pw = cr.convrot_linear_prepare_weights(to_dev(w.weight()), 128)
+    pad = 4096
+    buf = torch.full((pad + M * N + pad,), -7, dtype=torch.int16, device="cuda")
+    y = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    cr.convrot_linear_forward(to_dev_bf16(w.activations()), pw, out=y)
+    b = host(buf)
+    assert (b[:pad] == -7).all() and (b[pad + M * N:] == -7).all()
+
+
+# ----------------------------------------------------------- low-rank ----
+
+def test_lowrank_small_full(cr):
+    announce("lowrank small")
+    w = wl.scaled("lowrank_38656", M=520, K=1024, N=784, rank=256)
+    x, A, B = w.activations(), w.weight("w"), w.weight("w2")
+    bias = np.random.default_rng(0).normal(0, 0.01, w.N).astype(np.float32)
+    pa, qa, sa = _prepare_pair(cr, A, w.block)
+    pb, qb, sb = _prepare_pair(cr, B, w.block)
+    y = cr.lowrank_convrot_forward(to_dev_bf16(x), pa, pb, bias=to_dev(bias))
+    y_ref = oracle.lowrank_forward(x, qa, sa, qb, sb, w.block, bias=bias, out="bf16")
+    mism = assert_output_parity(bf16_bits(y), y_ref, "bf16", "lowrank small")
+    assert mism == 0
+
+
+# ---------------------------------------------------------------- MLP ----
+
+def test_mlp_small(cr):
+    """MLP pair with GELU: g within one bf16 ulp of the oracle's (GELU differs
+    between fp32 erff and fp64 erf in the last bit of rare ties), output within
+    the bf16 tolerance."""
+    announce("mlp small")
+    w = wl.scaled("mlp_16384", M=300, K=1024, N=512, ffn=2048)
+    x, Wu, Wd = w.activations(), w.weight("w"), w.weight("w2")
+    pu, qu, su = _prepare_pair(cr, Wu, w.block)
+    pd, qd, sd = _prepare_pair(cr, Wd, w.block)
+    y = cr.convrot_mlp_forward(to_dev_bf16(x), pu, pd)
+    y_ref, u_ref, g_ref = oracle.mlp_forward(x, qu, su, qd, sd, w.block, out="bf16",
+                                             return_intermediates=True)
+    # g from the GPU's up projection with the GELU epilogue, vs the oracle's g
+    qx, sx = cr.convrot_rotate_quantize(to_dev_bf16(x), w.block)
+    gb = bf16_bits(cr.convrot_gemm_dequant(qx, sx, pu, gelu=True))
+    diff = np.abs(gb.astype(np.int32) - g_ref.astype(np.int32))
+    print(f"[parity] mlp g: {np.count_nonzero(diff)} of {diff.size} differ, "
+          f"max {diff.max()} ulp", flush=True)
+    assert diff.max() <= 1
+    # u itself is bit-exact (plain bf16 epilogue)
+    ub = bf16_bits(cr.convrot_gemm_dequant(qx, sx, pu))
+    assert np.array_equal(ub, u_ref)
+    assert_output_parity(bf16_bits(y), y_ref, "bf16", "mlp small")

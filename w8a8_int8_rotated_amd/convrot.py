@@ -1,0 +1,300 @@
+"""Python binding of libconvrot (the C ABI in include/convrot.h).
+
+Argument marshalling only: PyTorch provides device memory and the current HIP
+stream; every step of the forward path runs in the library's HIP kernels.
+The functions carry the C names.  If the library has not been built the first
+call raises -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconvrot.so")
+
+OK, EINVAL, EALIGN, EWORKSPACE, ELAYOUT, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16, I8, I32 = 0, 1, 2, 3
+OUT_MAJOR, IN_MAJOR = 0, 1
+WEIGHTS_MAGIC = 0x38545243
+WEIGHTS_VERSION = 1
+FLAG_GELU = 1
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_p = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+
+class convrot_weights(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("version", ctypes.c_uint32),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+    ]
+
+
+_W = ctypes.POINTER(convrot_weights)
+
+_SIGNATURES = {
+    "convrot_status_string": (ctypes.c_char_p, [_c_int]),
+    "convrot_last_hip_error": (_c_int, []),
+    "convrot_version": (_c_int, []),
+    "convrot_weights_packed_bytes": (_c_sz, [_c_i64, _c_i64, _c_int]),
+    "convrot_prepare_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_int, _c_int, _c_int]),
+    "convrot_linear_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "lowrank_convrot_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
+    "convrot_mlp_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
+    "convrot_linear_prepare_weights": (
+        _c_int, [_c_p, _c_int, _c_int, _c_p, _c_i64, _c_i64, _c_int, _W, _c_p, _c_sz, _c_p]),
+    "convrot_linear_forward": (
+        _c_int, [_c_p, _c_i64, _W, _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "lowrank_convrot_forward": (
+        _c_int, [_c_p, _c_i64, _W, _W, _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "convrot_mlp_forward": (
+        _c_int, [_c_p, _c_i64, _W, _c_p, _W, _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "convrot_rotate_quantize": (
+        _c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_int, ctypes.c_uint32, _c_p, _c_p, _c_p]),
+    "convrot_gemm_i32": (_c_int, [_c_p, _c_i64, _W, _c_p, _c_p]),
+    "convrot_gemm_dequant": (
+        _c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_int, ctypes.c_uint32, _c_p]),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class ConvRotError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = library()
+        msg = lib.convrot_status_string(status).decode()
+        extra = ""
+        if status == EHIP:
+            extra = f" (hipError {lib.convrot_last_hip_error()})"
+        super().__init__(f"{fn} failed: {msg} [{status}]{extra}")
+        self.status = status
+
+
+def library():
+    """Load libconvrot.so (built in-tree by ``w8a8_int8_rotated_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m w8a8_int8_rotated_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != OK:
+        raise ConvRotError(fn, rc)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_tag(dt: torch.dtype) -> int:
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32}[dt]
+
+
+def _torch_dtype(tag: int) -> torch.dtype:
+    return {F32: torch.float32, BF16: torch.bfloat16}[tag]
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------- sizing ----
+
+def convrot_weights_packed_bytes(N: int, K: int, block: int) -> int:
+    return library().convrot_weights_packed_bytes(N, K, block)
+
+
+def convrot_prepare_workspace_bytes(N, K, block, w_dtype, layout) -> int:
+    return library().convrot_prepare_workspace_bytes(N, K, block, w_dtype, layout)
+
+
+def convrot_linear_workspace_bytes(M, K, N, block) -> int:
+    return library().convrot_linear_workspace_bytes(M, K, N, block)
+
+
+def lowrank_convrot_workspace_bytes(M, K, r, N, block) -> int:
+    return library().lowrank_convrot_workspace_bytes(M, K, r, N, block)
+
+
+def convrot_mlp_workspace_bytes(M, K, F, N, block) -> int:
+    return library().convrot_mlp_workspace_bytes(M, K, F, N, block)
+
+
+# ----------------------------------------------------------- weights ----
+
+class PreparedWeights:
+    """A prepared weight: the C descriptor plus the tensors it points into."""
+
+    def __init__(self, desc: convrot_weights, codes: torch.Tensor, scale: torch.Tensor):
+        self.desc = desc
+        self.codes = codes
+        self.scale = scale
+
+    @property
+    def N(self):
+        return self.desc.N
+
+    @property
+    def K(self):
+        return self.desc.K
+
+    @property
+    def block(self):
+        return self.desc.block
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def convrot_linear_prepare_weights(W: torch.Tensor, block: int, layout: int = OUT_MAJOR,
+                                   src_scale: torch.Tensor | None = None,
+                                   stream=None) -> PreparedWeights:
+    """Rotate + quantise + pack a weight (``[N, K]`` or ``[K, N]`` per layout)."""
+    lib = library()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    if layout == OUT_MAJOR:
+        N, K = W.shape
+    else:
+        K, N = W.shape
+    W = W.contiguous()
+    tag = _dtype_tag(W.dtype)
+    nbytes = lib.convrot_weights_packed_bytes(N, K, block)
+    if nbytes == 0:
+        raise ConvRotError("convrot_linear_prepare_weights", EUNSUPPORTED)
+    codes = torch.empty(nbytes, dtype=torch.int8, device=W.device)
+    scale = torch.empty(N, dtype=torch.float32, device=W.device)
+    desc = convrot_weights()
+    desc.codes = codes.data_ptr()
+    desc.scale = scale.data_ptr()
+    wsb = lib.convrot_prepare_workspace_bytes(N, K, block, tag, layout)
+    ws = _workspace(wsb, W.device, None)
+    rc = lib.convrot_linear_prepare_weights(
+        _ptr(W), tag, layout, _ptr(src_scale), N, K, block, ctypes.byref(desc), _ptr(ws),
+        wsb, _stream(stream))
+    _check("convrot_linear_prepare_weights", rc)
+    pw = PreparedWeights(desc, codes, scale)
+    pw._ws = ws  # keep alive until the stream has consumed it
+    return pw
+
+
+# ----------------------------------------------------------- forward ----
+
+def convrot_linear_forward(X: torch.Tensor, W: PreparedWeights, bias=None,
+                           out_dtype: torch.dtype = torch.bfloat16, out=None,
+                           workspace=None, stream=None) -> torch.Tensor:
+    lib = library()
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, W.N), dtype=out_dtype, device=X.device)
+    wsb = lib.convrot_linear_workspace_bytes(M, W.K, W.N, W.block)
+    ws = _workspace(wsb, X.device, workspace)
+    rc = lib.convrot_linear_forward(_ptr(X), M, W.ref(), _ptr(bias), _ptr(out),
+                                    _dtype_tag(out.dtype), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream(stream))
+    _check("convrot_linear_forward", rc)
+    return out
+
+
+def lowrank_convrot_forward(X: torch.Tensor, A: PreparedWeights, B: PreparedWeights,
+                            bias=None, out_dtype: torch.dtype = torch.bfloat16, out=None,
+                            workspace=None, stream=None) -> torch.Tensor:
+    lib = library()
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, B.N), dtype=out_dtype, device=X.device)
+    wsb = lib.lowrank_convrot_workspace_bytes(M, A.K, A.N, B.N, A.block)
+    ws = _workspace(wsb, X.device, workspace)
+    rc = lib.lowrank_convrot_forward(_ptr(X), M, A.ref(), B.ref(), _ptr(bias), _ptr(out),
+                                     _dtype_tag(out.dtype), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream))
+    _check("lowrank_convrot_forward", rc)
+    return out
+
+
+def convrot_mlp_forward(X: torch.Tensor, W_up: PreparedWeights, W_down: PreparedWeights,
+                        bias_up=None, bias_down=None, out_dtype: torch.dtype = torch.bfloat16,
+                        out=None, workspace=None, stream=None) -> torch.Tensor:
+    lib = library()
+    M = X.shape[0]
+    if out is None:
+        out = torch.empty((M, W_down.N), dtype=out_dtype, device=X.device)
+    wsb = lib.convrot_mlp_workspace_bytes(M, W_up.K, W_up.N, W_down.N, W_up.block)
+    ws = _workspace(wsb, X.device, workspace)
+    rc = lib.convrot_mlp_forward(_ptr(X), M, W_up.ref(), _ptr(bias_up), W_down.ref(),
+                                 _ptr(bias_down), _ptr(out), _dtype_tag(out.dtype), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream))
+    _check("convrot_mlp_forward", rc)
+    return out
+
+
+# ------------------------------------------------------------- hooks ----
+
+def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=None):
+    lib = library()
+    M, K = X.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if s is None:
+        s = torch.empty(M, dtype=torch.float32, device=X.device)
+    rc = lib.convrot_rotate_quantize(_ptr(X), _dtype_tag(X.dtype), M, K, block, 0, _ptr(q),
+                                     _ptr(s), _stream(stream))
+    _check("convrot_rotate_quantize", rc)
+    return q, s
+
+
+def convrot_gemm_i32(q_x: torch.Tensor, W: PreparedWeights, out=None, stream=None):
+    lib = library()
+    M = q_x.shape[0]
+    if out is None:
+        out = torch.empty((M, W.N), dtype=torch.int32, device=q_x.device)
+    rc = lib.convrot_gemm_i32(_ptr(q_x), M, W.ref(), _ptr(out), _stream(stream))
+    _check("convrot_gemm_i32", rc)
+    return out
+
+
+def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeights, bias=None,
+                         out_dtype: torch.dtype = torch.bfloat16, out=None, gelu: bool = False,
+                         stream=None):
+    lib = library()
+    M = q_x.shape[0]
+    if out is None:
+        out = torch.empty((M, W.N), dtype=out_dtype, device=q_x.device)
+    rc = lib.convrot_gemm_dequant(_ptr(q_x), _ptr(s_x), M, W.ref(), _ptr(bias), _ptr(out),
+                                  _dtype_tag(out.dtype), FLAG_GELU if gelu else 0,
+                                  _stream(stream))
+    _check("convrot_gemm_dequant", rc)
+    return out

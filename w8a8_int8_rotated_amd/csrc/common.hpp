@@ -1,0 +1,64 @@
+// Shared device helpers and launch declarations of libconvrot (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+// ---------------------------------------------------------------- bf16 ----
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the binary32.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// GELU, erf form, evaluated in fp32.
+__device__ __forceinline__ float gelu_erf(float z)
+{
+    const float k = 0.70710678118654752440f;
+    float e = erff(__fmul_rn(z, k));
+    return __fmul_rn(__fmul_rn(0.5f, z), __fadd_rn(1.0f, e));
+}
+
+} // namespace convrot
+
+// ------------------------------------------------------ kernel launchers ----
+// All launchers assume arguments were validated by the API layer.
+
+namespace convrot {
+
+enum class InType { F32 = 0, BF16 = 1 };
+enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3 };
+
+// Rotate (blockwise FWHT) + rowwise INT8 quantise.  src rows have stride ld
+// elements; q rows have stride K bytes.
+hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
+                           int64_t ld, int block, float inv_sqrt_b, int8_t *q,
+                           float *s, hipStream_t stream);
+
+// Transpose an [R, C] matrix of 1-, 2- or 4-byte elements into [C, R].
+hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
+                            int elem_bytes, hipStream_t stream);
+
+// acc/Y[M, N] = epilogue(qx[M, K] . qw[N, K]^T).
+hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
+                          const float *sw, const float *bias, void *Y,
+                          OutKind out, int64_t M, int64_t N, int64_t K,
+                          hipStream_t stream);
+
+} // namespace convrot

@@ -1,0 +1,372 @@
+// C ABI of libconvrot: argument validation, workspace carving and launch
+// sequencing.  Every check runs on the host before any launch; a call that
+// fails validation launches nothing.
+#include "convrot.h"
+#include "common.hpp"
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstdio>
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;
+constexpr int64_t kI32Bound = (int64_t)1 << 31;
+constexpr size_t kAlign = 256;
+
+thread_local int g_last_hip_error = 0;
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *e = std::getenv("CONVROT_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_block(int b) { return b == 64 || b == 128 || b == 256; }
+
+// fp32 1/sqrt(b), rounded once from double.
+float inv_sqrt_block(int b) { return (float)(1.0 / std::sqrt((double)b)); }
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return CONVROT_OK;
+    g_last_hip_error = (int)e;
+    if (log_enabled())
+        std::fprintf(stderr, "[convrot] HIP error %d: %s\n", (int)e, hipGetErrorString(e));
+    return CONVROT_EHIP;
+}
+
+// Shape rules shared by every projection (K inputs, N outputs, block b).
+int check_linear_shape(int64_t N, int64_t K, int block)
+{
+    if (N <= 0 || K <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
+    if (K % 128 != 0 || N % 16 != 0 || K > kMaxK || N * K >= kI32Bound)
+        return CONVROT_EUNSUPPORTED;
+    return CONVROT_OK;
+}
+
+int check_weights(const convrot_weights *W)
+{
+    if (!W) return CONVROT_EINVAL;
+    if (W->magic != CONVROT_WEIGHTS_MAGIC || W->version != CONVROT_WEIGHTS_VERSION)
+        return CONVROT_ELAYOUT;
+    if (!W->codes || !W->scale) return CONVROT_EINVAL;
+    if (!aligned16(W->codes) || !aligned16(W->scale)) return CONVROT_EALIGN;
+    int rc = check_linear_shape(W->N, W->K, W->block);
+    return rc == CONVROT_EINVAL ? CONVROT_ELAYOUT : rc;
+}
+
+int check_rows(int64_t M, int64_t K)
+{
+    if (M < 0) return CONVROT_EINVAL;
+    if (M * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    return CONVROT_OK;
+}
+
+int check_out_dtype(int y_dtype)
+{
+    return (y_dtype == CONVROT_BF16 || y_dtype == CONVROT_F32) ? CONVROT_OK : CONVROT_EUNSUPPORTED;
+}
+
+convrot::OutKind out_kind(int y_dtype)
+{
+    return y_dtype == CONVROT_F32 ? convrot::OutKind::F32 : convrot::OutKind::BF16;
+}
+
+// Bump allocator over a caller workspace.
+struct Carve {
+    char *base;
+    size_t used = 0;
+    explicit Carve(void *p) : base(static_cast<char *>(p)) {}
+    void *take(size_t bytes)
+    {
+        void *p = base ? base + used : nullptr;
+        used += round_up(bytes, kAlign);
+        return p;
+    }
+};
+
+size_t codes_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)K, kAlign); }
+size_t scales_bytes(int64_t M) { return round_up((size_t)M * 4u, kAlign); }
+
+} // namespace
+
+extern "C" {
+
+const char *convrot_status_string(int status)
+{
+    switch (status) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_EINVAL: return "invalid argument";
+    case CONVROT_EALIGN: return "pointer not 16-byte aligned";
+    case CONVROT_EWORKSPACE: return "workspace missing or too small";
+    case CONVROT_ELAYOUT: return "weight descriptor layout/version mismatch";
+    case CONVROT_EUNSUPPORTED: return "unsupported shape or dtype";
+    case CONVROT_EHIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int convrot_last_hip_error(void) { return g_last_hip_error; }
+
+int convrot_version(void) { return 100; }
+
+size_t convrot_weights_packed_bytes(int64_t N, int64_t K, int block)
+{
+    if (check_linear_shape(N, K, block) != CONVROT_OK) return 0;
+    return (size_t)N * (size_t)K;
+}
+
+size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block, int w_dtype,
+                                       int layout)
+{
+    if (check_linear_shape(N, K, block) != CONVROT_OK) return 0;
+    if (layout == CONVROT_IN_MAJOR && (w_dtype == CONVROT_F32 || w_dtype == CONVROT_BF16))
+        return round_up((size_t)N * (size_t)K * (w_dtype == CONVROT_F32 ? 4u : 2u), kAlign);
+    return 0;
+}
+
+size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block)
+{
+    if (M < 0 || check_linear_shape(N, K, block) != CONVROT_OK) return 0;
+    return codes_bytes(M, K) + scales_bytes(M);
+}
+
+size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r, int64_t N, int block)
+{
+    if (M < 0 || check_linear_shape(r, K, block) != CONVROT_OK ||
+        check_linear_shape(N, r, block) != CONVROT_OK)
+        return 0;
+    return codes_bytes(M, K) + scales_bytes(M) + round_up((size_t)M * (size_t)r * 2u, kAlign) +
+           codes_bytes(M, r) + scales_bytes(M);
+}
+
+size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N, int block)
+{
+    if (M < 0 || check_linear_shape(F, K, block) != CONVROT_OK ||
+        check_linear_shape(N, F, block) != CONVROT_OK)
+        return 0;
+    return codes_bytes(M, K) + scales_bytes(M) + round_up((size_t)M * (size_t)F * 2u, kAlign) +
+           codes_bytes(M, F) + scales_bytes(M);
+}
+
+int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
+                                   const float *src_scale, int64_t N, int64_t K, int block,
+                                   convrot_weights *out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!W || !out || !out->codes || !out->scale) return CONVROT_EINVAL;
+    int rc = check_linear_shape(N, K, block);
+    if (rc != CONVROT_OK) return rc;
+    if (layout != CONVROT_OUT_MAJOR && layout != CONVROT_IN_MAJOR) return CONVROT_EINVAL;
+    if (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16 && w_dtype != CONVROT_I8)
+        return CONVROT_EUNSUPPORTED;
+    const bool import = (w_dtype == CONVROT_I8);
+    if (import != (src_scale != nullptr)) return CONVROT_EINVAL;
+    if (!aligned16(W) || !aligned16(out->codes) || !aligned16(out->scale) ||
+        (src_scale && !aligned16(src_scale)))
+        return CONVROT_EALIGN;
+    const size_t need = convrot_prepare_workspace_bytes(N, K, block, w_dtype, layout);
+    if (need > 0 && (!ws || ws_bytes < need)) return CONVROT_EWORKSPACE;
+    if (ws && !aligned16(ws)) return CONVROT_EALIGN;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (import) {
+        if (layout == CONVROT_OUT_MAJOR)
+            e = hipMemcpyAsync(out->codes, W, (size_t)N * (size_t)K, hipMemcpyDeviceToDevice, s);
+        else
+            e = convrot::launch_transpose(W, out->codes, K, N, 1, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(out->scale, src_scale, (size_t)N * 4u, hipMemcpyDeviceToDevice, s);
+    } else {
+        const convrot::InType in =
+            (w_dtype == CONVROT_F32) ? convrot::InType::F32 : convrot::InType::BF16;
+        const void *rows = W;
+        if (layout == CONVROT_IN_MAJOR) {
+            e = convrot::launch_transpose(W, ws, K, N, w_dtype == CONVROT_F32 ? 4 : 2, s);
+            rows = ws;
+        }
+        if (e == hipSuccess)
+            e = convrot::launch_rotquant(rows, in, N, K, K, block, inv_sqrt_block(block),
+                                         out->codes, out->scale, s);
+    }
+    rc = hip_status(e);
+    if (rc != CONVROT_OK) return rc;
+    out->magic = CONVROT_WEIGHTS_MAGIC;
+    out->version = CONVROT_WEIGHTS_VERSION;
+    out->N = N;
+    out->K = K;
+    out->block = block;
+    out->flags = 0;
+    return CONVROT_OK;
+}
+
+int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
+                           const float *bias, void *Y, int y_dtype, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    int rc = check_weights(W);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, W->K)) != CONVROT_OK) return rc;
+    if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
+    if (M == 0) return CONVROT_OK;
+    if (!X || !Y) return CONVROT_EINVAL;
+    if (!aligned16(X) || !aligned16(Y) || (bias && !aligned16(bias)) || (ws && !aligned16(ws)))
+        return CONVROT_EALIGN;
+    const size_t need = convrot_linear_workspace_bytes(M, W->K, W->N, W->block);
+    if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
+
+    Carve c(ws);
+    int8_t *qx = static_cast<int8_t *>(c.take((size_t)M * (size_t)W->K));
+    float *sx = static_cast<float *>(c.take((size_t)M * 4u));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W->K, W->K, W->block,
+                                            inv_sqrt_block(W->block), qx, sx, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qx, W->codes, sx, W->scale, bias, Y, out_kind(y_dtype), M,
+                                    W->N, W->K, s);
+    return hip_status(e);
+}
+
+int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
+                            const convrot_weights *B, const float *bias, void *Y, int y_dtype,
+                            void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_weights(A);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_weights(B)) != CONVROT_OK) return rc;
+    if (A->N != B->K || A->block != B->block) return CONVROT_ELAYOUT;
+    if ((rc = check_rows(M, A->K)) != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, A->N)) != CONVROT_OK) return rc;
+    if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
+    if (M == 0) return CONVROT_OK;
+    if (!X || !Y) return CONVROT_EINVAL;
+    if (!aligned16(X) || !aligned16(Y) || (bias && !aligned16(bias)) || (ws && !aligned16(ws)))
+        return CONVROT_EALIGN;
+    const int64_t r = A->N;
+    const size_t need = lowrank_convrot_workspace_bytes(M, A->K, r, B->N, A->block);
+    if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
+
+    Carve c(ws);
+    int8_t *qx = static_cast<int8_t *>(c.take((size_t)M * (size_t)A->K));
+    float *sx = static_cast<float *>(c.take((size_t)M * 4u));
+    void *h = c.take((size_t)M * (size_t)r * 2u);
+    int8_t *qh = static_cast<int8_t *>(c.take((size_t)M * (size_t)r));
+    float *sh = static_cast<float *>(c.take((size_t)M * 4u));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float isb = inv_sqrt_block(A->block);
+    hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, A->K, A->K, A->block,
+                                            isb, qx, sx, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qx, A->codes, sx, A->scale, nullptr, h,
+                                    convrot::OutKind::BF16, M, r, A->K, s);
+    if (e == hipSuccess)
+        e = convrot::launch_rotquant(h, convrot::InType::BF16, M, r, r, B->block, isb, qh, sh, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qh, B->codes, sh, B->scale, bias, Y, out_kind(y_dtype), M,
+                                    B->N, r, s);
+    return hip_status(e);
+}
+
+int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
+                        const float *bias_up, const convrot_weights *W_down,
+                        const float *bias_down, void *Y, int y_dtype, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    int rc = check_weights(W_up);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_weights(W_down)) != CONVROT_OK) return rc;
+    if (W_up->N != W_down->K || W_up->block != W_down->block) return CONVROT_ELAYOUT;
+    if ((rc = check_rows(M, W_up->K)) != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, W_up->N)) != CONVROT_OK) return rc;
+    if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
+    if (M == 0) return CONVROT_OK;
+    if (!X || !Y) return CONVROT_EINVAL;
+    if (!aligned16(X) || !aligned16(Y) || (bias_up && !aligned16(bias_up)) ||
+        (bias_down && !aligned16(bias_down)) || (ws && !aligned16(ws)))
+        return CONVROT_EALIGN;
+    const int64_t F = W_up->N;
+    const size_t need = convrot_mlp_workspace_bytes(M, W_up->K, F, W_down->N, W_up->block);
+    if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
+
+    Carve c(ws);
+    int8_t *qx = static_cast<int8_t *>(c.take((size_t)M * (size_t)W_up->K));
+    float *sx = static_cast<float *>(c.take((size_t)M * 4u));
+    void *g = c.take((size_t)M * (size_t)F * 2u);
+    int8_t *qg = static_cast<int8_t *>(c.take((size_t)M * (size_t)F));
+    float *sg = static_cast<float *>(c.take((size_t)M * 4u));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float isb = inv_sqrt_block(W_up->block);
+    hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W_up->K, W_up->K,
+                                            W_up->block, isb, qx, sx, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qx, W_up->codes, sx, W_up->scale, bias_up, g,
+                                    convrot::OutKind::GELU_BF16, M, F, W_up->K, s);
+    if (e == hipSuccess)
+        e = convrot::launch_rotquant(g, convrot::InType::BF16, M, F, F, W_down->block, isb, qg,
+                                     sg, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qg, W_down->codes, sg, W_down->scale, bias_down, Y,
+                                    out_kind(y_dtype), M, W_down->N, F, s);
+    return hip_status(e);
+}
+
+int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int block,
+                            uint32_t flags, int8_t *q, float *s_out, void *stream)
+{
+    if (M < 0 || K <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
+    if (flags != 0) return CONVROT_EUNSUPPORTED;
+    if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
+    if (K > kMaxK || M * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    if (M == 0) return CONVROT_OK;
+    if (!X || !q || !s_out) return CONVROT_EINVAL;
+    if (!aligned16(X) || !aligned16(q) || !aligned16(s_out)) return CONVROT_EALIGN;
+    const convrot::InType in = x_dtype == CONVROT_F32 ? convrot::InType::F32 : convrot::InType::BF16;
+    return hip_status(convrot::launch_rotquant(X, in, M, K, K, block, inv_sqrt_block(block), q,
+                                               s_out, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W, int32_t *acc,
+                     void *stream)
+{
+    int rc = check_weights(W);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, W->K)) != CONVROT_OK) return rc;
+    if (M == 0) return CONVROT_OK;
+    if (!q_x || !acc) return CONVROT_EINVAL;
+    if (!aligned16(q_x) || !aligned16(acc)) return CONVROT_EALIGN;
+    return hip_status(convrot::launch_gemm_i8(q_x, W->codes, nullptr, nullptr, nullptr, acc,
+                                              convrot::OutKind::I32, M, W->N, W->K,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
+                         const convrot_weights *W, const float *bias, void *Y, int y_dtype,
+                         uint32_t flags, void *stream)
+{
+    int rc = check_weights(W);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, W->K)) != CONVROT_OK) return rc;
+    if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
+    if ((flags & ~CONVROT_FLAG_GELU) != 0) return CONVROT_EUNSUPPORTED;
+    const bool gelu = (flags & CONVROT_FLAG_GELU) != 0;
+    if (gelu && y_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
+    if (M == 0) return CONVROT_OK;
+    if (!q_x || !s_x || !Y) return CONVROT_EINVAL;
+    if (!aligned16(q_x) || !aligned16(s_x) || !aligned16(Y) || (bias && !aligned16(bias)))
+        return CONVROT_EALIGN;
+    return hip_status(convrot::launch_gemm_i8(
+        q_x, W->codes, s_x, W->scale, bias, Y,
+        gelu ? convrot::OutKind::GELU_BF16 : out_kind(y_dtype), M, W->N, W->K,
+        static_cast<hipStream_t>(stream)));
+}
+
+} // extern "C"

@@ -1,0 +1,373 @@
+// Fused rotate + rowwise INT8 quantise for gfx950.
+//
+// What it computes (per row x of length K, block b):
+//   v = blockdiag(H_b) . x  in fp32, butterfly strides h = 1, 2, ..., b/2 in
+//       ascending order (Sylvester H_b, natural order, unnormalised);
+//   amax = max |v|;  q = rint(v * (127/amax)) in [-127, 127];
+//   s = (amax/127) * fp32(1/sqrt(b));  a zero row gives q = 0, s = 0.
+// The rotation and the row-wise quantise are the fused prologue of a ConvRot
+// projection (MiniMax-H3-Rung-Omega README, "Technical Architecture Overview",
+// Floor 1); the block-diagonal Hadamard in front of the W8A8 linears is the
+// lehuy.net article's ("Cach nen hoat dong", second bullet).
+//
+// Data layout in registers.  A wave covers 512 consecutive elements of a row
+// per "step": 64 lanes x 8 elements.  A block of b elements is spread over
+// L = b/8 lanes, and lane i of the block holds the 8-element chunk pi(i) of it,
+// where pi is the GF(2)-linear map with pi(1)=1, pi(2)=2, pi(4)=7, pi(8)=12,
+// pi(16)=16.  With that assignment the partner of every cross-lane butterfly
+// stage is a single DPP pattern:
+//   chunk bit 0 (h =  8): lane ^ 1   quad_perm:[1,0,3,2]
+//   chunk bit 1 (h = 16): lane ^ 2   quad_perm:[2,3,0,1]
+//   chunk bit 2 (h = 32): lane ^ 7   row_half_mirror
+//   chunk bit 3 (h = 64): lane ^ 15  row_mirror
+//   chunk bit 4 (h =128): lane ^ 16  ds_swizzle SWAP16
+// so the 8 elements of a lane go through stages h = 1, 2, 4 in registers and
+// the remaining stages cost one v_fmac_f32_dpp each.
+//
+// Sign tracking.  A butterfly needs lo+up in the lower lane and lo-up in the
+// upper one.  Every lane instead computes r + c*partner with c = +1 (lower) or
+// -1 (upper), one fused multiply-add by +-1, which rounds exactly like the add
+// or subtract.  The upper lane then holds -(lo-up); the sign is the same for
+// every element of a lane, (-1)^popcount(pi(i)) after all stages, and is
+// folded into the quantisation multiplier (negation is exact and rint is odd).
+// Hence the codes equal those of the plain butterfly order bit for bit.
+//
+// Quantise: t = v * inv rounds once (fp32), then t + 1.5*2^23 rounds to an
+// integer with ties to even (|t| <= 127.00001 << 2^22), and the code is the low
+// byte of that float's bits.
+#include "common.hpp"
+
+namespace convrot {
+namespace {
+
+constexpr int kStep = 512;      // elements per wave step
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ int chunk_of_lane(int i)
+{
+    int c = 0;
+    if (i & 1) c ^= 1;
+    if (i & 2) c ^= 2;
+    if (i & 4) c ^= 7;
+    if (i & 8) c ^= 12;
+    if (i & 16) c ^= 16;
+    return c;
+}
+
+// One cross-lane butterfly stage on the 8 registers of a chunk.  The leading
+// s_nop covers the VALU-write -> DPP-read hazard of whatever precedes.
+#define CR_DPP_STAGE(CTRL, v, c)                                              \
+    asm volatile("s_nop 1\n\t"                                                \
+                 "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"   \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]),             \
+                   "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])              \
+                 : "v"(c))
+
+template <int STAGE>
+__device__ __forceinline__ void cross_stage(float (&v)[8], float c)
+{
+    if constexpr (STAGE == 0) {
+        CR_DPP_STAGE("quad_perm:[1,0,3,2]", v, c);
+    } else if constexpr (STAGE == 1) {
+        CR_DPP_STAGE("quad_perm:[2,3,0,1]", v, c);
+    } else if constexpr (STAGE == 2) {
+        CR_DPP_STAGE("row_half_mirror", v, c);
+    } else if constexpr (STAGE == 3) {
+        CR_DPP_STAGE("row_mirror", v, c);
+    } else {
+        static_assert(STAGE == 4, "b <= 256");
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[j]), 0x401F));
+            v[j] = __builtin_fmaf(p, c, v[j]);
+        }
+    }
+}
+
+// Butterflies h = 1, 2, 4 inside one lane's chunk (ascending).
+__device__ __forceinline__ void inlane_fwht8(float (&v)[8])
+{
+#pragma unroll
+    for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & h) == 0) {
+                float a = v[i], c = v[i + h];
+                v[i] = __fadd_rn(a, c);
+                v[i + h] = __fsub_rn(a, c);
+            }
+        }
+    }
+}
+
+template <int IN>
+__device__ __forceinline__ void load_chunk(const void *src, int64_t off, float (&v)[8])
+{
+    if constexpr (IN == int(InType::BF16)) {
+        const uint4 d = *reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const uint16_t *>(src) + off);
+        v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
+        v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
+        v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
+        v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(
+            reinterpret_cast<const float *>(src) + off);
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+__device__ __forceinline__ uint32_t code_bits(float v, float inv)
+{
+    return __float_as_uint(__fadd_rn(__fmul_rn(v, inv), kMagic));
+}
+
+__device__ __forceinline__ uint2 quantise_chunk(const float (&v)[8], float inv)
+{
+    uint32_t c0 = code_bits(v[0], inv), c1 = code_bits(v[1], inv);
+    uint32_t c2 = code_bits(v[2], inv), c3 = code_bits(v[3], inv);
+    uint32_t c4 = code_bits(v[4], inv), c5 = code_bits(v[5], inv);
+    uint32_t c6 = code_bits(v[6], inv), c7 = code_bits(v[7], inv);
+    // v_perm_b32: pick the low byte of each code into one dword.
+    uint32_t p01 = __builtin_amdgcn_perm(c1, c0, 0x0c0c0400u);
+    uint32_t p23 = __builtin_amdgcn_perm(c3, c2, 0x0c0c0400u);
+    uint32_t p45 = __builtin_amdgcn_perm(c5, c4, 0x0c0c0400u);
+    uint32_t p67 = __builtin_amdgcn_perm(c7, c6, 0x0c0c0400u);
+    uint2 r;
+    r.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    r.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
+    return r;
+}
+
+__device__ __forceinline__ float wave_max(float m)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        m = fmaxf(m, __shfl_xor(m, off, 64));
+    return m;
+}
+
+// IN: input type; B: Hadamard block; SPR: wave steps per row held per wave;
+// RPW: rows per wave (when WPR == 1); WPR: waves per row; NW: waves per WG.
+template <int IN, int B, int SPR, int RPW, int WPR, int NW>
+__global__ __launch_bounds__(NW * 64) void rotquant_kernel(
+    const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
+    int8_t *__restrict__ q, float *__restrict__ s)
+{
+    static_assert(RPW == 1 || WPR == 1, "multi-wave rows hold one row per wave");
+    static_assert(NW % WPR == 0, "");
+    constexpr int LPB = B / 8;
+    constexpr int NSTAGE = (B == 64) ? 3 : (B == 128) ? 4 : 5;
+    constexpr int GROUPS = NW / WPR;
+
+    __shared__ float red[NW];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int part = wave % WPR;
+    const int grp = wave / WPR;
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * RPW;
+    const int li = lane % LPB;
+    const int chunk = chunk_of_lane(li);
+    const int lane_off = (lane / LPB) * B + chunk * 8;
+    const int steps = (K + kStep - 1) / kStep;
+
+    float v[RPW][SPR][8];
+
+    // ---- loads: every chunk of every row this wave owns, all in flight ----
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int64_t row = row0 + r;
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            const int st = part + WPR * t;
+            const int e = st * kStep + lane_off;
+            if (row < M && st < steps && e < K) {
+                load_chunk<IN>(src, row * ld + e, v[r][t]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[r][t][j] = 0.0f;
+            }
+        }
+    }
+
+    // ---- rotation: in-lane stages, then cross-lane stages (uniform flow) ---
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int t = 0; t < SPR; ++t)
+            inlane_fwht8(v[r][t]);
+
+    float csign[NSTAGE];
+#pragma unroll
+    for (int k = 0; k < NSTAGE; ++k)
+        csign[k] = ((chunk >> k) & 1) ? -1.0f : 1.0f;
+
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) cross_stage<0>(v[r][t], csign[0]);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) cross_stage<1>(v[r][t], csign[1]);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) cross_stage<2>(v[r][t], csign[2]);
+    if constexpr (NSTAGE > 3) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int t = 0; t < SPR; ++t) cross_stage<3>(v[r][t], csign[3]);
+    }
+    if constexpr (NSTAGE > 4) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int t = 0; t < SPR; ++t) cross_stage<4>(v[r][t], csign[4]);
+    }
+
+    const bool negated = (__builtin_popcount(chunk) & 1) != 0;
+
+    // ---- per row: amax, scale, codes ----
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int64_t row = row0 + r;
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < SPR; ++t)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[r][t][j]));
+        m = wave_max(m);
+        if constexpr (WPR > 1) {
+            if (lane == 0) red[wave] = m;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) m = fmaxf(m, red[grp * WPR + w]);
+        }
+        const float inv = (m > 0.0f) ? __fdiv_rn(127.0f, m) : 0.0f;
+        const float invs = negated ? -inv : inv;
+        if (row < M) {
+            if (part == 0 && lane == 0)
+                s[row] = __fmul_rn(__fdiv_rn(m, 127.0f), inv_sqrt_b);
+#pragma unroll
+            for (int t = 0; t < SPR; ++t) {
+                const int st = part + WPR * t;
+                const int e = st * kStep + lane_off;
+                if (st < steps && e < K)
+                    *reinterpret_cast<uint2 *>(q + row * (int64_t)K + e) =
+                        quantise_chunk(v[r][t], invs);
+            }
+        }
+    }
+}
+
+template <int IN, int B, int SPR, int RPW, int WPR, int NW>
+hipError_t launch_cfg(const void *src, int64_t M, int64_t K, int64_t ld,
+                      float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+{
+    constexpr int rows_per_wg = (NW / WPR) * RPW;
+    const int64_t grid = (M + rows_per_wg - 1) / rows_per_wg;
+    hipLaunchKernelGGL((rotquant_kernel<IN, B, SPR, RPW, WPR, NW>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, src, M, (int)K, ld, inv_sqrt_b, q, s);
+    return hipGetLastError();
+}
+
+template <int IN, int B>
+hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
+                    float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+{
+    const int64_t steps = (K + kStep - 1) / kStep;
+    if (steps <= 1) return launch_cfg<IN, B, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 2) return launch_cfg<IN, B, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 4) return launch_cfg<IN, B, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 8) return launch_cfg<IN, B, 8, 1, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 12) return launch_cfg<IN, B, 12, 1, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 24) return launch_cfg<IN, B, 12, 1, 2, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 48) return launch_cfg<IN, B, 12, 1, 4, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 64) return launch_cfg<IN, B, 8, 1, 8, 8>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    return launch_cfg<IN, B, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+}
+
+template <int IN>
+hipError_t launch_in(const void *src, int64_t M, int64_t K, int64_t ld, int block,
+                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+{
+    switch (block) {
+    case 64: return launch_b<IN, 64>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    case 128: return launch_b<IN, 128>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    case 256: return launch_b<IN, 256>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// ------------------------------------------------------------ transpose ----
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ src,
+                                                        T *__restrict__ dst,
+                                                        int64_t R, int64_t C)
+{
+    __shared__ T tile[32][33];
+    const int64_t c0 = (int64_t)blockIdx.x * 32, r0 = (int64_t)blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+#pragma unroll
+    for (int k = 0; k < 32; k += 8) {
+        const int64_t r = r0 + ty + k, c = c0 + tx;
+        if (r < R && c < C) tile[ty + k][tx] = src[r * C + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 32; k += 8) {
+        const int64_t c = c0 + ty + k, r = r0 + tx;
+        if (r < R && c < C) dst[c * R + r] = tile[tx][ty + k];
+    }
+}
+
+} // namespace
+
+hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
+                           int64_t ld, int block, float inv_sqrt_b, int8_t *q,
+                           float *s, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    if (in == InType::BF16)
+        return launch_in<int(InType::BF16)>(src, M, K, ld, block, inv_sqrt_b, q, s, stream);
+    return launch_in<int(InType::F32)>(src, M, K, ld, block, inv_sqrt_b, q, s, stream);
+}
+
+hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
+                            int elem_bytes, hipStream_t stream)
+{
+    if (R == 0 || C == 0) return hipSuccess;
+    dim3 grid((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32));
+    switch (elem_bytes) {
+    case 1:
+        hipLaunchKernelGGL(transpose_kernel<int8_t>, grid, dim3(256), 0, stream,
+                           (const int8_t *)src, (int8_t *)dst, R, C);
+        break;
+    case 2:
+        hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                           (const uint16_t *)src, (uint16_t *)dst, R, C);
+        break;
+    case 4:
+        hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, stream,
+                           (const float *)src, (float *)dst, R, C);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+} // namespace convrot
