@@ -54,6 +54,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#if defined(__GNUC__) || defined(__clang__)
+#define CONVROT_API __attribute__((visibility("default")))
+#else
+#define CONVROT_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -108,37 +114,37 @@ typedef struct convrot_weights {
 } convrot_weights;
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char *convrot_status_string(int status);
+CONVROT_API const char *convrot_status_string(int status);
 
 /* The hipError_t of the most recent CONVROT_EHIP on this thread (0 if none). */
-int convrot_last_hip_error(void);
+CONVROT_API int convrot_last_hip_error(void);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
-int convrot_version(void);
+CONVROT_API int convrot_version(void);
 
 /* ------------------------------------------------------------------ */
 /* sizing queries (host only, no HIP calls)                            */
 /* ------------------------------------------------------------------ */
 
 /* Bytes of packed codes for an [N, K] weight (0 for invalid shapes). */
-size_t convrot_weights_packed_bytes(int64_t N, int64_t K, int block);
+CONVROT_API size_t convrot_weights_packed_bytes(int64_t N, int64_t K, int block);
 
 /* Workspace for convrot_linear_prepare_weights (0 is a valid answer). */
-size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block,
+CONVROT_API size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block,
                                        int w_dtype, int layout);
 
 /* Workspace for convrot_linear_forward: INT8 codes [M, K] and F32 row scales
  * [M] of the rotated activations, each region 256-byte aligned. */
-size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block);
+CONVROT_API size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block);
 
 /* Workspace for lowrank_convrot_forward (codes of X, bf16 intermediate
  * H [M, r], codes of H, and row scales). */
-size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r,
+CONVROT_API size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r,
                                        int64_t N, int block);
 
 /* Workspace for convrot_mlp_forward (codes of X, bf16 activation g [M, F],
  * codes of g, row scales). */
-size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
+CONVROT_API size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
                                    int block);
 
 /* ------------------------------------------------------------------ */
@@ -161,7 +167,7 @@ size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
  * per output channel, i.e. the INT8 image of W . R^T.  Import mode copies the
  * codes (transposing IN_MAJOR input) and scales without changing any value,
  * as the input-major repack does. */
-int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
+CONVROT_API int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
                                    const float *src_scale, int64_t N, int64_t K,
                                    int block, convrot_weights *out, void *ws,
                                    size_t ws_bytes, void *stream);
@@ -178,7 +184,7 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
  *   ws      device workspace of convrot_linear_workspace_bytes(M, K, N, b).
  * Rows are independent: forward on a row slice equals the same slice of the
  * full forward, bit for bit. */
-int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
+CONVROT_API int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
                            const float *bias, void *Y, int y_dtype, void *ws,
                            size_t ws_bytes, void *stream);
 
@@ -187,7 +193,7 @@ int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
  * with the same block and requantised per token.  Requires A->N == B->K (= r),
  * A->block == B->block and r % 128 == 0 (pad the rank with zero rows of A and
  * zero columns of B, which leaves the product unchanged). */
-int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
+CONVROT_API int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
                             const convrot_weights *B, const float *bias,
                             void *Y, int y_dtype, void *ws, size_t ws_bytes,
                             void *stream);
@@ -196,7 +202,7 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
  * erf form of GELU evaluated in fp32; Y = linear(g; W_down) + bias_down.
  * Requires W_up->N == W_down->K (= F).  GELU is applied in the epilogue of the
  * up projection, so u is never written. */
-int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
+CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
                         const float *bias_up, const convrot_weights *W_down,
                         const float *bias_down, void *Y, int y_dtype, void *ws,
                         size_t ws_bytes, void *stream);
@@ -208,12 +214,12 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
 
 /* Rotate and quantise rows: X [M, K] (x_dtype F32 or BF16) -> q [M, K] int8
  * and s [M] F32.  flags must be 0. */
-int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K,
+CONVROT_API int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K,
                             int block, uint32_t flags, int8_t *q, float *s,
                             void *stream);
 
 /* Exact INT32 contraction acc[M, N] = q_x [M, K] . codes(W)^T. */
-int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W,
+CONVROT_API int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W,
                      int32_t *acc, void *stream);
 
 /* Contraction plus the dequant epilogue from given codes and row scales:
@@ -222,7 +228,7 @@ int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W,
  * bf16(GELU(float(bf16(Y)))), the activation the MLP entry point feeds to its
  * down projection. */
 #define CONVROT_FLAG_GELU 1u
-int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
+CONVROT_API int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
                          const convrot_weights *W, const float *bias, void *Y,
                          int y_dtype, uint32_t flags, void *stream);
 

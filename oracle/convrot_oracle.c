@@ -42,6 +42,7 @@
  * of R2.  Build with -ffp-contract=off and without -ffast-math.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -53,6 +54,9 @@
 /* dtype tags used by this oracle only */
 #define OR_F32 0
 #define OR_BF16 1
+
+/* Threads an OpenMP region of this library uses (for reporting). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* bf16 <-> fp32                                                       */

@@ -41,6 +41,7 @@ def open_library(path):
     """Open a build of the oracle's C file and declare its signatures."""
     lib = ctypes.CDLL(path)
     sig = {
+        "oracle_num_threads": (_c_int, []),
         "oracle_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
         "oracle_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
         "oracle_fwht_f32": (_c_int, [_c_p, _c_i64, _c_int]),
@@ -112,6 +113,11 @@ def f32_to_bf16(x) -> np.ndarray:
     for i in range(flat.size):
         out[i] = f(float(flat[i]))
     return out.reshape(x.shape)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel regions use."""
+    return int(_load().oracle_num_threads())
 
 
 def inv_sqrt_b(b: int) -> np.float32:
@@ -304,7 +310,7 @@ def mlp_forward(X_bf16, qu, su, qd, sd, b: int, bias_up=None, bias_down=None,
 
 
 __all__ = [
-    "bf16_to_f32", "f32_to_bf16", "inv_sqrt_b", "fwht", "rowquant",
+    "num_threads", "bf16_to_f32", "f32_to_bf16", "inv_sqrt_b", "fwht", "rowquant",
     "rotate_quantize", "prepare_weights", "gemm_i32", "dequant",
     "linear_forward", "lowrank_forward", "gelu_f64", "gelu_bf16", "mlp_forward",
 ]

@@ -33,7 +33,7 @@ COMMON = [
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-disable-promote-alloca-to-lds=true",
-    "-Wall", "-Wno-unused-function",
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
