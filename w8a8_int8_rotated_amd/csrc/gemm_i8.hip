@@ -16,12 +16,23 @@
 // The weight tile is the MFMA A operand (rows = n) and the activation tile
 // the B operand (columns = m), so an accumulator lane holds 4 consecutive n of
 // one m and the epilogue stores 4 outputs per instruction.
-// K advances 128 bytes per stage through two LDS stages of 64 KiB each; the
-// next stage's global loads are issued before the current stage's MFMAs and
-// written to LDS after them, one barrier per stage.
-// LDS rows are 128 bytes; the 16-byte chunk c of tile row r lives at slot
-// c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), which keeps both the row-wise
-// writes and the column-wise MFMA fragment reads free of bank conflicts.
+//
+// K pipeline: K advances 64 bytes per stage; STAGES stages of 32 KiB (W and X
+// tiles, 256 rows x 64 B each) live in LDS.  Global -> LDS copies use the
+// direct-to-LDS load (global_load_lds_dwordx4: each lane fetches 16 bytes and
+// the wave's 1 KiB lands contiguously in LDS), so no registers stage the
+// tiles and no LDS write instructions are issued.  Tile kt + STAGES is
+// requested as soon as stage kt is consumed, STAGES - 1 tiles ahead of use.
+// The compiler does not order LDS reads after these copies, so every wait is
+// explicit: s_waitcnt vmcnt(n) for this wave's copies, then a barrier for the
+// other waves'.
+//
+// LDS rows are 64 bytes; chunk c (16 B) of tile row r sits at slot
+// c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A copy instruction writes 16
+// consecutive rows, so lane i fetches chunk (i & 3) ^ f(row) of its row; the
+// column-wise MFMA fragment reads (32 rows, one chunk) then hit distinct banks
+// for 32- and 64-bank LDS alike.
+//
 // Workgroups are renumbered so each of the 8 XCDs walks a contiguous range of
 // tiles, grouped 8 tile-rows high, for L2 reuse of both operands.
 #include "common.hpp"
@@ -33,12 +44,80 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 256;     // tile edge in m and in n
-constexpr int kBK = 128;       // K bytes per LDS stage
+constexpr int kBK = 64;        // K bytes per LDS stage
 constexpr int kThreads = 256;
-constexpr int kStageBytes = kTile * kBK;   // one operand, one stage: 32 KiB
 constexpr int kGroup = 8;      // tile-rows per L2 group
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `tiles` stages of this wave's copies (COPIES each) are
+// still in flight.
+template <int COPIES>
+__device__ __forceinline__ void wait_copies(int tiles)
+{
+    if (tiles >= 3) wait_vmcnt<3 * COPIES>();
+    else if (tiles == 2) wait_vmcnt<2 * COPIES>();
+    else if (tiles == 1) wait_vmcnt<1 * COPIES>();
+    else wait_vmcnt<0>();
+}
+
+// s_waitcnt lgkmcnt(0) with vmcnt/expcnt left unconstrained.
+__device__ __forceinline__ void wait_lds_reads()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Scheduling-group masks (LLVM AMDGPU sched_group_barrier).
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+
+// Order the current scheduling region as (MFMA, LDS read) pairs followed by
+// (MFMA, global->LDS copy) pairs, so reads and copies trickle out between
+// matrix instructions instead of blocking issue in a burst.  Every LDS read
+// precedes every copy in the region: a read placed after a copy in the same
+// block would get a conservative vmcnt wait on that copy.
+template <int MFMAS, int VMEMS, int DSREADS>
+__device__ __forceinline__ void interleave()
+{
+    static_assert(VMEMS + DSREADS <= MFMAS, "");
+#pragma unroll
+    for (int k = 0; k < DSREADS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < VMEMS; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+    if (MFMAS > VMEMS + DSREADS)
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, MFMAS - VMEMS - DSREADS, 0);
+}
+
+__device__ __forceinline__ void copy16(const int8_t *g, int8_t *lds)
+{
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(g),
+                                     (__attribute__((address_space(3))) void *)(lds), 16, 0, 0);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 with v_cvt_pk_bf16_f32 (round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
+{
+    const bf16x2 p = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, p);
+}
 
 template <int OUT, bool HAS_BIAS>
 __device__ __forceinline__ void store4(void *Y, int64_t off, const v16i &acc, int q,
@@ -71,21 +150,195 @@ __device__ __forceinline__ void store4(void *Y, int64_t off, const v16i &acc, in
                 }
             }
             uint2 o;
-            o.x = pack_bf16x2(y[0], y[1]);
-            o.y = pack_bf16x2(y[2], y[3]);
+            o.x = cvt_pk_bf16(y[0], y[1]);
+            o.y = cvt_pk_bf16(y[2], y[3]);
             *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(Y) + off) = o;
         }
     }
 }
 
-template <int OUT, bool HAS_BIAS>
+// Dequantise and store a wave's 128 x 128 block.  FULL: the tile lies inside
+// [M, N], so no per-lane bounds checks are needed.
+template <int OUT, bool HAS_BIAS, int TJ, bool FULL>
+__device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
+                                         const float (&sscale)[3][kTile], int M, int N,
+                                         int m0, int n0, int wm, int wn, int l32, int g)
+{
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float sxm[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+        sxm[j] = (OUT == int(OutKind::I32)) ? 0.0f : sscale[0][wm * 32 * TJ + 32 * j + l32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
+            const int nb = n0 + nl;
+            if (!FULL && nb >= N) continue;
+            float4 swv = zero4, bv = zero4;
+            if constexpr (OUT != int(OutKind::I32)) {
+                swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
+                if constexpr (HAS_BIAS) bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
+            }
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int m = m0 + wm * 32 * TJ + 32 * j + l32;
+                if (!FULL && m >= M) continue;
+                store4<OUT, HAS_BIAS>(Y, (int64_t)m * N + nb, acc[i][j], q, sxm[j], swv, bv);
+            }
+        }
+    }
+}
+
+// Per-wave state of the K loop, kept in registers.
+struct CopyPlan {
+    uint32_t offw[4];   // byte offsets of this lane's 16-byte W chunks, per copy
+    uint32_t offx[4];   // same for X
+};
+
+// Direct-to-LDS copies of K-tile `kt` into one stage (wave-uniform LDS bases).
+__device__ __forceinline__ void issue_stage(const int8_t *qw, const int8_t *qx,
+                                            const CopyPlan &cp, int kt, int wave,
+                                            int8_t *__restrict__ dst_w,
+                                            int8_t *__restrict__ dst_x)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        copy16(qw + kt * kBK + cp.offw[j], dst_w + (wave * 4 + j) * 1024);
+        copy16(qx + kt * kBK + cp.offx[j], dst_x + (wave * 4 + j) * 1024);
+    }
+}
+
+__device__ __forceinline__ void read_frags(const int8_t *__restrict__ sw_,
+                                           const int8_t *__restrict__ sx_, int frow_w,
+                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = *reinterpret_cast<const v4i *>(sw_ + frow_w + 2048 * i + foff);
+        b[i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * i + foff);
+    }
+}
+
+__device__ __forceinline__ void mfma16(v16i (&acc)[4][4], const v4i (&a)[4], const v4i (&b)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+template <int S, int I>
+__device__ __forceinline__ int8_t *pick(int8_t *p0, int8_t *p1, int8_t *p2, int8_t *p3)
+{
+    constexpr int k = I % S;
+    return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3;
+}
+
+// The K loop over one 256 x 256 tile.  Each LDS stage is a separate object
+// reached through its own restrict pointer, and the loop is unrolled by the
+// stage count so every access names its stage at compile time.  That lets
+// the compiler prove that an LDS read of one stage does not depend on copies
+// still landing in another, so it only waits (vmcnt) for copies into the
+// stage being read.  Waiting for the other waves' copies is explicit: each
+// wave retires its own copies of the next tile, then all meet at a barrier.
+template <int S>
+__device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
+                                       int8_t *__restrict__ w2, int8_t *__restrict__ w3,
+                                       int8_t *__restrict__ x0, int8_t *__restrict__ x1,
+                                       int8_t *__restrict__ x2, int8_t *__restrict__ x3,
+                                       const int8_t *qw, const int8_t *qx, const CopyPlan &cp,
+                                       int nk, int wave, int frow_w, int frow_x, int foff0,
+                                       int foff1, v16i (&acc)[4][4])
+{
+    static_assert(S == 2 || S == 4, "stages");
+    constexpr int COPIES = 8;
+    v4i a0[4], b0[4], a1[4], b1[4];
+
+    // prologue: every stage starts free
+    issue_stage(qw, qx, cp, 0, wave, pick<S, 0>(w0, w1, w2, w3), pick<S, 0>(x0, x1, x2, x3));
+    issue_stage(qw, qx, cp, min(1, nk - 1), wave, pick<S, 1>(w0, w1, w2, w3),
+                pick<S, 1>(x0, x1, x2, x3));
+    if constexpr (S == 4) {
+        issue_stage(qw, qx, cp, min(2, nk - 1), wave, w2, x2);
+        issue_stage(qw, qx, cp, min(3, nk - 1), wave, w3, x3);
+    }
+    wait_vmcnt<(S - 1) * COPIES>();
+    block_barrier();
+    read_frags(w0, x0, frow_w, frow_x, foff0, a0, b0);
+
+    // One step = the second half of K-tile kt (MFMAs on the sub-step-1
+    // fragments, with the reads of tile kt+1's sub-step 0 and the copies of
+    // tile kt+S interleaved) and the first half of tile kt+1.
+#define CONVROT_STEP(I)                                                                  \
+    do {                                                                                 \
+        int8_t *cw_ = pick<S, I>(w0, w1, w2, w3), *cx_ = pick<S, I>(x0, x1, x2, x3);      \
+        int8_t *nw_ = pick<S, I + 1>(w0, w1, w2, w3), *nx_ = pick<S, I + 1>(x0, x1, x2, x3); \
+        wait_lds_reads();                                                                \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
+        mfma16(acc, a0, b0);                                                             \
+        interleave<16, 0, 8>();                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+        wait_lds_reads();                                                                \
+        wait_vmcnt<(S - 2) * COPIES>();                                                  \
+        block_barrier();                                                                 \
+        read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
+        issue_stage(qw, qx, cp, min(kt + I + S, nk - 1), wave, cw_, cx_);                \
+        mfma16(acc, a1, b1);                                                             \
+        interleave<16, COPIES, 8>();                                                     \
+        __builtin_amdgcn_sched_barrier(0);                                               \
+    } while (0)
+
+    // nk - 1 steps (K-tiles 0 .. nk-2), S at a time, then the rest in line
+    int kt = 0;
+    for (; kt + S < nk; kt += S) {
+        CONVROT_STEP(0);
+        CONVROT_STEP(1);
+        if constexpr (S == 4) {
+            CONVROT_STEP(2);
+            CONVROT_STEP(3);
+        }
+    }
+    // nk is a multiple of S: S - 1 steps remain
+    CONVROT_STEP(0);
+    if constexpr (S == 4) {
+        CONVROT_STEP(1);
+        CONVROT_STEP(2);
+    }
+#undef CONVROT_STEP
+    {
+        const int8_t *lw = pick<S, S - 1>(w0, w1, w2, w3), *lx = pick<S, S - 1>(x0, x1, x2, x3);
+        wait_lds_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(lw, lx, frow_w, frow_x, foff1, a1, b1);
+        mfma16(acc, a0, b0);
+        interleave<16, 0, 8>();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma16(acc, a1, b1);
+    }
+    // No copy may still be writing LDS when the workgroup moves on.
+    wait_vmcnt<0>();
+}
+
+// One 256 (n) x 256 (m) output tile per 256-thread workgroup, one workgroup
+// per CU (256 AGPR accumulators per lane).  S: LDS stages (4 when the K-tile
+// count is a multiple of 4, else 2).
+template <int OUT, bool HAS_BIAS, int S>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw,
     const float *__restrict__ sx, const float *__restrict__ sw,
     const float *__restrict__ bias, void *__restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, int tiles_per_xcd)
 {
-    __shared__ __attribute__((aligned(16))) int8_t smem[2][2][kStageBytes];  // [stage][W|X]
+    constexpr int STAGE = kTile * kBK;   // 16 KiB per operand
+    __shared__ __attribute__((aligned(1024))) int8_t sw0[STAGE], sw1[STAGE], sw2[S == 4 ? STAGE : 16],
+        sw3[S == 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t sx0[STAGE], sx1[STAGE], sx2[S == 4 ? STAGE : 16],
+        sx3[S == 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) float sscale[3][kTile];   // s_x, s_w, bias
 
     // ---- tile selection: XCD-contiguous ranges, grouped along m ----
     const int pid = blockIdx.x;
@@ -102,25 +355,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
 
-    // ---- global -> LDS copy assignment: 8 rows per thread and operand ----
-    const int crow = tid >> 3, cch = tid & 7;
-    uint32_t offx[8], offw[8];
+    // ---- copy plan: a copy moves 16 rows x 64 B; wave w moves rows
+    // [(4w + j) 16, +16) of each operand; lane i takes row + i/4 and the chunk
+    // that belongs in slot i & 3 of that row ----
+    CopyPlan cp;
 #pragma unroll
-    for (int l = 0; l < 8; ++l) {
-        const int r = crow + 32 * l;
-        offx[l] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + cch * 16;
-        offw[l] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + cch * 16;
+    for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 16 + (lane >> 2);
+        const uint32_t c = ((lane & 3) ^ swz(r)) << 4;
+        cp.offw[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c;
+        cp.offx[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c;
     }
-    const int lds_w = crow * kBK + ((cch ^ swz(crow)) << 4);  // + 4096 * l
 
     // ---- fragment read assignment ----
     const int l32 = lane & 31, g = lane >> 5;
-    const int fx = g ^ swz(l32);
-    int foff[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) foff[s] = ((2 * s) ^ fx) << 4;
-    const int frow_w = (wn * 128 + l32) * kBK;  // + 4096 * i
-    const int frow_x = (wm * 128 + l32) * kBK;  // + 4096 * j
+    const int foff0 = ((0 + g) ^ swz(l32)) << 4;
+    const int foff1 = ((2 + g) ^ swz(l32)) << 4;
+    const int frow_w = (wn * 128 + l32) * kBK;   // + 2048 * i
+    const int frow_x = (wm * 128 + l32) * kBK;   // + 2048 * j
+
+    // The tile's scales: plain loads issued ahead of the first K-tile copies,
+    // written to LDS before the epilogue.
+    float sc_x = 0.f, sc_w = 0.f, sc_b = 0.f;
+    if constexpr (OUT != int(OutKind::I32)) {
+        sc_x = sx[min(m0 + tid, M - 1)];
+        sc_w = sw[min(n0 + tid, N - 1)];
+        if constexpr (HAS_BIAS) sc_b = bias[min(n0 + tid, N - 1)];
+    }
 
     v16i acc[4][4];
 #pragma unroll
@@ -130,107 +391,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    v4i rw[8], rx[8];
-#pragma unroll
-    for (int l = 0; l < 8; ++l) {
-        rw[l] = *reinterpret_cast<const v4i *>(qw + offw[l]);
-        rx[l] = *reinterpret_cast<const v4i *>(qx + offx[l]);
-    }
-#pragma unroll
-    for (int l = 0; l < 8; ++l) {
-        *reinterpret_cast<v4i *>(&smem[0][0][lds_w + 4096 * l]) = rw[l];
-        *reinterpret_cast<v4i *>(&smem[0][1][lds_w + 4096 * l]) = rx[l];
+    k_loop<S>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, qw, qx, cp, K / kBK, wave, frow_w,
+              frow_x, foff0, foff1, acc);
+
+    if constexpr (OUT != int(OutKind::I32)) {
+        sscale[0][tid] = sc_x;
+        sscale[1][tid] = sc_w;
+        sscale[2][tid] = sc_b;
     }
     __syncthreads();
 
-    const int nk = K / kBK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int8_t *bw = qw + (kt + 1) * kBK;
-            const int8_t *bx = qx + (kt + 1) * kBK;
-#pragma unroll
-            for (int l = 0; l < 8; ++l) {
-                rw[l] = *reinterpret_cast<const v4i *>(bw + offw[l]);
-                rx[l] = *reinterpret_cast<const v4i *>(bx + offx[l]);
-            }
-        }
-        const int8_t *sw_ = smem[cur][0];
-        const int8_t *sx_ = smem[cur][1];
-        v4i a[2][4], b[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[0][i] = *reinterpret_cast<const v4i *>(sw_ + frow_w + 4096 * i + foff[0]);
-            b[0][i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 4096 * i + foff[0]);
-        }
-        // Sub-step s: read the fragments of s+1, then 16 MFMAs on those of s.
-        // The scheduling barriers keep each group together so the LDS reads
-        // of the next sub-step overlap the current MFMAs.
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int c = s & 1;
-            if (s < 3) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[c ^ 1][i] = *reinterpret_cast<const v4i *>(sw_ + frow_w + 4096 * i + foff[s + 1]);
-                    b[c ^ 1][i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 4096 * i + foff[s + 1]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (more) {
-#pragma unroll
-            for (int l = 0; l < 8; ++l) {
-                *reinterpret_cast<v4i *>(&smem[cur ^ 1][0][lds_w + 4096 * l]) = rw[l];
-                *reinterpret_cast<v4i *>(&smem[cur ^ 1][1][lds_w + 4096 * l]) = rx[l];
-            }
-        }
-        __syncthreads();
-    }
-
     // ---- epilogue: lane holds n = nb..nb+3 of one m per (i, j, q) ----
-    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int m = m0 + wm * 128 + 32 * j + l32;
-        if (m >= M) continue;
-        const float sxm = (OUT == int(OutKind::I32)) ? 0.0f : sx[m];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int nb = n0 + wn * 128 + 32 * i + 8 * q + 4 * g;
-                if (nb >= N) continue;
-                float4 swv = zero4, bv = zero4;
-                if constexpr (OUT != int(OutKind::I32)) {
-                    swv = *reinterpret_cast<const float4 *>(sw + nb);
-                    if constexpr (HAS_BIAS) bv = *reinterpret_cast<const float4 *>(bias + nb);
-                }
-                store4<OUT, HAS_BIAS>(Y, (int64_t)m * N + nb, acc[i][j], q, sxm, swv, bv);
-            }
-        }
-    }
+    if (m0 + kTile <= M && n0 + kTile <= N)
+        epilogue<OUT, HAS_BIAS, 4, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+    else
+        epilogue<OUT, HAS_BIAS, 4, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
 }
 
 template <int OUT, bool HAS_BIAS>
-hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx,
-                    const float *sw, const float *bias, void *Y, int64_t M,
-                    int64_t N, int64_t K, hipStream_t stream)
+hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
+                    const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
+                    hipStream_t stream)
 {
     const int tiles_m = (int)((M + kTile - 1) / kTile);
     const int tiles_n = (int)((N + kTile - 1) / kTile);
     const int tiles = tiles_m * tiles_n;
     const int per_xcd = (tiles + 7) / 8;
-    hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS>), dim3(8 * per_xcd), dim3(kThreads), 0,
-                       stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m,
-                       tiles_n, per_xcd);
+    const int nk = (int)(K / kBK);
+    if (nk % 4 == 0)
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 4>), dim3(8 * per_xcd), dim3(kThreads),
+                           0, stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m,
+                           tiles_n, per_xcd);
+    else
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 2>), dim3(8 * per_xcd), dim3(kThreads),
+                           0, stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m,
+                           tiles_n, per_xcd);
     return hipGetLastError();
 }
 
