@@ -37,6 +37,8 @@
 // tiles, grouped 8 tile-rows high, for L2 reuse of both operands.
 #include "common.hpp"
 
+#include <utility>
+
 namespace convrot {
 namespace {
 
@@ -80,27 +82,35 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 // Scheduling-group masks (LLVM AMDGPU sched_group_barrier).
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
 
-// Order the current scheduling region as (MFMA, LDS read) pairs followed by
-// (MFMA, global->LDS copy) pairs, so reads and copies trickle out between
-// matrix instructions instead of blocking issue in a burst.  Every LDS read
-// precedes every copy in the region: a read placed after a copy in the same
-// block would get a conservative vmcnt wait on that copy.
+// Order the current scheduling region so that LDS reads and global->LDS
+// copies trickle out between matrix instructions instead of blocking issue in
+// a burst: the memory instructions (all LDS reads first, then all copies --
+// a read placed after a copy in the same block would get a conservative vmcnt
+// wait on that copy) are spread evenly behind the MFMAs.
+template <int MFMAS, int VMEMS, int DSREADS, int K>
+__device__ __forceinline__ void interleave_slot()
+{
+    constexpr int TOTAL = VMEMS + DSREADS;
+    // memory ops whose share falls in MFMA slot K: ops [LO, HI)
+    constexpr int LO = (K * TOTAL + MFMAS - 1) / MFMAS;
+    constexpr int HI = ((K + 1) * TOTAL + MFMAS - 1) / MFMAS;
+    constexpr int RD_LO = LO < DSREADS ? LO : DSREADS, RD_HI = HI < DSREADS ? HI : DSREADS;
+    constexpr int VM_LO = LO > DSREADS ? LO : DSREADS, VM_HI = HI > DSREADS ? HI : DSREADS;
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    if constexpr (RD_HI > RD_LO) __builtin_amdgcn_sched_group_barrier(kSgDsRead, RD_HI - RD_LO, 0);
+    if constexpr (VM_HI > VM_LO) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, VM_HI - VM_LO, 0);
+}
+
+template <int MFMAS, int VMEMS, int DSREADS, int... K>
+__device__ __forceinline__ void interleave_all(std::integer_sequence<int, K...>)
+{
+    (interleave_slot<MFMAS, VMEMS, DSREADS, K>(), ...);
+}
+
 template <int MFMAS, int VMEMS, int DSREADS>
 __device__ __forceinline__ void interleave()
 {
-    static_assert(VMEMS + DSREADS <= MFMAS, "");
-#pragma unroll
-    for (int k = 0; k < DSREADS; ++k) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < VMEMS; ++k) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-    }
-    if (MFMAS > VMEMS + DSREADS)
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, MFMAS - VMEMS - DSREADS, 0);
+    interleave_all<MFMAS, VMEMS, DSREADS>(std::make_integer_sequence<int, MFMAS>{});
 }
 
 __device__ __forceinline__ void copy16(const int8_t *g, int8_t *lds)
@@ -192,41 +202,49 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
 }
 
 // Per-wave state of the K loop, kept in registers.
+template <int TJ>
 struct CopyPlan {
-    uint32_t offw[4];   // byte offsets of this lane's 16-byte W chunks, per copy
-    uint32_t offx[4];   // same for X
+    uint32_t offw[4];    // byte offsets of this lane's 16-byte W chunks, per copy
+    uint32_t offx[TJ];   // same for X
 };
 
-// Direct-to-LDS copies of K-tile `kt` into one stage (wave-uniform LDS bases).
+// Direct-to-LDS copies of K-tile `kt` into one stage (wave-uniform LDS bases):
+// wave w fills W rows [(4w + j) 16, +16) and X rows [(TJ w + j) 16, +16).
+template <int TJ>
 __device__ __forceinline__ void issue_stage(const int8_t *qw, const int8_t *qx,
-                                            const CopyPlan &cp, int kt, int wave,
+                                            const CopyPlan<TJ> &cp, int kt, int wave,
                                             int8_t *__restrict__ dst_w,
                                             int8_t *__restrict__ dst_x)
 {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
         copy16(qw + kt * kBK + cp.offw[j], dst_w + (wave * 4 + j) * 1024);
-        copy16(qx + kt * kBK + cp.offx[j], dst_x + (wave * 4 + j) * 1024);
-    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+        copy16(qx + kt * kBK + cp.offx[j], dst_x + (wave * TJ + j) * 1024);
 }
 
+template <int TJ>
 __device__ __forceinline__ void read_frags(const int8_t *__restrict__ sw_,
                                            const int8_t *__restrict__ sx_, int frow_w,
-                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[4])
+                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[TJ])
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
         a[i] = *reinterpret_cast<const v4i *>(sw_ + frow_w + 2048 * i + foff);
-        b[i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * i + foff);
-    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+        b[j] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * j + foff);
 }
 
-__device__ __forceinline__ void mfma16(v16i (&acc)[4][4], const v4i (&a)[4], const v4i (&b)[4])
+template <int TJ>
+__device__ __forceinline__ void mfma_block(v16i (&acc)[4][TJ], const v4i (&a)[4],
+                                           const v4i (&b)[TJ])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
@@ -237,37 +255,38 @@ __device__ __forceinline__ int8_t *pick(int8_t *p0, int8_t *p1, int8_t *p2, int8
     return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3;
 }
 
-// The K loop over one 256 x 256 tile.  Each LDS stage is a separate object
-// reached through its own restrict pointer, and the loop is unrolled by the
-// stage count so every access names its stage at compile time.  That lets
-// the compiler prove that an LDS read of one stage does not depend on copies
-// still landing in another, so it only waits (vmcnt) for copies into the
-// stage being read.  Waiting for the other waves' copies is explicit: each
-// wave retires its own copies of the next tile, then all meet at a barrier.
-template <int S>
+// The K loop over one tile.  Each LDS stage is a separate object reached
+// through its own restrict pointer, and the loop is unrolled by the stage
+// count so every access names its stage at compile time.  That lets the
+// compiler prove that an LDS read of one stage does not depend on copies still
+// landing in another, so it only waits (vmcnt) for copies into the stage being
+// read.  Waiting for the other waves' copies is explicit: each wave retires
+// its own copies of the next K-tile, then all meet at a barrier.
+// Requires nk % S == 0.
+template <int TJ, int S>
 __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
                                        int8_t *__restrict__ w2, int8_t *__restrict__ w3,
                                        int8_t *__restrict__ x0, int8_t *__restrict__ x1,
                                        int8_t *__restrict__ x2, int8_t *__restrict__ x3,
-                                       const int8_t *qw, const int8_t *qx, const CopyPlan &cp,
-                                       int nk, int wave, int frow_w, int frow_x, int foff0,
-                                       int foff1, v16i (&acc)[4][4])
+                                       const int8_t *qw, const int8_t *qx,
+                                       const CopyPlan<TJ> &cp, int nk, int wave, int frow_w,
+                                       int frow_x, int foff0, int foff1,
+                                       v16i (&acc)[4][TJ])
 {
-    static_assert(S == 2 || S == 4, "stages");
-    constexpr int COPIES = 8;
-    v4i a0[4], b0[4], a1[4], b1[4];
+    static_assert(S >= 2 && S <= 4, "stages");
+    constexpr int COPIES = 4 + TJ;           // copy instructions per wave per K-tile
+    constexpr int MF = 4 * TJ;               // MFMAs per sub-step
+    constexpr int RD = 4 + TJ;               // fragment reads per sub-step
+    v4i a0[4], b0[TJ], a1[4], b1[TJ];
 
     // prologue: every stage starts free
-    issue_stage(qw, qx, cp, 0, wave, pick<S, 0>(w0, w1, w2, w3), pick<S, 0>(x0, x1, x2, x3));
-    issue_stage(qw, qx, cp, min(1, nk - 1), wave, pick<S, 1>(w0, w1, w2, w3),
-                pick<S, 1>(x0, x1, x2, x3));
-    if constexpr (S == 4) {
-        issue_stage(qw, qx, cp, min(2, nk - 1), wave, w2, x2);
-        issue_stage(qw, qx, cp, min(3, nk - 1), wave, w3, x3);
-    }
+    issue_stage<TJ>(qw, qx, cp, 0, wave, w0, x0);
+    issue_stage<TJ>(qw, qx, cp, min(1, nk - 1), wave, w1, x1);
+    if constexpr (S >= 3) issue_stage<TJ>(qw, qx, cp, min(2, nk - 1), wave, w2, x2);
+    if constexpr (S >= 4) issue_stage<TJ>(qw, qx, cp, min(3, nk - 1), wave, w3, x3);
     wait_vmcnt<(S - 1) * COPIES>();
     block_barrier();
-    read_frags(w0, x0, frow_w, frow_x, foff0, a0, b0);
+    read_frags<TJ>(w0, x0, frow_w, frow_x, foff0, a0, b0);
 
     // One step = the second half of K-tile kt (MFMAs on the sub-step-1
     // fragments, with the reads of tile kt+1's sub-step 0 and the copies of
@@ -278,17 +297,17 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         int8_t *nw_ = pick<S, I + 1>(w0, w1, w2, w3), *nx_ = pick<S, I + 1>(x0, x1, x2, x3); \
         wait_lds_reads();                                                                \
         __builtin_amdgcn_sched_barrier(0);                                               \
-        read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
-        mfma16(acc, a0, b0);                                                             \
-        interleave<16, 0, 8>();                                                          \
+        read_frags<TJ>(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                          \
+        mfma_block<TJ>(acc, a0, b0);                                                     \
+        interleave<MF, 0, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         wait_lds_reads();                                                                \
         wait_vmcnt<(S - 2) * COPIES>();                                                  \
         block_barrier();                                                                 \
-        read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
-        issue_stage(qw, qx, cp, min(kt + I + S, nk - 1), wave, cw_, cx_);                \
-        mfma16(acc, a1, b1);                                                             \
-        interleave<16, COPIES, 8>();                                                     \
+        read_frags<TJ>(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                          \
+        issue_stage<TJ>(qw, qx, cp, min(kt + I + S, nk - 1), wave, cw_, cx_);            \
+        mfma_block<TJ>(acc, a1, b1);                                                     \
+        interleave<MF, COPIES, RD>();                                                    \
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
 
@@ -297,47 +316,47 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
     for (; kt + S < nk; kt += S) {
         CONVROT_STEP(0);
         CONVROT_STEP(1);
-        if constexpr (S == 4) {
-            CONVROT_STEP(2);
-            CONVROT_STEP(3);
-        }
+        if constexpr (S >= 3) CONVROT_STEP(2);
+        if constexpr (S >= 4) CONVROT_STEP(3);
     }
     // nk is a multiple of S: S - 1 steps remain
     CONVROT_STEP(0);
-    if constexpr (S == 4) {
-        CONVROT_STEP(1);
-        CONVROT_STEP(2);
-    }
+    if constexpr (S >= 3) CONVROT_STEP(1);
+    if constexpr (S >= 4) CONVROT_STEP(2);
 #undef CONVROT_STEP
     {
         const int8_t *lw = pick<S, S - 1>(w0, w1, w2, w3), *lx = pick<S, S - 1>(x0, x1, x2, x3);
         wait_lds_reads();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(lw, lx, frow_w, frow_x, foff1, a1, b1);
-        mfma16(acc, a0, b0);
-        interleave<16, 0, 8>();
+        read_frags<TJ>(lw, lx, frow_w, frow_x, foff1, a1, b1);
+        mfma_block<TJ>(acc, a0, b0);
+        interleave<MF, 0, RD>();
         __builtin_amdgcn_sched_barrier(0);
-        mfma16(acc, a1, b1);
+        mfma_block<TJ>(acc, a1, b1);
     }
     // No copy may still be writing LDS when the workgroup moves on.
     wait_vmcnt<0>();
 }
 
-// One 256 (n) x 256 (m) output tile per 256-thread workgroup, one workgroup
-// per CU (256 AGPR accumulators per lane).  S: LDS stages (4 when the K-tile
-// count is a multiple of 4, else 2).
-template <int OUT, bool HAS_BIAS, int S>
-__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
+// One 256 (n) x 64 TJ (m) output tile per 256-thread workgroup; wave (wn, wm)
+// computes 128 (n) x 32 TJ (m).  TJ = 4: 256 AGPR accumulators, one workgroup
+// per CU.  TJ = 2: 128 accumulators, two workgroups per CU, so one
+// workgroup's barriers and epilogue overlap the other's matrix work.
+// S: LDS stages of (256 + 64 TJ) x 64 bytes; nk % S == 0.
+template <int OUT, bool HAS_BIAS, int TJ, int S, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_i8_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw,
     const float *__restrict__ sx, const float *__restrict__ sw,
     const float *__restrict__ bias, void *__restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, int tiles_per_xcd)
 {
-    constexpr int STAGE = kTile * kBK;   // 16 KiB per operand
-    __shared__ __attribute__((aligned(1024))) int8_t sw0[STAGE], sw1[STAGE], sw2[S == 4 ? STAGE : 16],
-        sw3[S == 4 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) int8_t sx0[STAGE], sx1[STAGE], sx2[S == 4 ? STAGE : 16],
-        sx3[S == 4 ? STAGE : 16];
+    constexpr int BM = 64 * TJ;
+    constexpr int SW = kTile * kBK;          // W stage bytes
+    constexpr int SX = BM * kBK;             // X stage bytes
+    __shared__ __attribute__((aligned(1024))) int8_t sw0[SW], sw1[SW], sw2[S >= 3 ? SW : 16],
+        sw3[S >= 4 ? SW : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t sx0[SX], sx1[SX], sx2[S >= 3 ? SX : 16],
+        sx3[S >= 4 ? SX : 16];
     __shared__ __attribute__((aligned(16))) float sscale[3][kTile];   // s_x, s_w, bias
 
     // ---- tile selection: XCD-contiguous ranges, grouped along m ----
@@ -349,84 +368,102 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int gsz = min(tiles_m - first_m, kGroup);
     const int tm = first_m + (t % width) % gsz;
     const int tn = (t % width) / gsz;
-    const int m0 = tm * kTile, n0 = tn * kTile;
+    const int m0 = tm * BM, n0 = tn * kTile;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
 
-    // ---- copy plan: a copy moves 16 rows x 64 B; wave w moves rows
-    // [(4w + j) 16, +16) of each operand; lane i takes row + i/4 and the chunk
-    // that belongs in slot i & 3 of that row ----
-    CopyPlan cp;
+    // ---- copy plan: a copy moves 16 rows x 64 B; lane i takes row + i/4 and
+    // the chunk that belongs in slot i & 3 of that row ----
+    CopyPlan<TJ> cp;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = (wave * 4 + j) * 16 + (lane >> 2);
-        const uint32_t c = ((lane & 3) ^ swz(r)) << 4;
-        cp.offw[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c;
-        cp.offx[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c;
+        cp.offw[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int r = (wave * TJ + j) * 16 + (lane >> 2);
+        cp.offx[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
     }
 
     // ---- fragment read assignment ----
     const int l32 = lane & 31, g = lane >> 5;
     const int foff0 = ((0 + g) ^ swz(l32)) << 4;
     const int foff1 = ((2 + g) ^ swz(l32)) << 4;
-    const int frow_w = (wn * 128 + l32) * kBK;   // + 2048 * i
-    const int frow_x = (wm * 128 + l32) * kBK;   // + 2048 * j
+    const int frow_w = (wn * 128 + l32) * kBK;       // + 2048 * i
+    const int frow_x = (wm * 32 * TJ + l32) * kBK;   // + 2048 * j
 
     // The tile's scales: plain loads issued ahead of the first K-tile copies,
     // written to LDS before the epilogue.
     float sc_x = 0.f, sc_w = 0.f, sc_b = 0.f;
     if constexpr (OUT != int(OutKind::I32)) {
-        sc_x = sx[min(m0 + tid, M - 1)];
+        sc_x = sx[min(m0 + (tid % BM), M - 1)];
         sc_w = sw[min(n0 + tid, N - 1)];
         if constexpr (HAS_BIAS) sc_b = bias[min(n0 + tid, N - 1)];
     }
 
-    v16i acc[4][4];
+    v16i acc[4][TJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    k_loop<S>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, qw, qx, cp, K / kBK, wave, frow_w,
-              frow_x, foff0, foff1, acc);
+    k_loop<TJ, S>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, qw, qx, cp, K / kBK, wave, frow_w,
+                  frow_x, foff0, foff1, acc);
 
     if constexpr (OUT != int(OutKind::I32)) {
-        sscale[0][tid] = sc_x;
+        if (tid < BM) sscale[0][tid] = sc_x;
         sscale[1][tid] = sc_w;
         sscale[2][tid] = sc_b;
     }
     __syncthreads();
 
     // ---- epilogue: lane holds n = nb..nb+3 of one m per (i, j, q) ----
-    if (m0 + kTile <= M && n0 + kTile <= N)
-        epilogue<OUT, HAS_BIAS, 4, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+    if (m0 + BM <= M && n0 + kTile <= N)
+        epilogue<OUT, HAS_BIAS, TJ, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
     else
-        epilogue<OUT, HAS_BIAS, 4, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+        epilogue<OUT, HAS_BIAS, TJ, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
 }
+
+template <int OUT, bool HAS_BIAS, int TJ, int S, int OCC>
+hipError_t launch_cfg(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
+                      const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
+                      hipStream_t stream)
+{
+    constexpr int BM = 64 * TJ;
+    const int tiles_m = (int)((M + BM - 1) / BM);
+    const int tiles_n = (int)((N + kTile - 1) / kTile);
+    const int tiles = tiles_m * tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, TJ, S, OCC>), dim3(8 * per_xcd),
+                       dim3(kThreads), 0, stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N,
+                       (int)K, tiles_m, tiles_n, per_xcd);
+    return hipGetLastError();
+}
+
+#ifndef CONVROT_GEMM_TJ
+#define CONVROT_GEMM_TJ 4
+#endif
 
 template <int OUT, bool HAS_BIAS>
 hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream)
 {
-    const int tiles_m = (int)((M + kTile - 1) / kTile);
-    const int tiles_n = (int)((N + kTile - 1) / kTile);
-    const int tiles = tiles_m * tiles_n;
-    const int per_xcd = (tiles + 7) / 8;
     const int nk = (int)(K / kBK);
-    if (nk % 4 == 0)
-        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 4>), dim3(8 * per_xcd), dim3(kThreads),
-                           0, stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m,
-                           tiles_n, per_xcd);
-    else
-        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 2>), dim3(8 * per_xcd), dim3(kThreads),
-                           0, stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m,
-                           tiles_n, per_xcd);
-    return hipGetLastError();
+    if constexpr (CONVROT_GEMM_TJ == 4) {
+        if (nk % 4 == 0)
+            return launch_cfg<OUT, HAS_BIAS, 4, 4, 1>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
+        return launch_cfg<OUT, HAS_BIAS, 4, 2, 1>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
+    } else {
+        if (nk % 3 == 0)
+            return launch_cfg<OUT, HAS_BIAS, 2, 3, 2>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
+        return launch_cfg<OUT, HAS_BIAS, 2, 2, 2>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
+    }
 }
 
 } // namespace
