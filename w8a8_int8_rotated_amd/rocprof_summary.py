@@ -1,0 +1,122 @@
+"""Summarise rocprofv3 CSV output into the short text files kept in profiles/.
+
+    python -m w8a8_int8_rotated_amd.rocprof_summary stats <run_kernel_stats.csv> \\
+        --command "<rocprofv3 command>" --workload qkv_38656 -o profiles/X.md
+    python -m w8a8_int8_rotated_amd.rocprof_summary traffic \\
+        --fetch <fetch run_counter_collection.csv> --write <write ...csv> \\
+        --copy-bytes 536870912 --kernel gemm_i8_kernel --source <kernel .hip> \\
+        --command-fetch "..." --command-write "..." -o profiles/Y.md
+
+`traffic` scales each counter by what it reads for the plain device copy of
+known size recorded in the same run (FETCH_SIZE and WRITE_SIZE are in KiB per
+dispatch), and records the SHA-256 of the kernel source so a reader (and
+bench.py) can tell whether the figure still applies to the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import sys
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "").replace("convrot::(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    out = [f"# Kernel durations -- {args.workload}", "",
+           "Command (run from /tmp, repository at $R):", "", "```", args.command, "```", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    out.append("")
+    text = "\n".join(out)
+    _emit(text, args.output)
+
+
+def _counter(path, counter):
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def _pick(agg, needle):
+    vals = [v for k, vs in agg.items() if needle in k for v in vs]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {needle!r}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def traffic(args):
+    fetch = _counter(args.fetch, "FETCH_SIZE")
+    write = _counter(args.write, "WRITE_SIZE")
+    cf, _ = _pick(fetch, COPY_KERNEL)
+    cw, _ = _pick(write, COPY_KERNEL)
+    kf, nf = _pick(fetch, args.kernel)
+    kw, nw = _pick(write, args.kernel)
+    sf = args.copy_bytes / (cf * 1024.0)
+    sw = args.copy_bytes / (cw * 1024.0)
+    rd = kf * 1024.0 * sf
+    wr = kw * 1024.0 * sw
+    sha = hashlib.sha256(open(args.source, "rb").read()).hexdigest()
+    out = [f"# HBM traffic of `{args.kernel}` -- {args.workload}", "",
+           "Commands (run from /tmp, repository at $R):", "", "```", args.command_fetch,
+           args.command_write, "```", "",
+           f"Calibration: the plain device copy `{COPY_KERNEL}` of {args.copy_bytes} bytes reads "
+           f"FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB per dispatch, so the scale "
+           f"factors are {sf:.4f} (fetch) and {sw:.4f} (write).", "",
+           "| counter | kernel dispatches | KiB per dispatch | scaled bytes per launch |",
+           "|---|---:|---:|---:|",
+           f"| FETCH_SIZE | {nf} | {kf:.0f} | {rd:.4g} |",
+           f"| WRITE_SIZE | {nw} | {kw:.0f} | {wr:.4g} |", "",
+           f"traffic_bytes_per_launch: {rd + wr:.6g}",
+           f"read_bytes_per_launch: {rd:.6g}",
+           f"write_bytes_per_launch: {wr:.6g}",
+           f"algorithmic_bytes_per_launch: {args.algorithmic_bytes:.6g}",
+           f"kernel_source_sha256: {sha}", ""]
+    _emit("\n".join(out), args.output)
+
+
+def _emit(text, path):
+    if path:
+        open(path, "w").write(text)
+    else:
+        sys.stdout.write(text)
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = p.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    s.add_argument("--workload", required=True)
+    s.add_argument("-o", "--output")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--algorithmic-bytes", type=float, default=0.0)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("-o", "--output")
+    a = p.parse_args()
+    stats(a) if a.cmd == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
