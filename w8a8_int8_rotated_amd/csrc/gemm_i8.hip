@@ -129,73 +129,93 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, p);
 }
 
-template <int OUT, bool HAS_BIAS>
-__device__ __forceinline__ void store4(void *Y, int64_t off, const v16i &acc, int q,
-                                       float sxm, const float4 &swv, const float4 &bv)
-{
-    if constexpr (OUT == int(OutKind::I32)) {
-        int4 o;
-        o.x = acc[4 * q + 0]; o.y = acc[4 * q + 1];
-        o.z = acc[4 * q + 2]; o.w = acc[4 * q + 3];
-        *reinterpret_cast<int4 *>(reinterpret_cast<int32_t *>(Y) + off) = o;
-    } else {
-        float y[4];
-        const float sw4[4] = {swv.x, swv.y, swv.z, swv.w};
-        const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float f = __fmul_rn(__fmul_rn((float)acc[4 * q + t], sxm), sw4[t]);
-            if constexpr (HAS_BIAS) f = __fadd_rn(f, b4[t]);
-            y[t] = f;
-        }
-        if constexpr (OUT == int(OutKind::F32)) {
-            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Y) + off) =
-                make_float4(y[0], y[1], y[2], y[3]);
-        } else {
-            if constexpr (OUT == int(OutKind::GELU_BF16)) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float u = __uint_as_float(f32_to_bf16_bits(y[t]) << 16);
-                    y[t] = gelu_erf(u);
-                }
-            }
-            uint2 o;
-            o.x = cvt_pk_bf16(y[0], y[1]);
-            o.y = cvt_pk_bf16(y[2], y[3]);
-            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(Y) + off) = o;
-        }
-    }
-}
 
 // Dequantise and store a wave's 128 x 128 block.  FULL: the tile lies inside
 // [M, N], so no per-lane bounds checks are needed.
+// fp32 value of one output: ((float)acc * s_x) * s_w (+ bias), optionally
+// followed by bf16 rounding and GELU (the MLP's up projection).
+template <int OUT, bool HAS_BIAS>
+__device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float bn)
+{
+    float f = __fmul_rn(__fmul_rn((float)acc, sxm), swn);
+    if constexpr (HAS_BIAS) f = __fadd_rn(f, bn);
+    if constexpr (OUT == int(OutKind::GELU_BF16))
+        f = gelu_erf(__uint_as_float(f32_to_bf16_bits(f) << 16));
+    return f;
+}
+
+// Dequantise and store a wave's 128 (n) x 32 TJ (m) block.  FULL: the tile
+// lies inside [M, N], so no per-lane bounds checks are needed.
+//
+// Accumulator layout: lane (l32, g) holds, for sub-tile (i, j) and q = 0..3,
+// n = 32 i + 8 q + 4 g + 0..3 of row m = 32 j + l32.  For bf16 outputs the two
+// lanes of a row exchange halves with v_permlane32_swap so that each holds
+// 8 consecutive columns (16 bytes): the lower lane n = 32 i + 16 p + 0..7, the
+// upper lane + 8..15, for q = 2p, 2p + 1.  Rows are the outer loop so the
+// 16-byte stores of one 128-byte line leave back to back.
 template <int OUT, bool HAS_BIAS, int TJ, bool FULL>
 __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                                          const float (&sscale)[3][kTile], int M, int N,
                                          int m0, int n0, int wm, int wn, int l32, int g)
 {
-    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    float sxm[TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-        sxm[j] = (OUT == int(OutKind::I32)) ? 0.0f : sscale[0][wm * 32 * TJ + 32 * j + l32];
+    for (int j = 0; j < TJ; ++j) {
+        const int ml = wm * 32 * TJ + 32 * j + l32;
+        const int m = m0 + ml;
+        if (!FULL && m >= M) continue;
+        const float sxm = (OUT == int(OutKind::I32)) ? 0.0f : sscale[0][ml];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (OUT == int(OutKind::I32) || OUT == int(OutKind::F32)) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
-            const int nb = n0 + nl;
-            if (!FULL && nb >= N) continue;
-            float4 swv = zero4, bv = zero4;
-            if constexpr (OUT != int(OutKind::I32)) {
-                swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
-                if constexpr (HAS_BIAS) bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
+                    const int nb = n0 + nl;
+                    if (!FULL && nb >= N) continue;
+                    const int64_t off = (int64_t)m * N + nb;
+                    if constexpr (OUT == int(OutKind::I32)) {
+                        int4 o;
+                        o.x = acc[i][j][4 * q + 0]; o.y = acc[i][j][4 * q + 1];
+                        o.z = acc[i][j][4 * q + 2]; o.w = acc[i][j][4 * q + 3];
+                        *reinterpret_cast<int4 *>(reinterpret_cast<int32_t *>(Y) + off) = o;
+                    } else {
+                        const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
+                        const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
+                        float4 o;
+                        o.x = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 0], sxm, swv.x, bv.x);
+                        o.y = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 1], sxm, swv.y, bv.y);
+                        o.z = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 2], sxm, swv.z, bv.z);
+                        o.w = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 3], sxm, swv.w, bv.w);
+                        *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Y) + off) = o;
+                    }
+                }
+            } else {
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const int m = m0 + wm * 32 * TJ + 32 * j + l32;
-                if (!FULL && m >= M) continue;
-                store4<OUT, HAS_BIAS>(Y, (int64_t)m * N + nb, acc[i][j], q, sxm[j], swv, bv);
+                for (int p = 0; p < 2; ++p) {
+                    uint32_t d[2][2];   // [q - 2p][dword]
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int q = 2 * p + h;
+                        const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
+                        const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
+                        const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
+                        d[h][0] = cvt_pk_bf16(
+                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 0], sxm, swv.x, bv.x),
+                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 1], sxm, swv.y, bv.y));
+                        d[h][1] = cvt_pk_bf16(
+                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 2], sxm, swv.z, bv.z),
+                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 3], sxm, swv.w, bv.w));
+                    }
+                    // upper lanes' q = 2p half <-> lower lanes' q = 2p + 1 half
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(d[0][0], d[1][0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(d[0][1], d[1][1], false, false);
+                    const int nb = n0 + wn * 128 + 32 * i + 16 * p + 8 * g;
+                    if (!FULL && nb >= N) continue;
+                    uint4 o;
+                    o.x = s0[0]; o.y = s1[0]; o.z = s0[1]; o.w = s1[1];
+                    *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(Y) +
+                                               (int64_t)m * N + nb) = o;
+                }
             }
         }
     }
