@@ -15,17 +15,22 @@
 // v_mfma_i32_32x32x32_i8 (256 int32 accumulators per lane, held in AGPRs).
 // The weight tile is the MFMA A operand (rows = n) and the activation tile
 // the B operand (columns = m), so an accumulator lane holds 4 consecutive n of
-// one m and the epilogue stores 4 outputs per instruction.
+// one m; in the bf16 epilogue lane pairs exchange halves with
+// v_permlane32_swap so that every lane stores 16 contiguous bytes.
 //
-// K pipeline: K advances 64 bytes per stage; STAGES stages of 32 KiB (W and X
+// Persistent schedule: one workgroup per CU walks a sequence of tiles, and the
+// copy stream runs on across tile boundaries, so the next tile's first
+// K-tiles land while the current one is dequantised and stored.
+//
+// K pipeline: K advances 64 bytes per K-tile; S stages of 32 KiB (W and X
 // tiles, 256 rows x 64 B each) live in LDS.  Global -> LDS copies use the
-// direct-to-LDS load (global_load_lds_dwordx4: each lane fetches 16 bytes and
-// the wave's 1 KiB lands contiguously in LDS), so no registers stage the
-// tiles and no LDS write instructions are issued.  Tile kt + STAGES is
-// requested as soon as stage kt is consumed, STAGES - 1 tiles ahead of use.
-// The compiler does not order LDS reads after these copies, so every wait is
-// explicit: s_waitcnt vmcnt(n) for this wave's copies, then a barrier for the
-// other waves'.
+// direct-to-LDS buffer load (buffer_load_dwordx4 ... lds: each lane fetches
+// 16 bytes and the wave's 1 KiB lands contiguously in LDS), so no registers
+// stage the tiles and no LDS write instructions are issued.  The copies of
+// each K-tile are split over the two halves of a step and spread between the
+// MFMAs, which keeps the texture-address queue from filling.  Every wait on a
+// copy is explicit: s_waitcnt vmcnt(n) for this wave's copies, then a barrier
+// for the other waves'.
 //
 // LDS rows are 64 bytes; chunk c (16 B) of tile row r sits at slot
 // c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A copy instruction writes 16
@@ -37,6 +42,7 @@
 // tiles, grouped 8 tile-rows high, for L2 reuse of both operands.
 #include "common.hpp"
 
+#include <algorithm>
 #include <utility>
 
 namespace convrot {
@@ -49,6 +55,8 @@ constexpr int kTile = 256;     // tile edge in m and in n
 constexpr int kBK = 64;        // K bytes per LDS stage
 constexpr int kThreads = 256;
 constexpr int kGroup = 8;      // tile-rows per L2 group
+// buffer resource word 3: raw (untyped) 32-bit data format, no swizzle
+constexpr int kRsrcWord3 = 0x00020000;
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
@@ -58,17 +66,6 @@ __device__ __forceinline__ void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Wait until at most `tiles` stages of this wave's copies (COPIES each) are
-// still in flight.
-template <int COPIES>
-__device__ __forceinline__ void wait_copies(int tiles)
-{
-    if (tiles >= 3) wait_vmcnt<3 * COPIES>();
-    else if (tiles == 2) wait_vmcnt<2 * COPIES>();
-    else if (tiles == 1) wait_vmcnt<1 * COPIES>();
-    else wait_vmcnt<0>();
 }
 
 // s_waitcnt lgkmcnt(0) with vmcnt/expcnt left unconstrained.
@@ -84,18 +81,16 @@ constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
 
 // Order the current scheduling region so that LDS reads and global->LDS
 // copies trickle out between matrix instructions instead of blocking issue in
-// a burst: the memory instructions (all LDS reads first, then all copies --
-// a read placed after a copy in the same block would get a conservative vmcnt
-// wait on that copy) are spread evenly behind the MFMAs.
+// bursts: the reads take every other MFMA slot from the first, the copies are
+// spread evenly from the last slot backwards, so neither the LDS nor the
+// texture-address queue sees the whole wave's requests at once.
 template <int MFMAS, int VMEMS, int DSREADS, int K>
 __device__ __forceinline__ void interleave_slot()
 {
-    constexpr int TOTAL = VMEMS + DSREADS;
-    // memory ops whose share falls in MFMA slot K: ops [LO, HI)
-    constexpr int LO = (K * TOTAL + MFMAS - 1) / MFMAS;
-    constexpr int HI = ((K + 1) * TOTAL + MFMAS - 1) / MFMAS;
-    constexpr int RD_LO = LO < DSREADS ? LO : DSREADS, RD_HI = HI < DSREADS ? HI : DSREADS;
-    constexpr int VM_LO = LO > DSREADS ? LO : DSREADS, VM_HI = HI > DSREADS ? HI : DSREADS;
+    // reads [RD_LO, RD_HI) and copies [VM_LO, VM_HI) follow MFMA slot K
+    constexpr int RD_LO = (K * DSREADS + MFMAS - 1) / MFMAS;
+    constexpr int RD_HI = ((K + 1) * DSREADS + MFMAS - 1) / MFMAS;
+    constexpr int VM_LO = (K * VMEMS) / MFMAS, VM_HI = ((K + 1) * VMEMS) / MFMAS;
     __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
     if constexpr (RD_HI > RD_LO) __builtin_amdgcn_sched_group_barrier(kSgDsRead, RD_HI - RD_LO, 0);
     if constexpr (VM_HI > VM_LO) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, VM_HI - VM_LO, 0);
@@ -111,12 +106,6 @@ template <int MFMAS, int VMEMS, int DSREADS>
 __device__ __forceinline__ void interleave()
 {
     interleave_all<MFMAS, VMEMS, DSREADS>(std::make_integer_sequence<int, MFMAS>{});
-}
-
-__device__ __forceinline__ void copy16(const int8_t *g, int8_t *lds)
-{
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(g),
-                                     (__attribute__((address_space(3))) void *)(lds), 16, 0, 0);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -153,6 +142,21 @@ __device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float b
 // 8 consecutive columns (16 bytes): the lower lane n = 32 i + 16 p + 0..7, the
 // upper lane + 8..15, for q = 2p, 2p + 1.  Rows are the outer loop so the
 // 16-byte stores of one 128-byte line leave back to back.
+// Copy one accumulator fragment from AGPRs to VGPRs where it is used.  Left
+// to itself the compiler copies the whole tile at once after the K loop
+// (the values cross basic blocks), which does not fit in 256 VGPRs.
+__device__ __forceinline__ v16i acc_frag(const v16i &a)
+{
+    v16i v;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        int x;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(a[e]));
+        v[e] = x;
+    }
+    return v;
+}
+
 template <int OUT, bool HAS_BIAS, int TJ, bool FULL>
 __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                                          const float (&sscale)[3][kTile], int M, int N,
@@ -166,6 +170,7 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
         const float sxm = (OUT == int(OutKind::I32)) ? 0.0f : sscale[0][ml];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const v16i av = OUT == int(OutKind::I32) ? acc[i][j] : acc_frag(acc[i][j]);
             if constexpr (OUT == int(OutKind::I32) || OUT == int(OutKind::F32)) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -182,10 +187,10 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                         const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
                         const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
                         float4 o;
-                        o.x = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 0], sxm, swv.x, bv.x);
-                        o.y = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 1], sxm, swv.y, bv.y);
-                        o.z = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 2], sxm, swv.z, bv.z);
-                        o.w = dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 3], sxm, swv.w, bv.w);
+                        o.x = dequant1<OUT, HAS_BIAS>(av[4 * q + 0], sxm, swv.x, bv.x);
+                        o.y = dequant1<OUT, HAS_BIAS>(av[4 * q + 1], sxm, swv.y, bv.y);
+                        o.z = dequant1<OUT, HAS_BIAS>(av[4 * q + 2], sxm, swv.z, bv.z);
+                        o.w = dequant1<OUT, HAS_BIAS>(av[4 * q + 3], sxm, swv.w, bv.w);
                         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(Y) + off) = o;
                     }
                 }
@@ -200,11 +205,11 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                         const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
                         const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
                         d[h][0] = cvt_pk_bf16(
-                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 0], sxm, swv.x, bv.x),
-                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 1], sxm, swv.y, bv.y));
+                            dequant1<OUT, HAS_BIAS>(av[4 * q + 0], sxm, swv.x, bv.x),
+                            dequant1<OUT, HAS_BIAS>(av[4 * q + 1], sxm, swv.y, bv.y));
                         d[h][1] = cvt_pk_bf16(
-                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 2], sxm, swv.z, bv.z),
-                            dequant1<OUT, HAS_BIAS>(acc[i][j][4 * q + 3], sxm, swv.w, bv.w));
+                            dequant1<OUT, HAS_BIAS>(av[4 * q + 2], sxm, swv.z, bv.z),
+                            dequant1<OUT, HAS_BIAS>(av[4 * q + 3], sxm, swv.w, bv.w));
                     }
                     // upper lanes' q = 2p half <-> lower lanes' q = 2p + 1 half
                     const auto s0 = __builtin_amdgcn_permlane32_swap(d[0][0], d[1][0], false, false);
@@ -217,54 +222,84 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                                                (int64_t)m * N + nb) = o;
                 }
             }
+            // keep the scheduler from hoisting every accumulator read and
+            // scale load of the tile, which would not fit in registers
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// Per-wave state of the K loop, kept in registers.
-template <int TJ>
-struct CopyPlan {
-    uint32_t offw[4];    // byte offsets of this lane's 16-byte W chunks, per copy
-    uint32_t offx[TJ];   // same for X
+// Copies of one tile go through buffer resources whose base is the tile's
+// first row and whose size ends at the matrix's last row, so rows past the end
+// are out of range and read as zero (they only feed outputs that are never
+// stored).  Per lane, the offset within a tile is the same for both operands
+// and for every tile: copy j of wave w moves rows [(4w + j) 16, +16) x 64 B,
+// and lane i takes row + i/4 and the chunk that belongs in slot i & 3 of it.
+struct TileSrc {
+    __amdgpu_buffer_rsrc_t w, x;
 };
 
-// Direct-to-LDS copies of K-tile `kt` into one stage (wave-uniform LDS bases):
-// wave w fills W rows [(4w + j) 16, +16) and X rows [(TJ w + j) 16, +16).
-template <int TJ>
-__device__ __forceinline__ void issue_stage(const int8_t *qw, const int8_t *qx,
-                                            const CopyPlan<TJ> &cp, int kt, int wave,
-                                            int8_t *__restrict__ dst_w,
-                                            int8_t *__restrict__ dst_x)
+__device__ __forceinline__ TileSrc tile_src(const int8_t *qw, const int8_t *qx, int m0, int n0,
+                                            int M, int N, int K)
 {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        copy16(qw + kt * kBK + cp.offw[j], dst_w + (wave * 4 + j) * 1024);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-        copy16(qx + kt * kBK + cp.offx[j], dst_x + (wave * TJ + j) * 1024);
+    TileSrc t;
+    t.w = __builtin_amdgcn_make_buffer_rsrc((void *)(qw + (int64_t)n0 * K), (short)0,
+                                            (N - n0) * K, kRsrcWord3);
+    t.x = __builtin_amdgcn_make_buffer_rsrc((void *)(qx + (int64_t)m0 * K), (short)0,
+                                            (M - m0) * K, kRsrcWord3);
+    return t;
 }
 
-template <int TJ>
+__device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t (&voff)[4])
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 16 + (lane >> 2);
+        voff[j] = (uint32_t)r * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
+    }
+}
+
+// Half H of K-tile `k` of the copy stream into one stage: copies j = 2H and
+// 2H + 1 of both operands.  Below nk the K-tile belongs to the current tile,
+// from nk on to the next one (the last tile of a workgroup re-reads its own
+// first K-tiles, which no one consumes).
+template <int H>
+__device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nxt,
+                                           const uint32_t (&voff)[4], int k, int nk, int wave,
+                                           int8_t *__restrict__ dst_w, int8_t *__restrict__ dst_x)
+{
+    const bool next = k >= nk;
+    const __amdgpu_buffer_rsrc_t rw = next ? nxt.w : cur.w, rx = next ? nxt.x : cur.x;
+    const int soff = (next ? k - nk : k) * kBK;
+#pragma unroll
+    for (int j = 2 * H; j < 2 * H + 2; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rw, (__attribute__((address_space(3))) void *)(dst_w + (wave * 4 + j) * 1024), 16,
+            voff[j], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (__attribute__((address_space(3))) void *)(dst_x + (wave * 4 + j) * 1024), 16,
+            voff[j], soff, 0, 0);
+    }
+}
+
 __device__ __forceinline__ void read_frags(const int8_t *__restrict__ sw_,
                                            const int8_t *__restrict__ sx_, int frow_w,
-                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[TJ])
+                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[4])
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
         a[i] = *reinterpret_cast<const v4i *>(sw_ + frow_w + 2048 * i + foff);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-        b[j] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * j + foff);
+        b[i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * i + foff);
+    }
 }
 
-template <int TJ>
-__device__ __forceinline__ void mfma_block(v16i (&acc)[4][TJ], const v4i (&a)[4],
-                                           const v4i (&b)[TJ])
+__device__ __forceinline__ void mfma_block(v16i (&acc)[4][4], const v4i (&a)[4],
+                                           const v4i (&b)[4])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+        for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
@@ -275,59 +310,85 @@ __device__ __forceinline__ int8_t *pick(int8_t *p0, int8_t *p1, int8_t *p2, int8
     return k == 0 ? p0 : k == 1 ? p1 : k == 2 ? p2 : p3;
 }
 
-// The K loop over one tile.  Each LDS stage is a separate object reached
-// through its own restrict pointer, and the loop is unrolled by the stage
-// count so every access names its stage at compile time.  That lets the
-// compiler prove that an LDS read of one stage does not depend on copies still
-// landing in another, so it only waits (vmcnt) for copies into the stage being
-// read.  Waiting for the other waves' copies is explicit: each wave retires
-// its own copies of the next K-tile, then all meet at a barrier.
-// Requires nk % S == 0.
-template <int TJ, int S>
+template <int N1, int N2>
+__device__ __forceinline__ void wait_vmcnt_either(bool second)
+{
+    if (second) wait_vmcnt<N2>();
+    else wait_vmcnt<N1>();
+}
+
+// The K loop of one tile, in a stream of tiles.  Each LDS stage is a separate
+// object reached through its own restrict pointer, and the loop is unrolled
+// by the stage count so every access names its stage at compile time: the
+// compiler then proves that an LDS read of one stage does not depend on copies
+// still landing in another and only waits for copies into the stage read.
+// Waiting for the other waves' copies is explicit: each wave retires its own
+// copies of the next K-tile, then all meet at a barrier.
+//
+// Step k (K-tile k, stage k % S) runs the MFMAs of its two 32-byte sub-steps.
+// Its first half reads the sub-step-1 fragments and copies the second half of
+// stream K-tile k + S - 1 into stage (k - 1) % S (free since step k - 1's
+// barrier); its second half, after the barrier, reads the next K-tile's
+// sub-step-0 fragments and copies the first half of K-tile k + S into stage
+// k % S.  Copies of a K-tile are thus issued in stream order, 8 per wave.
+//
+// On entry: first == true -> nothing is in flight and every stage is free;
+// first == false -> K-tiles 0 .. S-2 of this tile are in flight, issued during
+// the previous tile, followed by EPI younger memory operations per wave (the
+// previous tile's stores and this tile's scale loads); stage S-1 is free.
+// On exit: K-tiles 0 .. S-2 of the next tile are in flight.  Requires
+// nk % S == 0.
+template <int S, int EPI>
 __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
                                        int8_t *__restrict__ w2, int8_t *__restrict__ w3,
                                        int8_t *__restrict__ x0, int8_t *__restrict__ x1,
                                        int8_t *__restrict__ x2, int8_t *__restrict__ x3,
-                                       const int8_t *qw, const int8_t *qx,
-                                       const CopyPlan<TJ> &cp, int nk, int wave, int frow_w,
-                                       int frow_x, int foff0, int foff1,
-                                       v16i (&acc)[4][TJ])
+                                       const TileSrc &cur, const TileSrc &nxt,
+                                       const uint32_t (&voff)[4], int nk, bool first, int wave,
+                                       int frow_w, int frow_x, int foff0, int foff1,
+                                       v16i (&acc)[4][4])
 {
-    static_assert(S >= 2 && S <= 4, "stages");
-    constexpr int COPIES = 4 + TJ;           // copy instructions per wave per K-tile
-    constexpr int MF = 4 * TJ;               // MFMAs per sub-step
-    constexpr int RD = 4 + TJ;               // fragment reads per sub-step
-    v4i a0[4], b0[TJ], a1[4], b1[TJ];
+    static_assert(S == 2 || S == 4, "stages");
+    constexpr int C = 8;                     // copy instructions per wave per K-tile
+    constexpr int CH = C / 2;                // ... per half
+    static_assert((S - 2) * C + CH + EPI < 64, "vmcnt range");
+    v4i a0[4], b0[4], a1[4], b1[4];
+    int8_t *const wl = pick<S, S - 1>(w0, w1, w2, w3), *const xl = pick<S, S - 1>(x0, x1, x2, x3);
 
-    // prologue: every stage starts free
-    issue_stage<TJ>(qw, qx, cp, 0, wave, w0, x0);
-    issue_stage<TJ>(qw, qx, cp, min(1, nk - 1), wave, w1, x1);
-    if constexpr (S >= 3) issue_stage<TJ>(qw, qx, cp, min(2, nk - 1), wave, w2, x2);
-    if constexpr (S >= 4) issue_stage<TJ>(qw, qx, cp, min(3, nk - 1), wave, w3, x3);
-    wait_vmcnt<(S - 1) * COPIES>();
+    if (first) {
+        issue_half<0>(cur, nxt, voff, 0, nk, wave, w0, x0);
+        issue_half<1>(cur, nxt, voff, 0, nk, wave, w0, x0);
+        if constexpr (S == 4) {
+            issue_half<0>(cur, nxt, voff, 1, nk, wave, w1, x1);
+            issue_half<1>(cur, nxt, voff, 1, nk, wave, w1, x1);
+            issue_half<0>(cur, nxt, voff, 2, nk, wave, w2, x2);
+            issue_half<1>(cur, nxt, voff, 2, nk, wave, w2, x2);
+        }
+    }
+    issue_half<0>(cur, nxt, voff, S - 1, nk, wave, wl, xl);
+    wait_vmcnt_either<(S - 2) * C + CH + EPI, (S - 2) * C + CH>(first);
     block_barrier();
-    read_frags<TJ>(w0, x0, frow_w, frow_x, foff0, a0, b0);
+    read_frags(w0, x0, frow_w, frow_x, foff0, a0, b0);
 
-    // One step = the second half of K-tile kt (MFMAs on the sub-step-1
-    // fragments, with the reads of tile kt+1's sub-step 0 and the copies of
-    // tile kt+S interleaved) and the first half of tile kt+1.
 #define CONVROT_STEP(I)                                                                  \
     do {                                                                                 \
+        int8_t *pw_ = pick<S, I + S - 1>(w0, w1, w2, w3), *px_ = pick<S, I + S - 1>(x0, x1, x2, x3); \
         int8_t *cw_ = pick<S, I>(w0, w1, w2, w3), *cx_ = pick<S, I>(x0, x1, x2, x3);      \
         int8_t *nw_ = pick<S, I + 1>(w0, w1, w2, w3), *nx_ = pick<S, I + 1>(x0, x1, x2, x3); \
         wait_lds_reads();                                                                \
         __builtin_amdgcn_sched_barrier(0);                                               \
-        read_frags<TJ>(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                          \
-        mfma_block<TJ>(acc, a0, b0);                                                     \
-        interleave<MF, 0, RD>();                                                         \
+        read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
+        issue_half<1>(cur, nxt, voff, kt + (I) + S - 1, nk, wave, pw_, px_);             \
+        mfma_block(acc, a0, b0);                                                         \
+        interleave<16, CH, 8>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         wait_lds_reads();                                                                \
-        wait_vmcnt<(S - 2) * COPIES>();                                                  \
+        wait_vmcnt_either<(S - 2) * C, (S - 2) * C + EPI>(!first && kt + (I) < S - 2);   \
         block_barrier();                                                                 \
-        read_frags<TJ>(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                          \
-        issue_stage<TJ>(qw, qx, cp, min(kt + I + S, nk - 1), wave, cw_, cx_);            \
-        mfma_block<TJ>(acc, a1, b1);                                                     \
-        interleave<MF, COPIES, RD>();                                                    \
+        read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
+        issue_half<0>(cur, nxt, voff, kt + (I) + S, nk, wave, cw_, cx_);                 \
+        mfma_block(acc, a1, b1);                                                         \
+        interleave<16, CH, 8>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
 
@@ -336,154 +397,184 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
     for (; kt + S < nk; kt += S) {
         CONVROT_STEP(0);
         CONVROT_STEP(1);
-        if constexpr (S >= 3) CONVROT_STEP(2);
-        if constexpr (S >= 4) CONVROT_STEP(3);
+        if constexpr (S == 4) {
+            CONVROT_STEP(2);
+            CONVROT_STEP(3);
+        }
     }
-    // nk is a multiple of S: S - 1 steps remain
     CONVROT_STEP(0);
-    if constexpr (S >= 3) CONVROT_STEP(1);
-    if constexpr (S >= 4) CONVROT_STEP(2);
+    if constexpr (S == 4) {
+        CONVROT_STEP(1);
+        CONVROT_STEP(2);
+    }
 #undef CONVROT_STEP
+    // K-tile nk - 1: no barrier, nothing to overwrite but stage S - 2
     {
-        const int8_t *lw = pick<S, S - 1>(w0, w1, w2, w3), *lx = pick<S, S - 1>(x0, x1, x2, x3);
         wait_lds_reads();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags<TJ>(lw, lx, frow_w, frow_x, foff1, a1, b1);
-        mfma_block<TJ>(acc, a0, b0);
-        interleave<MF, 0, RD>();
+        read_frags(wl, xl, frow_w, frow_x, foff1, a1, b1);
+        issue_half<1>(cur, nxt, voff, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
+                      pick<S, S - 2>(x0, x1, x2, x3));
+        mfma_block(acc, a0, b0);
+        interleave<16, CH, 8>();
         __builtin_amdgcn_sched_barrier(0);
-        mfma_block<TJ>(acc, a1, b1);
+        mfma_block(acc, a1, b1);
     }
-    // No copy may still be writing LDS when the workgroup moves on.
-    wait_vmcnt<0>();
 }
 
-// One 256 (n) x 64 TJ (m) output tile per 256-thread workgroup; wave (wn, wm)
-// computes 128 (n) x 32 TJ (m).  TJ = 4: 256 AGPR accumulators, one workgroup
-// per CU.  TJ = 2: 128 accumulators, two workgroups per CU, so one
-// workgroup's barriers and epilogue overlap the other's matrix work.
-// S: LDS stages of (256 + 64 TJ) x 64 bytes; nk % S == 0.
-template <int OUT, bool HAS_BIAS, int TJ, int S, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_i8_kernel(
+// Persistent GEMM: one 256-thread workgroup per CU walks a sequence of
+// 256 (n) x 256 (m) output tiles; wave (wn, wm) computes 128 x 128 of each in
+// 256 AGPR accumulators.  The copy stream runs across tile boundaries, so the
+// next tile's first K-tiles land while the current one is dequantised and
+// stored, and its stores drain while the next tile computes.
+// S: LDS stages of 2 x 16 KiB (4 when nk % 4 == 0, else 2).
+template <int OUT, bool HAS_BIAS, int S>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw,
     const float *__restrict__ sx, const float *__restrict__ sw,
     const float *__restrict__ bias, void *__restrict__ Y, int M, int N, int K,
-    int tiles_m, int tiles_n, int tiles_per_xcd)
+    int tiles_m, int tiles_n, int tiles_per_xcd, int wgs_per_xcd)
 {
-    constexpr int BM = 64 * TJ;
-    constexpr int SW = kTile * kBK;          // W stage bytes
-    constexpr int SX = BM * kBK;             // X stage bytes
-    __shared__ __attribute__((aligned(1024))) int8_t sw0[SW], sw1[SW], sw2[S >= 3 ? SW : 16],
-        sw3[S >= 4 ? SW : 16];
-    __shared__ __attribute__((aligned(1024))) int8_t sx0[SX], sx1[SX], sx2[S >= 3 ? SX : 16],
-        sx3[S >= 4 ? SX : 16];
+    constexpr int STG = kTile * kBK;   // 16 KiB per operand
+    constexpr bool BF16_OUT = OUT == int(OutKind::BF16) || OUT == int(OutKind::GELU_BF16);
+    constexpr int NSCALE = OUT == int(OutKind::I32) ? 0 : (HAS_BIAS ? 3 : 2);
+    // memory operations per wave between a tile's K-tile S-2 copies and its
+    // K-tile S-1 copies: the previous tile's stores (bf16: 4 x 4 x 2 of 16 B)
+    // and this tile's scale loads; other outputs drain at the tile boundary
+    constexpr int EPI = (BF16_OUT ? 32 : 0) + NSCALE;
+    __shared__ __attribute__((aligned(1024))) int8_t sw0[STG], sw1[STG], sw2[S == 4 ? STG : 16],
+        sw3[S == 4 ? STG : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t sx0[STG], sx1[STG], sx2[S == 4 ? STG : 16],
+        sx3[S == 4 ? STG : 16];
     __shared__ __attribute__((aligned(16))) float sscale[3][kTile];   // s_x, s_w, bias
 
-    // ---- tile selection: XCD-contiguous ranges, grouped along m ----
-    const int pid = blockIdx.x;
-    const int t = (pid & 7) * tiles_per_xcd + (pid >> 3);
-    if (t >= tiles_m * tiles_n) return;
-    const int width = kGroup * tiles_n;
-    const int first_m = (t / width) * kGroup;
-    const int gsz = min(tiles_m - first_m, kGroup);
-    const int tm = first_m + (t % width) % gsz;
-    const int tn = (t % width) / gsz;
-    const int m0 = tm * BM, n0 = tn * kTile;
-
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave & 1, wm = wave >> 1;
+    const int tiles = tiles_m * tiles_n;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int nk = K / kBK;
 
-    // ---- copy plan: a copy moves 16 rows x 64 B; lane i takes row + i/4 and
-    // the chunk that belongs in slot i & 3 of that row ----
-    CopyPlan<TJ> cp;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 16 + (lane >> 2);
-        cp.offw[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-        const int r = (wave * TJ + j) * 16 + (lane >> 2);
-        cp.offx[j] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
-    }
+    // i-th tile of this workgroup (XCD-contiguous ranges, grouped along m),
+    // or false past the end
+    auto tile_at = [&](int i, int &m0, int &n0) -> bool {
+        const int tl = slot + i * wgs_per_xcd;
+        const int t = xcd * tiles_per_xcd + tl;
+        if (tl >= tiles_per_xcd || t >= tiles) return false;
+        const int width = kGroup * tiles_n;
+        const int first_m = (t / width) * kGroup;
+        const int gsz = min(tiles_m - first_m, kGroup);
+        m0 = (first_m + (t % width) % gsz) * kTile;
+        n0 = ((t % width) / gsz) * kTile;
+        return true;
+    };
 
-    // ---- fragment read assignment ----
+    int m0, n0;
+    if (!tile_at(0, m0, n0)) return;
+
     const int l32 = lane & 31, g = lane >> 5;
     const int foff0 = ((0 + g) ^ swz(l32)) << 4;
     const int foff1 = ((2 + g) ^ swz(l32)) << 4;
-    const int frow_w = (wn * 128 + l32) * kBK;       // + 2048 * i
-    const int frow_x = (wm * 32 * TJ + l32) * kBK;   // + 2048 * j
+    const int frow_w = (wn * 128 + l32) * kBK;   // + 2048 * i
+    const int frow_x = (wm * 128 + l32) * kBK;   // + 2048 * j
 
-    // The tile's scales: plain loads issued ahead of the first K-tile copies,
-    // written to LDS before the epilogue.
+    auto load_scales = [&](int m0_, int n0_, float &a, float &b, float &c) {
+        if constexpr (OUT != int(OutKind::I32)) {
+            a = sx[min(m0_ + tid, M - 1)];
+            b = sw[min(n0_ + tid, N - 1)];
+            if constexpr (HAS_BIAS) c = bias[min(n0_ + tid, N - 1)];
+        }
+    };
+
     float sc_x = 0.f, sc_w = 0.f, sc_b = 0.f;
-    if constexpr (OUT != int(OutKind::I32)) {
-        sc_x = sx[min(m0 + (tid % BM), M - 1)];
-        sc_w = sw[min(n0 + tid, N - 1)];
-        if constexpr (HAS_BIAS) sc_b = bias[min(n0 + tid, N - 1)];
+    load_scales(m0, n0, sc_x, sc_w, sc_b);
+    uint32_t voff[4];
+    lane_offsets(K, wave, lane, voff);
+    TileSrc cur = tile_src(qw, qx, m0, n0, M, N, K);
+    int nm0 = m0, nn0 = n0;
+    bool more = tile_at(1, nm0, nn0);
+    TileSrc nxt = more ? tile_src(qw, qx, nm0, nn0, M, N, K) : cur;
+
+    for (int it = 0;; ++it) {
+        v16i acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+        k_loop<S, EPI>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voff, nk, it == 0,
+                       wave, frow_w, frow_x, foff0, foff1, acc);
+
+        if constexpr (OUT != int(OutKind::I32)) {
+            sscale[0][tid] = sc_x;
+            sscale[1][tid] = sc_w;
+            sscale[2][tid] = sc_b;
+        }
+        // not __syncthreads(): its fence would also wait for the next tile's
+        // copies already in flight
+        wait_lds_reads();
+        block_barrier();
+        const bool full = m0 + kTile <= M && n0 + kTile <= N;
+        if (full)
+            epilogue<OUT, HAS_BIAS, 4, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+        else
+            epilogue<OUT, HAS_BIAS, 4, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+
+        if (!more) break;
+        // The next tile's waits count exactly EPI operations issued after its
+        // first copies.  A partial tile issues fewer stores (and other outputs
+        // more), so drain them: every copy issued so far has then landed.
+        if (!BF16_OUT || !full) wait_vmcnt<0>();
+        m0 = nm0;
+        n0 = nn0;
+        cur = nxt;
+        load_scales(m0, n0, sc_x, sc_w, sc_b);
+        more = tile_at(it + 2, nm0, nn0);
+        if (more) nxt = tile_src(qw, qx, nm0, nn0, M, N, K);
+        // sscale is rewritten only after the next K loop's barriers
     }
-
-    v16i acc[4][TJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-
-    k_loop<TJ, S>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, qw, qx, cp, K / kBK, wave, frow_w,
-                  frow_x, foff0, foff1, acc);
-
-    if constexpr (OUT != int(OutKind::I32)) {
-        if (tid < BM) sscale[0][tid] = sc_x;
-        sscale[1][tid] = sc_w;
-        sscale[2][tid] = sc_b;
-    }
-    __syncthreads();
-
-    // ---- epilogue: lane holds n = nb..nb+3 of one m per (i, j, q) ----
-    if (m0 + BM <= M && n0 + kTile <= N)
-        epilogue<OUT, HAS_BIAS, TJ, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
-    else
-        epilogue<OUT, HAS_BIAS, TJ, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+    // No copy may still be writing LDS when the workgroup ends.
+    wait_vmcnt<0>();
 }
 
-template <int OUT, bool HAS_BIAS, int TJ, int S, int OCC>
-hipError_t launch_cfg(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
-                      const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
-                      hipStream_t stream)
+int cu_count()
 {
-    constexpr int BM = 64 * TJ;
-    const int tiles_m = (int)((M + BM - 1) / BM);
-    const int tiles_n = (int)((N + kTile - 1) / kTile);
-    const int tiles = tiles_m * tiles_n;
-    const int per_xcd = (tiles + 7) / 8;
-    hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, TJ, S, OCC>), dim3(8 * per_xcd),
-                       dim3(kThreads), 0, stream, qx, qw, sx, sw, bias, Y, (int)M, (int)N,
-                       (int)K, tiles_m, tiles_n, per_xcd);
-    return hipGetLastError();
+    static int cached = 0;
+    if (cached == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cached = n;
+        else
+            cached = 256;
+    }
+    return cached;
 }
-
-#ifndef CONVROT_GEMM_TJ
-#define CONVROT_GEMM_TJ 4
-#endif
 
 template <int OUT, bool HAS_BIAS>
 hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream)
 {
+    const int tiles_m = (int)((M + kTile - 1) / kTile);
+    const int tiles_n = (int)((N + kTile - 1) / kTile);
+    const int tiles = tiles_m * tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    const int wgs_per_xcd = std::max(1, std::min(cu_count() / 8, per_xcd));
     const int nk = (int)(K / kBK);
-    if constexpr (CONVROT_GEMM_TJ == 4) {
-        if (nk % 4 == 0)
-            return launch_cfg<OUT, HAS_BIAS, 4, 4, 1>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
-        return launch_cfg<OUT, HAS_BIAS, 4, 2, 1>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
-    } else {
-        if (nk % 3 == 0)
-            return launch_cfg<OUT, HAS_BIAS, 2, 3, 2>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
-        return launch_cfg<OUT, HAS_BIAS, 2, 2, 2>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
-    }
+    const dim3 grid(8 * wgs_per_xcd), block(kThreads);
+    if (nk % 4 == 0)
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 4>), grid, block, 0, stream, qx, qw, sx,
+                           sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
+                           wgs_per_xcd);
+    else
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 2>), grid, block, 0, stream, qx, qw, sx,
+                           sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
+                           wgs_per_xcd);
+    return hipGetLastError();
 }
 
 } // namespace
