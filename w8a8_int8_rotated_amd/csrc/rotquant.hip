@@ -107,22 +107,39 @@ __device__ __forceinline__ void inlane_fwht8(float (&v)[8])
     }
 }
 
+// buffer resource word 3: raw (untyped) 32-bit data format, no swizzle
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// One row as a buffer resource of `bytes` bytes: loads past the end read as
+// zero and stores past the end are dropped, so a partial last step needs no
+// per-lane branches.  A row beyond M gets an empty range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes,
+                                             kRsrcWord3);
+}
+
+// The 8 elements of one chunk at element offset e of the row.
 template <int IN>
-__device__ __forceinline__ void load_chunk(const void *src, int64_t off, float (&v)[8])
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t row, int e, float (&v)[8])
 {
     if constexpr (IN == int(InType::BF16)) {
-        const uint4 d = *reinterpret_cast<const uint4 *>(
-            reinterpret_cast<const uint16_t *>(src) + off);
-        v[0] = bf16_lo(d.x); v[1] = bf16_hi(d.x);
-        v[2] = bf16_lo(d.y); v[3] = bf16_hi(d.y);
-        v[4] = bf16_lo(d.z); v[5] = bf16_hi(d.z);
-        v[6] = bf16_lo(d.w); v[7] = bf16_hi(d.w);
+        const v4i d = __builtin_amdgcn_raw_buffer_load_b128(row, e * 2, 0, 0);
+        v[0] = bf16_lo(d[0]); v[1] = bf16_hi(d[0]);
+        v[2] = bf16_lo(d[1]); v[3] = bf16_hi(d[1]);
+        v[4] = bf16_lo(d[2]); v[5] = bf16_hi(d[2]);
+        v[6] = bf16_lo(d[3]); v[7] = bf16_hi(d[3]);
     } else {
-        const float4 *p = reinterpret_cast<const float4 *>(
-            reinterpret_cast<const float *>(src) + off);
-        const float4 a = p[0], b = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        const v4i a = __builtin_amdgcn_raw_buffer_load_b128(row, e * 4, 0, 0);
+        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(row, e * 4 + 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[j] = __int_as_float(a[j]);
+            v[4 + j] = __int_as_float(c[j]);
+        }
     }
 }
 
@@ -156,7 +173,8 @@ __device__ __forceinline__ float wave_max(float m)
     return m;
 }
 
-// IN: input type; B: Hadamard block; SPR: wave steps per row held per wave;
+// IN: input type; B: Hadamard block; SPR: wave steps held per wave (an upper
+// bound: steps past the end of the row are skipped by a wave-uniform branch);
 // RPW: rows per wave (when WPR == 1); WPR: waves per row; NW: waves per WG.
 template <int IN, int B, int SPR, int RPW, int WPR, int NW>
 __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
@@ -168,11 +186,12 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
     constexpr int LPB = B / 8;
     constexpr int NSTAGE = (B == 64) ? 3 : (B == 128) ? 4 : 5;
     constexpr int GROUPS = NW / WPR;
+    constexpr int ESIZE = IN == int(InType::BF16) ? 2 : 4;
 
     __shared__ float red[NW];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int part = wave % WPR;
     const int grp = wave / WPR;
     const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * RPW;
@@ -180,61 +199,53 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
     const int chunk = chunk_of_lane(li);
     const int lane_off = (lane / LPB) * B + chunk * 8;
     const int steps = (K + kStep - 1) / kStep;
+    // steps of this wave: part, part + WPR, ... below `steps`
+    const int my_steps = (steps - part + WPR - 1) / WPR;
+
+    __amdgpu_buffer_rsrc_t src_row[RPW], q_row[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const int64_t row = row0 + r;
+        const bool in = row < M;
+        src_row[r] = row_rsrc(reinterpret_cast<const char *>(src) + (in ? row : 0) * ld * ESIZE,
+                              in ? K * ESIZE : 0);
+        q_row[r] = row_rsrc(q + (in ? row : 0) * (int64_t)K, in ? K : 0);
+    }
 
     float v[RPW][SPR][8];
 
     // ---- loads: every chunk of every row this wave owns, all in flight ----
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int64_t row = row0 + r;
-#pragma unroll
-        for (int t = 0; t < SPR; ++t) {
-            const int st = part + WPR * t;
-            const int e = st * kStep + lane_off;
-            if (row < M && st < steps && e < K) {
-                load_chunk<IN>(src, row * ld + e, v[r][t]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[r][t][j] = 0.0f;
-            }
-        }
-    }
-
-    // ---- rotation: in-lane stages, then cross-lane stages (uniform flow) ---
-#pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int t = 0; t < SPR; ++t)
-            inlane_fwht8(v[r][t]);
+            if (t < my_steps)
+                load_chunk<IN>(src_row[r], (part + WPR * t) * kStep + lane_off, v[r][t]);
 
     float csign[NSTAGE];
 #pragma unroll
     for (int k = 0; k < NSTAGE; ++k)
         csign[k] = ((chunk >> k) & 1) ? -1.0f : 1.0f;
 
+    // ---- rotation (wave-uniform control flow: the DPP stages need every
+    // lane) and the row's |max| ----
+    float m[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
+    for (int r = 0; r < RPW; ++r) {
+        m[r] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < SPR; ++t) cross_stage<0>(v[r][t], csign[0]);
+        for (int t = 0; t < SPR; ++t) {
+            if (t < my_steps) {
+                inlane_fwht8(v[r][t]);
+                cross_stage<0>(v[r][t], csign[0]);
+                cross_stage<1>(v[r][t], csign[1]);
+                cross_stage<2>(v[r][t], csign[2]);
+                if constexpr (NSTAGE > 3) cross_stage<3>(v[r][t], csign[3]);
+                if constexpr (NSTAGE > 4) cross_stage<4>(v[r][t], csign[4]);
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int t = 0; t < SPR; ++t) cross_stage<1>(v[r][t], csign[1]);
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int t = 0; t < SPR; ++t) cross_stage<2>(v[r][t], csign[2]);
-    if constexpr (NSTAGE > 3) {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int t = 0; t < SPR; ++t) cross_stage<3>(v[r][t], csign[3]);
-    }
-    if constexpr (NSTAGE > 4) {
-#pragma unroll
-        for (int r = 0; r < RPW; ++r)
-#pragma unroll
-            for (int t = 0; t < SPR; ++t) cross_stage<4>(v[r][t], csign[4]);
+                for (int j = 0; j < 8; ++j) m[r] = fmaxf(m[r], fabsf(v[r][t][j]));
+            }
+        }
     }
 
     const bool negated = (__builtin_popcount(chunk) & 1) != 0;
@@ -243,30 +254,24 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         const int64_t row = row0 + r;
-        float m = 0.0f;
-#pragma unroll
-        for (int t = 0; t < SPR; ++t)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[r][t][j]));
-        m = wave_max(m);
+        float mx = wave_max(m[r]);
         if constexpr (WPR > 1) {
-            if (lane == 0) red[wave] = m;
+            if (lane == 0) red[wave] = mx;
             __syncthreads();
 #pragma unroll
-            for (int w = 0; w < WPR; ++w) m = fmaxf(m, red[grp * WPR + w]);
+            for (int w = 0; w < WPR; ++w) mx = fmaxf(mx, red[grp * WPR + w]);
         }
-        const float inv = (m > 0.0f) ? __fdiv_rn(127.0f, m) : 0.0f;
+        const float inv = (mx > 0.0f) ? __fdiv_rn(127.0f, mx) : 0.0f;
         const float invs = negated ? -inv : inv;
-        if (row < M) {
-            if (part == 0 && lane == 0)
-                s[row] = __fmul_rn(__fdiv_rn(m, 127.0f), inv_sqrt_b);
+        if (part == 0 && lane == 0 && row < M)
+            s[row] = __fmul_rn(__fdiv_rn(mx, 127.0f), inv_sqrt_b);
 #pragma unroll
-            for (int t = 0; t < SPR; ++t) {
-                const int st = part + WPR * t;
-                const int e = st * kStep + lane_off;
-                if (st < steps && e < K)
-                    *reinterpret_cast<uint2 *>(q + row * (int64_t)K + e) =
-                        quantise_chunk(v[r][t], invs);
+        for (int t = 0; t < SPR; ++t) {
+            if (t < my_steps) {
+                const uint2 c = quantise_chunk(v[r][t], invs);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    (v2i){(int)c.x, (int)c.y}, q_row[r], (part + WPR * t) * kStep + lane_off,
+                    0, 0);
             }
         }
     }
@@ -283,6 +288,9 @@ hipError_t launch_cfg(const void *src, int64_t M, int64_t K, int64_t ld,
     return hipGetLastError();
 }
 
+// Rows of up to 4 steps (2048 elements) are held by one wave, several rows
+// per wave when they are short; longer rows are split over 2..16 waves of
+// at most 6 steps each (8 beyond 96 steps), which keeps a wave near 80 VGPRs.
 template <int IN, int B>
 hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
@@ -291,11 +299,10 @@ hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
     if (steps <= 1) return launch_cfg<IN, B, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 2) return launch_cfg<IN, B, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 4) return launch_cfg<IN, B, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 8) return launch_cfg<IN, B, 8, 1, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 12) return launch_cfg<IN, B, 12, 1, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 24) return launch_cfg<IN, B, 12, 1, 2, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 48) return launch_cfg<IN, B, 12, 1, 4, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 64) return launch_cfg<IN, B, 8, 1, 8, 8>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 12) return launch_cfg<IN, B, 6, 1, 2, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 24) return launch_cfg<IN, B, 6, 1, 4, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 48) return launch_cfg<IN, B, 6, 1, 8, 8>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 96) return launch_cfg<IN, B, 6, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     return launch_cfg<IN, B, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
 }
 
