@@ -43,6 +43,9 @@ __device__ __forceinline__ float gelu_erf(float z)
 namespace convrot {
 
 enum class InType { F32 = 0, BF16 = 1 };
+
+// Compute units of the current device (queried once; 256 if the query fails).
+int device_cu_count();
 enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3 };
 
 // Rotate (blockwise FWHT) + rowwise INT8 quantise.  src rows have stride ld

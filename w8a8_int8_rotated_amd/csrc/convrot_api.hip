@@ -9,6 +9,25 @@
 #include <cstdlib>
 #include <cstdio>
 
+namespace convrot {
+
+int device_cu_count()
+{
+    // one entry per device ordinal; a race only repeats the same query
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    if (dev < 64) cached[dev] = n;
+    return n;
+}
+
+} // namespace convrot
+
 namespace {
 
 constexpr int64_t kMaxK = 65536;

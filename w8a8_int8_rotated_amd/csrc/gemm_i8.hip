@@ -540,21 +540,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     wait_vmcnt<0>();
 }
 
-int cu_count()
-{
-    static int cached = 0;
-    if (cached == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            cached = n;
-        else
-            cached = 256;
-    }
-    return cached;
-}
-
 template <int OUT, bool HAS_BIAS>
 hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
@@ -564,7 +549,7 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
     const int tiles_n = (int)((N + kTile - 1) / kTile);
     const int tiles = tiles_m * tiles_n;
     const int per_xcd = (tiles + 7) / 8;
-    const int wgs_per_xcd = std::max(1, std::min(cu_count() / 8, per_xcd));
+    const int wgs_per_xcd = std::max(1, std::min(device_cu_count() / 8, per_xcd));
     const int nk = (int)(K / kBK);
     const dim3 grid(8 * wgs_per_xcd), block(kThreads);
     if (nk % 4 == 0)

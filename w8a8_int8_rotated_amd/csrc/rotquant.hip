@@ -37,6 +37,8 @@
 // byte of that float's bits.
 #include "common.hpp"
 
+#include <algorithm>
+
 namespace convrot {
 namespace {
 
@@ -288,9 +290,153 @@ hipError_t launch_cfg(const void *src, int64_t M, int64_t K, int64_t ld,
     return hipGetLastError();
 }
 
+// Streaming variant for rows split over WPR waves (K > 2048): one persistent
+// workgroup per CU walks row groups, and each wave loads the raw input of
+// its next group before rotating the current one, so memory and the rotation
+// overlap inside the wave as well as across waves.
+template <int IN, int B, int SPR, int WPR, int NW>
+__global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
+    const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
+    int8_t *__restrict__ q, float *__restrict__ s)
+{
+    static_assert(NW % WPR == 0 && WPR > 1, "");
+    constexpr int LPB = B / 8;
+    constexpr int NSTAGE = (B == 64) ? 3 : (B == 128) ? 4 : 5;
+    constexpr int GROUPS = NW / WPR;
+    constexpr int ESIZE = IN == int(InType::BF16) ? 2 : 4;
+    constexpr int DW = IN == int(InType::BF16) ? 4 : 8;   // raw dwords per lane per step
+
+    __shared__ float red[2][NW];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wave % WPR;
+    const int grp = wave / WPR;
+    const int li = lane % LPB;
+    const int chunk = chunk_of_lane(li);
+    const int lane_off = (lane / LPB) * B + chunk * 8;
+    const int steps = (K + kStep - 1) / kStep;
+    const int my_steps = (steps - part + WPR - 1) / WPR;
+    const int64_t ngroups = (M + GROUPS - 1) / GROUPS;
+
+    float csign[NSTAGE];
+#pragma unroll
+    for (int k = 0; k < NSTAGE; ++k)
+        csign[k] = ((chunk >> k) & 1) ? -1.0f : 1.0f;
+    const bool negated = (__builtin_popcount(chunk) & 1) != 0;
+
+    // Every memory instruction is unconditional (steps past the row end fall
+    // outside the buffer range: loads read zero, stores are dropped), so the
+    // compiler can count them and wait for the prefetched loads only.
+    int raw[SPR][DW];
+    auto issue = [&](int64_t gi) {
+        const int64_t row = gi * GROUPS + grp;
+        const bool in = row < M;
+        const __amdgpu_buffer_rsrc_t r = row_rsrc(
+            reinterpret_cast<const char *>(src) + (in ? row : 0) * ld * ESIZE, in ? K * ESIZE : 0);
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            const int e = (part + WPR * t) * kStep + lane_off;
+            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) raw[t][j] = a[j];
+            if constexpr (DW == 8) {
+                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) raw[t][4 + j] = c[j];
+            }
+        }
+    };
+    const __amdgpu_buffer_rsrc_t srs = row_rsrc(s, (int)(M * 4 < 0x7fffffff ? M * 4 : 0x7fffffff));
+
+    int64_t gi = blockIdx.x;
+    issue(gi);
+    {
+        // the loop's stores, into an empty range: both ways into the loop
+        // then carry the same sequence of memory operations, and the
+        // compiler's waits at the top of the loop cover the loads only
+        const __amdgpu_buffer_rsrc_t none = row_rsrc(q, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(0, none, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < SPR; ++t)
+            __builtin_amdgcn_raw_buffer_store_b64((v2i){0, 0}, none, 0, 0, 0);
+    }
+    int par = 0;
+    for (; gi < ngroups; gi += gridDim.x, par ^= 1) {
+        const int64_t row = gi * GROUPS + grp;
+        float v[SPR][8];
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            if constexpr (DW == 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[t][2 * j] = bf16_lo((uint32_t)raw[t][j]);
+                    v[t][2 * j + 1] = bf16_hi((uint32_t)raw[t][j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[t][j] = __int_as_float(raw[t][j]);
+            }
+        }
+        // next group (or this one again on the last pass: its loads are
+        // harmless and keep the sequence uniform)
+        issue(gi + gridDim.x < ngroups ? gi + gridDim.x : gi);
+
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            if (t < my_steps) {
+                inlane_fwht8(v[t]);
+                cross_stage<0>(v[t], csign[0]);
+                cross_stage<1>(v[t], csign[1]);
+                cross_stage<2>(v[t], csign[2]);
+                if constexpr (NSTAGE > 3) cross_stage<3>(v[t], csign[3]);
+                if constexpr (NSTAGE > 4) cross_stage<4>(v[t], csign[4]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[t][j]));
+            }
+        }
+        // the row's |max| over its WPR waves; red[] alternates between passes
+        // so a fast wave cannot overwrite values a slow one still reads
+        float mx = wave_max(m);
+        if (lane == 0) red[par][wave] = mx;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) mx = fmaxf(mx, red[par][grp * WPR + w]);
+        const float inv = (mx > 0.0f) ? __fdiv_rn(127.0f, mx) : 0.0f;
+        const float invs = negated ? -inv : inv;
+        const bool in = row < M;
+        // the scale: one lane per row writes, every other lane's offset is
+        // out of range
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_int(__fmul_rn(__fdiv_rn(mx, 127.0f), inv_sqrt_b)), srs,
+            (part == 0 && lane == 0 && in) ? (int)(row * 4) : 0x7ffffff0, 0, 0);
+        const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + (in ? row : 0) * (int64_t)K, in ? K : 0);
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            const uint2 c = quantise_chunk(v[t], invs);
+            __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)c.x, (int)c.y}, qr,
+                                                  (part + WPR * t) * kStep + lane_off, 0, 0);
+        }
+    }
+}
+
+template <int IN, int B, int SPR, int WPR, int NW>
+hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
+                         float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+{
+    constexpr int rows_per_wg = NW / WPR;
+    const int64_t groups = (M + rows_per_wg - 1) / rows_per_wg;
+    const int64_t grid = std::min<int64_t>(groups, device_cu_count());
+    hipLaunchKernelGGL((rotquant_stream_kernel<IN, B, SPR, WPR, NW>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, src, M, (int)K, ld, inv_sqrt_b, q, s);
+    return hipGetLastError();
+}
+
 // Rows of up to 4 steps (2048 elements) are held by one wave, several rows
-// per wave when they are short; longer rows are split over 2..16 waves of
-// at most 6 steps each (8 beyond 96 steps), which keeps a wave near 80 VGPRs.
+// per wave when they are short.  Longer rows are split over 2..16 waves of
+// at most 6 steps each and streamed by one 16-wave workgroup per CU; beyond
+// 96 steps the one-shot kernel holds 8 steps per wave.
 template <int IN, int B>
 hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
@@ -299,10 +445,10 @@ hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
     if (steps <= 1) return launch_cfg<IN, B, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 2) return launch_cfg<IN, B, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 4) return launch_cfg<IN, B, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 12) return launch_cfg<IN, B, 6, 1, 2, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 24) return launch_cfg<IN, B, 6, 1, 4, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 48) return launch_cfg<IN, B, 6, 1, 8, 8>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 96) return launch_cfg<IN, B, 6, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 12) return launch_stream<IN, B, 6, 2, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 24) return launch_stream<IN, B, 6, 4, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 48) return launch_stream<IN, B, 6, 8, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 96) return launch_stream<IN, B, 6, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     return launch_cfg<IN, B, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
 }
 
