@@ -1,17 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the ConvRot W8A8 INT8 linear forward on one MI355X.
 
-One step = one ``convrot_linear_forward`` call (rotate + rowwise INT8
-quantise kernel, then the INT8 MFMA GEMM with the fused dequant epilogue) over
-the fused-QKV-shaped workload M=38656 tokens, K=5376, N=16128, b=128, bf16
-activations drawn from Student-t(4), bf16 output.  The weights are prepared
+One step = one forward call through the C ABI over one batch of synthetic
+input already resident in HBM.  The default workload is the fused-QKV-shaped
+linear M=38656 tokens, K=5376, N=16128, b=128, bf16 activations drawn from
+Student-t(4), bf16 output: one ``convrot_linear_forward`` = the rotate +
+rowwise INT8 quantise kernel, then the INT8 MFMA GEMM with the fused dequant
+epilogue.  ``--workload`` also takes the other workloads (``linear_4096``,
+``mlp_16384``: up GEMM with GELU, rotquant of g, down GEMM; ``lowrank_38656``:
+rotquant, GEMM to r, rotquant of H, GEMM to N).  Weights are prepared
 (rotated, quantised, packed) before the timed region, as at model load.
 
-Prints ONE JSON line: effective INT8 TOPS (2*M*N*K per step / step time), the
-roofline of the dominant kernel (the GEMM, timed with HIP events on the
-stream it runs on), the rotate+quantise kernel against HBM bandwidth, and the
-CPU oracle timed on a bounded sample of the same rows (which also checks the
-benchmarked outputs on those rows).
+Prints ONE JSON line: effective INT8 TOPS (algorithmic 2*M*N*K summed over the
+projections, per step time); ``roofline`` for the dominant kernel (its
+algorithmic ops or bytes per launch over its average launch time, timed with
+HIP events recorded on the stream the kernel runs on); ``kernels`` with every
+kernel of the step; ``roofline_rotquant`` for the first rotate+quantise pass;
+and ``cpu_baseline``, the CPU oracle timed on a bounded sample of the same
+rows, which also checks the benchmarked outputs on those rows.
 
     python bench.py [--steps 20] [--warmup 5] [--workload qkv_38656]
 """
@@ -31,7 +37,10 @@ sys.path.insert(0, ROOT)
 METRIC = "effective INT8 TOPS & % INT8 MFMA peak, ConvRot linear M=38656 K=5376"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
-GEMM_SRC = os.path.join(ROOT, "w8a8_int8_rotated_amd", "csrc", "gemm_i8.hip")
+RIDGE = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # ops per byte
+CSRC = os.path.join(ROOT, "w8a8_int8_rotated_amd", "csrc")
+SOURCES = {"gemm_i8": os.path.join(CSRC, "gemm_i8.hip"),
+           "rotquant": os.path.join(CSRC, "rotquant.hip")}
 
 
 def log(msg):
@@ -56,18 +65,164 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def recorded_traffic(workload):
-    """HBM bytes per GEMM launch from the committed counter summary, if it
-    was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"gemm_i8_{workload}_pmc.md")
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not sha or not val or sha.group(1) != source_sha(GEMM_SRC):
+    if not sha or not val or sha.group(1) != source_sha(SOURCES[kernel]):
         return None
     return float(val.group(1))
+
+
+class Stage:
+    """One kernel launch of the step, with its algorithmic cost."""
+
+    def __init__(self, name, kernel, fn, ops, nbytes):
+        self.name, self.kernel, self.fn = name, kernel, fn
+        self.ops, self.bytes = float(ops), float(nbytes)
+        self.bound = "mfma" if self.ops / self.bytes > RIDGE else "hbm"
+        self.ms = None
+
+    def roofline(self, workload):
+        if self.bound == "mfma":
+            achieved = self.ops / (self.ms * 1e-3) / 1e12
+            peak, unit = PEAK_INT8_TOPS, "TFLOP/s"
+        else:
+            achieved = self.bytes / (self.ms * 1e-3) / 1e9
+            peak, unit = PEAK_HBM_GBS, "GB/s"
+        return {
+            "kernel": self.name, "bound": self.bound, "achieved": round(achieved, 2),
+            "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": recorded_traffic(self.kernel, workload),
+            "ops_per_launch": self.ops, "bytes_per_launch": self.bytes,
+            "avg_launch_ms": round(self.ms, 5),
+        }
+
+
+def rq_bytes(M, K):
+    return 3.0 * M * K + 4.0 * M          # bf16 in, codes out, row scale
+
+
+def gemm_cost(M, N, K, out_bytes=2, bias=False):
+    ops = 2.0 * M * N * K
+    nbytes = M * K + N * K + out_bytes * M * N + 4.0 * (M + N) + (4.0 * N if bias else 0)
+    return ops, nbytes
+
+
+def setup(w, cr, torch, np, dev):
+    """Device inputs, prepared weights, the step and its stages."""
+    b = w.block
+    x = w.activations()
+    X = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    host = {"x": x}
+    stream = torch.cuda.current_stream()
+    out_dt = torch.bfloat16 if w.out == "bf16" else torch.float32
+    ob = 2 if w.out == "bf16" else 4
+
+    def prep(W):
+        Wd = torch.from_numpy(W).to(dev)
+        pw = cr.convrot_linear_prepare_weights(Wd, b)
+        torch.cuda.synchronize()
+        return pw
+
+    M, K = w.M, w.K
+    if w.kind == "linear":
+        W = w.weight()
+        bias = w.bias()
+        host.update(W=W, bias=bias)
+        pw = prep(W)
+        bias_d = None if bias is None else torch.from_numpy(bias).to(dev)
+        N = w.N
+        Y = torch.empty((M, N), dtype=out_dt, device=dev)
+        ws = torch.empty(cr.convrot_linear_workspace_bytes(M, K, N, b), dtype=torch.uint8,
+                         device=dev)
+        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def step():
+            cr.convrot_linear_forward(X, pw, bias=bias_d, out=Y, workspace=ws, stream=stream)
+
+        stages = [
+            Stage("rotquant (FWHT + absmax + INT8 codes)", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
+                  0.0, rq_bytes(M, K)),
+            Stage("gemm_i8 (INT8 MFMA + dequant epilogue)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qx, sx, pw, bias=bias_d, out=Y, stream=stream),
+                  *gemm_cost(M, N, K, ob, bias is not None)),
+        ]
+        ops = 2.0 * M * N * K
+    elif w.kind == "lowrank":
+        A, B = w.weight("w"), w.weight("w2")
+        host.update(A=A, B=B)
+        pa, pb = prep(A), prep(B)
+        r, N = w.rank, w.N
+        Y = torch.empty((M, N), dtype=out_dt, device=dev)
+        ws = torch.empty(cr.lowrank_convrot_workspace_bytes(M, K, r, N, b), dtype=torch.uint8,
+                         device=dev)
+        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        H = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
+        qh = torch.empty((M, r), dtype=torch.int8, device=dev)
+        sh = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def step():
+            cr.lowrank_convrot_forward(X, pa, pb, out=Y, workspace=ws, stream=stream)
+
+        stages = [
+            Stage("rotquant X", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
+                  0.0, rq_bytes(M, K)),
+            Stage("gemm_i8 factor 1 (K -> r)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qx, sx, pa, out=H, stream=stream),
+                  *gemm_cost(M, r, K)),
+            Stage("rotquant H", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(H, b, q=qh, s=sh, stream=stream),
+                  0.0, rq_bytes(M, r)),
+            Stage("gemm_i8 factor 2 (r -> N)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qh, sh, pb, out=Y, stream=stream),
+                  *gemm_cost(M, N, r, ob)),
+        ]
+        ops = 2.0 * M * r * (K + N)
+    elif w.kind == "mlp":
+        Wu, Wd = w.weight("w"), w.weight("w2")
+        host.update(Wu=Wu, Wd=Wd)
+        pu, pd = prep(Wu), prep(Wd)
+        F, N = w.ffn, w.N
+        Y = torch.empty((M, N), dtype=out_dt, device=dev)
+        ws = torch.empty(cr.convrot_mlp_workspace_bytes(M, K, F, N, b), dtype=torch.uint8,
+                         device=dev)
+        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        G = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        qg = torch.empty((M, F), dtype=torch.int8, device=dev)
+        sg = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def step():
+            cr.convrot_mlp_forward(X, pu, pd, out=Y, workspace=ws, stream=stream)
+
+        stages = [
+            Stage("rotquant X", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
+                  0.0, rq_bytes(M, K)),
+            Stage("gemm_i8 up + GELU (K -> F)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qx, sx, pu, out=G, gelu=True, stream=stream),
+                  *gemm_cost(M, F, K)),
+            Stage("rotquant g", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(G, b, q=qg, s=sg, stream=stream),
+                  0.0, rq_bytes(M, F)),
+            Stage("gemm_i8 down (F -> N)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qg, sg, pd, out=Y, stream=stream),
+                  *gemm_cost(M, N, F, ob)),
+        ]
+        ops = 2.0 * M * F * (K + N)
+    else:
+        raise SystemExit(f"unknown workload kind {w.kind}")
+    return step, stages, ops, Y, host
 
 
 def main():
@@ -88,10 +243,7 @@ def main():
 
     cr.library()
     w = wl.WORKLOADS[args.workload]
-    if w.kind != "linear":
-        raise SystemExit("bench.py times the linear forward; pick a 'linear' workload")
     dev = torch.device("cuda", 0)
-    M, K, N, b = w.M, w.K, w.N, w.block
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -104,25 +256,9 @@ def main():
         log(f"copy probe: 3 x {args.copy_probe_mib} MiB device copies")
 
     t0 = time.time()
-    x = w.activations()
-    W = w.weight()
-    bias = w.bias()
-    log(f"inputs generated in {time.time() - t0:.1f}s: X {x.shape} bf16, W {W.shape} f32")
-
-    X = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-    Wd = torch.from_numpy(W).to(dev)
-    pw = cr.convrot_linear_prepare_weights(Wd, b)
-    torch.cuda.synchronize()
-    del Wd
-    bias_d = None if bias is None else torch.from_numpy(bias).to(dev)
-    out_dt = torch.bfloat16 if w.out == "bf16" else torch.float32
-    Y = torch.empty((M, N), dtype=out_dt, device=dev)
-    ws = torch.empty(cr.convrot_linear_workspace_bytes(M, K, N, b), dtype=torch.uint8,
-                     device=dev)
+    step, stages, ops, Y, host = setup(w, cr, torch, np, dev)
     stream = torch.cuda.current_stream()
-
-    def step():
-        cr.convrot_linear_forward(X, pw, bias=bias_d, out=Y, workspace=ws, stream=stream)
+    log(f"{w.name}: inputs generated and weights prepared in {time.time() - t0:.1f}s")
 
     for _ in range(args.warmup):
         step()
@@ -140,34 +276,41 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    ops = 2.0 * M * N * K
     tops = ops / (ms_per_step * 1e-3) / 1e12
     log(f"forward: {ms_per_step:.4f} ms/step, {tops:.1f} TOPS (wall {wall:.3f}s)")
 
-    # ---- per-kernel durations: the same two kernels, launched through the
-    # stage hooks with HIP events between them on the same stream ----
-    qx = torch.empty((M, K), dtype=torch.int8, device=dev)
-    sx = torch.empty(M, dtype=torch.float32, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---- per-kernel durations: the step's kernels, launched through the
+    # stage hooks on the same stream with HIP events between them ----
     for _ in range(2):
-        cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream)
-        cr.convrot_gemm_dequant(qx, sx, pw, bias=bias_d, out=Y, stream=stream)
+        for st in stages:
+            st.fn()
     torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(args.steps)]
     for e in evs:
         e[0].record(stream)
-        cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream)
-        e[1].record(stream)
-        cr.convrot_gemm_dequant(qx, sx, pw, bias=bias_d, out=Y, stream=stream)
-        e[2].record(stream)
+        for i, st in enumerate(stages):
+            st.fn()
+            e[i + 1].record(stream)
     torch.cuda.synchronize()
-    rq_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
-    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
-    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    rq_bytes = 3.0 * M * K + 4.0 * M
-    rq_gbs = rq_bytes / (rq_ms * 1e-3) / 1e9
-    log(f"rotquant {rq_ms:.4f} ms ({rq_gbs:.0f} GB/s); gemm {gemm_ms:.4f} ms "
-        f"({gemm_tops:.1f} TOPS)")
-    traffic = recorded_traffic(w.name)
+    for i, st in enumerate(stages):
+        st.ms = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / len(evs)
+    for st in stages:
+        r = st.roofline(w.name)
+        log(f"{st.name}: {st.ms:.4f} ms, {r['achieved']} {r['unit']} ({100 * r['frac']:.1f}%)")
+    dominant = max(stages, key=lambda s: s.ms)
+    first_rq = next(s for s in stages if s.kernel == "rotquant")
+
+    cfg = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.block,
+           "activations": "bf16 Student-t(4)" if w.x_dist == "student_t4" else "bf16 normal",
+           "out": w.out, "bias": w.bias_std is not None, "seed": w.seed}
+    if w.kind == "lowrank":
+        cfg["rank"] = w.rank
+    if w.kind == "mlp":
+        cfg["ffn"] = w.ffn
+    if w.n_outliers():
+        cfg["outlier_channels"] = w.n_outliers()
+        cfg["outlier_gain"] = w.outlier_gain
 
     result = {
         "metric": METRIC,
@@ -182,65 +325,56 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {
-            "workload": w.name, "M": M, "K": K, "N": N, "block": b,
-            "activations": "bf16 Student-t(4)" if w.x_dist == "student_t4" else "bf16 normal",
-            "out": w.out, "bias": bias is not None, "seed": w.seed,
-        },
+        "config": cfg,
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
-        "roofline": {
-            "kernel": "gemm_i8 (INT8 MFMA + dequant epilogue)",
-            "bound": "mfma",
-            "achieved": round(gemm_tops, 2),
-            "peak": PEAK_INT8_TOPS,
-            "unit": "TFLOP/s",
-            "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-            "traffic": traffic,
-            "ops_per_launch": ops,
-            "avg_launch_ms": round(gemm_ms, 5),
-        },
-        "roofline_rotquant": {
-            "kernel": "rotquant (FWHT + absmax + INT8 codes)",
-            "bound": "hbm",
-            "achieved": round(rq_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(rq_gbs / PEAK_HBM_GBS, 4),
-            "bytes_per_launch": rq_bytes,
-            "avg_launch_ms": round(rq_ms, 5),
-        },
+        "roofline": dominant.roofline(w.name),
+        "roofline_rotquant": first_rq.roofline(w.name),
+        "kernels": [s.roofline(w.name) for s in stages],
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, w, x, W, bias, Y)
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, w, host, Y)
 
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(args, w, x, W, bias, Y):
+def cpu_baseline(args, w, host, Y):
     """The oracle (as it stands) on a bounded, seeded sample of the same rows;
     its outputs are also compared with the benchmarked GPU outputs."""
     import numpy as np
     import oracle
 
-    M, K, N, b = w.M, w.K, w.N, w.block
+    M, b, x = w.M, w.block, host["x"]
     t0 = time.perf_counter()
-    qw, sw = oracle.prepare_weights(W, b)
+    if w.kind == "linear":
+        qw, sw = oracle.prepare_weights(host["W"], b)
+        run = lambda rows: oracle.linear_forward(x[rows], qw, sw, b, bias=host["bias"], out=w.out)
+        ops_row = 2.0 * w.N * w.K
+    elif w.kind == "lowrank":
+        qa, sa = oracle.prepare_weights(host["A"], b)
+        qb, sb = oracle.prepare_weights(host["B"], b)
+        run = lambda rows: oracle.lowrank_forward(x[rows], qa, sa, qb, sb, b, out=w.out)
+        ops_row = 2.0 * w.rank * (w.K + w.N)
+    else:
+        qu, su = oracle.prepare_weights(host["Wu"], b)
+        qd, sd = oracle.prepare_weights(host["Wd"], b)
+        run = lambda rows: oracle.mlp_forward(x[rows], qu, su, qd, sd, b, out=w.out)
+        ops_row = 2.0 * w.ffn * (w.K + w.N)
     prep_s = time.perf_counter() - t0
     rng = np.random.default_rng(1234)
-    probe = np.sort(rng.choice(M, 32, replace=False))
+    probe = np.sort(rng.choice(M, min(M, 16), replace=False))
     t0 = time.perf_counter()
-    oracle.linear_forward(x[probe], qw, sw, b, bias=bias, out=w.out)
+    run(probe)
     per_row = (time.perf_counter() - t0) / len(probe)
     n = int(min(M, max(64, args.cpu_seconds / max(per_row, 1e-9))))
     rows = np.sort(rng.choice(M, n, replace=False))
     rows[0], rows[-1] = 0, M - 1
     rows = np.unique(rows)
     t0 = time.perf_counter()
-    y_ref = oracle.linear_forward(x[rows], qw, sw, b, bias=bias, out=w.out)
+    y_ref = run(rows)
     dt = time.perf_counter() - t0
-    cpu_tops = 2.0 * len(rows) * N * K / dt / 1e12
+    cpu_tops = ops_row * len(rows) / dt / 1e12
     log(f"oracle: {len(rows)} rows in {dt:.2f}s = {cpu_tops:.4f} TOPS on "
         f"{oracle.num_threads()} threads (weight prep {prep_s:.1f}s, not timed)")
 
@@ -260,8 +394,9 @@ def cpu_baseline(args, w, x, W, bias, Y):
         "unit": "TOPS",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"{len(rows)} of {M} rows (seeded), full N={N} and K={K}; rotate+quantise "
-                  f"of those rows, INT32 GEMM and epilogue; weight preparation excluded",
+        "sample": f"{len(rows)} of {M} rows (seeded), every projection over its full width "
+                  f"and depth: rotate+quantise of those rows, INT32 contraction and epilogue"
+                  f"{', GELU' if w.kind == 'mlp' else ''}; weight preparation excluded",
         "seconds": round(dt, 2),
     }
     parity = {"rows": int(len(rows)), "normwise_err": err, "mismatches": mism,

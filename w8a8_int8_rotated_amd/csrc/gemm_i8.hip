@@ -122,16 +122,31 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
 
 // Dequantise and store a wave's 128 x 128 block.  FULL: the tile lies inside
 // [M, N], so no per-lane bounds checks are needed.
-// fp32 value of one output: ((float)acc * s_x) * s_w (+ bias), optionally
-// followed by bf16 rounding and GELU (the MLP's up projection).
+// fp32 value of one output: ((float)acc * s_x) * s_w (+ bias).
 template <int OUT, bool HAS_BIAS>
 __device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float bn)
 {
     float f = __fmul_rn(__fmul_rn((float)acc, sxm), swn);
     if constexpr (HAS_BIAS) f = __fadd_rn(f, bn);
-    if constexpr (OUT == int(OutKind::GELU_BF16))
-        f = gelu_erf(__uint_as_float(f32_to_bf16_bits(f) << 16));
     return f;
+}
+
+// bf16(GELU(u)) for every bf16 bit pattern u (GELU in its erf form, fp32, on
+// the bf16 value of the up projection's output).  The MLP's up projection
+// looks its outputs up here instead of evaluating erff per element.  Every
+// launch that reads the table is preceded on its own stream by a launch that
+// (re)writes it with the same values, so a reader never sees a partial table.
+__device__ uint16_t g_gelu_bf16[65536];
+
+__global__ __launch_bounds__(256) void gelu_table_kernel()
+{
+    const uint32_t u = blockIdx.x * 256u + threadIdx.x;
+    g_gelu_bf16[u] = (uint16_t)(cvt_pk_bf16(gelu_erf(__uint_as_float(u << 16)), 0.0f) & 0xffffu);
+}
+
+__device__ __forceinline__ uint32_t gelu_pair(uint32_t u2)
+{
+    return (uint32_t)g_gelu_bf16[u2 & 0xffffu] | ((uint32_t)g_gelu_bf16[u2 >> 16] << 16);
 }
 
 // Dequantise and store a wave's 128 (n) x 32 TJ (m) block.  FULL: the tile
@@ -158,11 +173,81 @@ __device__ __forceinline__ v16i acc_frag(const v16i &a)
     return v;
 }
 
+// GELU epilogue, one 32-row slab j of a wave's block: dequantise, round to
+// bf16 and look up bf16(GELU(u)) for its 4 x 32 columns ...
+template <int OUT, bool HAS_BIAS, int TJ, int J>
+__device__ __forceinline__ void gelu_lookup(const v16i (&acc)[4][TJ],
+                                            const float (&sscale)[3][kTile], int wm, int wn,
+                                            int l32, int g, uint32_t (&gv)[4][2][2][2])
+{
+    const int ml = wm * 32 * TJ + 32 * J + l32;
+    const float sxm = sscale[0][ml];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const v16i av = acc_frag(acc[i][J]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q = 2 * p + h;
+                const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
+                const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
+                gv[i][p][h][0] = gelu_pair(cvt_pk_bf16(
+                    dequant1<OUT, HAS_BIAS>(av[4 * q + 0], sxm, swv.x, bv.x),
+                    dequant1<OUT, HAS_BIAS>(av[4 * q + 1], sxm, swv.y, bv.y)));
+                gv[i][p][h][1] = gelu_pair(cvt_pk_bf16(
+                    dequant1<OUT, HAS_BIAS>(av[4 * q + 2], sxm, swv.z, bv.z),
+                    dequant1<OUT, HAS_BIAS>(av[4 * q + 3], sxm, swv.w, bv.w)));
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// ... and store them, 16 contiguous bytes per lane (as the bf16 epilogue).
+template <int TJ, bool FULL, int J>
+__device__ __forceinline__ void gelu_store(void *Y, const uint32_t (&gv)[4][2][2][2], int M,
+                                           int N, int m0, int n0, int wm, int wn, int l32,
+                                           int g)
+{
+    const int m = m0 + wm * 32 * TJ + 32 * J + l32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(gv[i][p][0][0], gv[i][p][1][0],
+                                                             false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(gv[i][p][0][1], gv[i][p][1][1],
+                                                             false, false);
+            const int nb = n0 + wn * 128 + 32 * i + 16 * p + 8 * g;
+            if (!FULL && (m >= M || nb >= N)) continue;
+            uint4 o;
+            o.x = s0[0]; o.y = s1[0]; o.z = s0[1]; o.w = s1[1];
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(Y) + (int64_t)m * N + nb) = o;
+        }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int OUT, bool HAS_BIAS, int TJ, bool FULL>
 __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                                          const float (&sscale)[3][kTile], int M, int N,
                                          int m0, int n0, int wm, int wn, int l32, int g)
 {
+    if constexpr (OUT == int(OutKind::GELU_BF16)) {
+        // GELU outputs, 32 rows at a time: the table lookups of the next
+        // rows are issued before the stores of the current ones, so waiting
+        // for a lookup never waits for a store.
+        uint32_t ga[4][2][2][2], gb[4][2][2][2];   // [i][p][q - 2p][dword]
+        gelu_lookup<OUT, HAS_BIAS, TJ, 0>(acc, sscale, wm, wn, l32, g, ga);
+        gelu_lookup<OUT, HAS_BIAS, TJ, 1>(acc, sscale, wm, wn, l32, g, gb);
+        gelu_store<TJ, FULL, 0>(Y, ga, M, N, m0, n0, wm, wn, l32, g);
+        gelu_lookup<OUT, HAS_BIAS, TJ, 2>(acc, sscale, wm, wn, l32, g, ga);
+        gelu_store<TJ, FULL, 1>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
+        gelu_lookup<OUT, HAS_BIAS, TJ, 3>(acc, sscale, wm, wn, l32, g, gb);
+        gelu_store<TJ, FULL, 2>(Y, ga, M, N, m0, n0, wm, wn, l32, g);
+        gelu_store<TJ, FULL, 3>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
         const int ml = wm * 32 * TJ + 32 * j + l32;
@@ -228,6 +313,7 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+
 }
 
 // Copies of one tile go through buffer resources whose base is the tile's
@@ -552,6 +638,8 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
     const int wgs_per_xcd = std::max(1, std::min(device_cu_count() / 8, per_xcd));
     const int nk = (int)(K / kBK);
     const dim3 grid(8 * wgs_per_xcd), block(kThreads);
+    if constexpr (OUT == int(OutKind::GELU_BF16))
+        hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
     if (nk % 4 == 0)
         hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 4>), grid, block, 0, stream, qx, qw, sx,
                            sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
