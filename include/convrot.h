@@ -199,7 +199,7 @@ CONVROT_API int lowrank_convrot_forward(const void *X, int64_t M, const convrot_
                             void *stream);
 
 /* MLP pair: u = bf16(linear(X; W_up) + bias_up); g = bf16(GELU(u)) with the
- * erf form of GELU evaluated in fp32; Y = linear(g; W_down) + bias_down.
+ * erf form of GELU (see convrot_gelu_bf16); Y = linear(g; W_down) + bias_down.
  * Requires W_up->N == W_down->K (= F).  GELU is applied in the epilogue of the
  * up projection, so u is never written. */
 CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
@@ -231,6 +231,12 @@ CONVROT_API int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_wei
 CONVROT_API int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
                          const convrot_weights *W, const float *bias, void *Y,
                          int y_dtype, uint32_t flags, void *stream);
+
+/* g[i] = bf16(GELU(u[i])) for n bf16 values, exactly as the MLP entry point
+ * and CONVROT_FLAG_GELU apply it: GELU in its erf form, 0.5 z (1 + erf(z /
+ * sqrt 2)), evaluated in fp64 on the bf16 value z, rounded to fp32 and then
+ * to bf16 (nearest even).  u and g are device pointers; n >= 0. */
+CONVROT_API int convrot_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g, void *stream);
 
 #ifdef __cplusplus
 }

@@ -172,6 +172,9 @@ def test_hook_validation(cr):
     assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, cr.BF16, 2,
                                     None) == cr.EUNSUPPORTED
     assert lib.convrot_gemm_i32(FAKE_ODD, 4, ctypes.byref(d), FAKE, None) == cr.EALIGN
+    assert lib.convrot_gelu_bf16(FAKE, -1, FAKE, None) == cr.EINVAL
+    assert lib.convrot_gelu_bf16(None, 0, None, None) == cr.OK
+    assert lib.convrot_gelu_bf16(None, 4, FAKE, None) == cr.EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

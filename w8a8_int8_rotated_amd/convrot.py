@@ -65,6 +65,7 @@ _SIGNATURES = {
     "convrot_gemm_i32": (_c_int, [_c_p, _c_i64, _W, _c_p, _c_p]),
     "convrot_gemm_dequant": (
         _c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_int, ctypes.c_uint32, _c_p]),
+    "convrot_gelu_bf16": (_c_int, [_c_p, _c_i64, _c_p, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -297,4 +298,17 @@ def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeight
                                   _dtype_tag(out.dtype), FLAG_GELU if gelu else 0,
                                   _stream(stream))
     _check("convrot_gemm_dequant", rc)
+    return out
+
+
+def convrot_gelu_bf16(u: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """bf16(GELU(u)) elementwise, as the MLP's up projection applies it."""
+    lib = library()
+    if u.dtype != torch.bfloat16:
+        raise ValueError("u must be bf16")
+    u = u.contiguous()
+    if out is None:
+        out = torch.empty_like(u)
+    _check("convrot_gelu_bf16", lib.convrot_gelu_bf16(_ptr(u), u.numel(), _ptr(out),
+                                                      _stream(stream)))
     return out

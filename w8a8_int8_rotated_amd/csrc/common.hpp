@@ -27,14 +27,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// GELU, erf form, evaluated in fp32.
-__device__ __forceinline__ float gelu_erf(float z)
-{
-    const float k = 0.70710678118654752440f;
-    float e = erff(__fmul_rn(z, k));
-    return __fmul_rn(__fmul_rn(0.5f, z), __fadd_rn(1.0f, e));
-}
-
 } // namespace convrot
 
 // ------------------------------------------------------ kernel launchers ----
@@ -53,6 +45,9 @@ enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3 };
 hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
                            int64_t ld, int block, float inv_sqrt_b, int8_t *q,
                            float *s, hipStream_t stream);
+
+// g[i] = bf16(GELU(u[i])) for bf16 u, as the MLP's up projection applies it.
+hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream);
 
 // Transpose an [R, C] matrix of 1-, 2- or 4-byte elements into [C, R].
 hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,

@@ -388,4 +388,12 @@ int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
         static_cast<hipStream_t>(stream)));
 }
 
+int convrot_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g, void *stream)
+{
+    if (n < 0) return CONVROT_EINVAL;
+    if (n == 0) return CONVROT_OK;
+    if (!u || !g) return CONVROT_EINVAL;
+    return hip_status(convrot::launch_gelu_bf16(u, g, n, static_cast<hipStream_t>(stream)));
+}
+
 } // extern "C"

@@ -131,17 +131,30 @@ __device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float b
     return f;
 }
 
-// bf16(GELU(u)) for every bf16 bit pattern u (GELU in its erf form, fp32, on
-// the bf16 value of the up projection's output).  The MLP's up projection
-// looks its outputs up here instead of evaluating erff per element.  Every
-// launch that reads the table is preceded on its own stream by a launch that
-// (re)writes it with the same values, so a reader never sees a partial table.
+// bf16(GELU(u)) for every bf16 bit pattern u: GELU in its erf form,
+// 0.5 z (1 + erf(z / sqrt 2)), evaluated in fp64 on the bf16 value z of the
+// up projection's output, then rounded to fp32 and to bf16 (round to nearest
+// even both times).  The MLP's up projection looks its outputs up here
+// instead of evaluating erf per element.  Every launch that reads the table is
+// preceded on its own stream by a launch that (re)writes it with the same
+// values, so a reader never sees a partial table.
 __device__ uint16_t g_gelu_bf16[65536];
 
 __global__ __launch_bounds__(256) void gelu_table_kernel()
 {
     const uint32_t u = blockIdx.x * 256u + threadIdx.x;
-    g_gelu_bf16[u] = (uint16_t)(cvt_pk_bf16(gelu_erf(__uint_as_float(u << 16)), 0.0f) & 0xffffu);
+    const double z = (double)__uint_as_float(u << 16);
+    const double gd = 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+    g_gelu_bf16[u] = (uint16_t)f32_to_bf16_bits((float)gd);
+}
+
+// g[i] = bf16(GELU(u[i])) through the same table (the elementwise form the
+// MLP entry point applies inside its up projection).
+__global__ __launch_bounds__(256) void gelu_apply_kernel(const uint16_t *__restrict__ u,
+                                                         uint16_t *__restrict__ g, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) g[i] = g_gelu_bf16[u[i]];
 }
 
 __device__ __forceinline__ uint32_t gelu_pair(uint32_t u2)
@@ -674,6 +687,15 @@ hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
                   : launch_t<int(OutKind::GELU_BF16), false>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
+    hipLaunchKernelGGL(gelu_apply_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       u, g, n);
+    return hipGetLastError();
 }
 
 } // namespace convrot

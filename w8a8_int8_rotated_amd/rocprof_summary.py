@@ -6,6 +6,8 @@
         --fetch <fetch run_counter_collection.csv> --write <write ...csv> \\
         --copy-bytes 536870912 --kernel gemm_i8_kernel --source <kernel .hip> \\
         --command-fetch "..." --command-write "..." -o profiles/Y.md
+    python -m w8a8_int8_rotated_amd.rocprof_summary counters <run_counter_collection.csv> ... \\
+        --kernel gemm_i8_kernel --command "..." --command "..." -o profiles/Z.md
 
 `traffic` scales each counter by what it reads for the plain device copy of
 known size recorded in the same run (FETCH_SIZE and WRITE_SIZE are in KiB per
@@ -88,6 +90,49 @@ def traffic(args):
     _emit("\n".join(out), args.output)
 
 
+def counters(args):
+    """Average of every counter per dispatch of the kernel, over one or more
+    counter runs, with the derived figures the GEMM analysis uses."""
+    vals = {}
+    durs = []
+    for path in args.csv:
+        for r in csv.DictReader(open(path)):
+            if args.kernel not in r["Kernel_Name"]:
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {args.kernel!r}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    out = [f"# Counters of `{args.kernel}` -- {args.workload}", "",
+           "Commands (run from /tmp, repository at $R):", "", "```", *args.command, "```", "",
+           "| counter | dispatches | average per dispatch |", "|---|---:|---:|"]
+    for k in sorted(avg):
+        out.append(f"| {k} | {len(vals[k])} | {avg[k]:.6g} |")
+    out += ["", "Derived (per dispatch):", ""]
+    if "TCC_EA0_RDREQ_sum" in avg:
+        out.append(f"- L2 read misses to the fabric: {avg['TCC_EA0_RDREQ_sum'] * 128 / 1e9:.3f} GB "
+                   f"(128-byte requests)")
+    if "TCC_EA0_WRREQ_sum" in avg:
+        out.append(f"- L2 write requests: {avg['TCC_EA0_WRREQ_sum'] * 64 / 1e9:.3f} GB (64-byte)")
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+        h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
+        out.append(f"- L2 hit rate: {100 * h / (h + m):.1f}%")
+    if "GRBM_GUI_ACTIVE" in avg and durs:
+        d = sum(durs) / len(durs)
+        clk = avg["GRBM_GUI_ACTIVE"] / args.xcds / d
+        out.append(f"- shader clock: {clk:.3f} GHz (GRBM_GUI_ACTIVE / {args.xcds} XCDs over the "
+                   f"dispatch's {d / 1e3:.1f} us under the profiler)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / args.simds
+            out.append(f"- MFMA busy: {100 * busy / (clk * d):.1f}% of the dispatch's cycles per "
+                       f"SIMD ({args.simds} SIMDs)")
+    if "SQ_INSTS_VALU_MFMA_MOPS_I8" in avg:
+        out.append(f"- INT8 MFMA operations: {avg['SQ_INSTS_VALU_MFMA_MOPS_I8'] * 512:.4g}")
+    out.append("")
+    _emit("\n".join(out), args.output)
+
+
 def _emit(text, path):
     if path:
         open(path, "w").write(text)
@@ -114,8 +159,16 @@ def main():
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("-o", "--output")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--simds", type=int, default=1024)
+    c.add_argument("-o", "--output")
     a = p.parse_args()
-    stats(a) if a.cmd == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "counters": counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
