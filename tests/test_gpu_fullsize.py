@@ -78,3 +78,24 @@ def test_mlp_16384_fullsize(cr):
     y_ref = oracle.mlp_forward(x[rows], qu, su, qd, sd, w.block, out="bf16")
     yr = bf16_bits(y[torch.from_numpy(rows).cuda()])
     assert assert_output_parity(yr, y_ref, "bf16", "mlp_16384 sampled rows") == 0
+
+
+def test_qk_38656_small_k(cr):
+    """Small-K GEMM at the attention QK shape (K = head_dim = 128, one Hadamard
+    block per row): M = N = 38656, sampled output rows and INT32 rows."""
+    w = wl.WORKLOADS["qk_38656"]
+    announce(w.description)
+    x, W = w.activations(), w.weight()
+    pw, qw, sw = _prep(cr, W, w.block)
+    X = to_dev_bf16(x)
+    y = cr.convrot_linear_forward(X, pw)
+    qx, sx = cr.convrot_rotate_quantize(X, w.block)
+    torch.cuda.synchronize()
+    qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
+    assert np.array_equal(host(qx), qx_ref) and np.array_equal(host(sx), sx_ref)
+    rows = sample_rows(w.M, 48)
+    y_ref = oracle.linear_forward(x[rows], qw, sw, w.block, out="bf16")
+    yr = bf16_bits(y[torch.from_numpy(rows).cuda()])
+    assert assert_output_parity(yr, y_ref, "bf16", "qk_38656 sampled rows") == 0
+    acc = cr.convrot_gemm_i32(qx[torch.from_numpy(rows[:8]).cuda()].contiguous(), pw)
+    assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref[rows[:8]], qw))

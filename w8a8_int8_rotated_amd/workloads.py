@@ -151,6 +151,11 @@ WORKLOADS = {
         "mlp_16384", "mlp", M=16384, K=5376, N=5376, ffn=21504, block=128,
         out="bf16", x_dist="normal", w_std=0.02,
         description="MLP pair up M=16384 K=5376 N=21504, GELU, down K=21504 N=5376"),
+    "qk_38656": Workload(
+        "qk_38656", "linear", M=38656, K=128, N=38656, block=128, out="bf16",
+        x_dist="normal", w_std=0.02,
+        description="small-K INT8 GEMM at the attention QK shape: T=38656 tokens, "
+                    "head_dim K=128, b=128, bf16 out"),
     "lowrank_38656": Workload(
         "lowrank_38656", "lowrank", M=38656, K=5376, N=5376, rank=512, block=128,
         out="bf16", x_dist="normal", outlier_frac=0.02, outlier_gain=25.0,
