@@ -52,7 +52,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kTile = 256;     // tile edge in m and in n
+constexpr int kTile = 256;     // tile edge in n (and in m for TJ = 4)
 constexpr int kBK = 64;        // K bytes per LDS stage
 constexpr int kThreads = 256;
 constexpr int kGroup = 4;      // tile-rows per L2 group
@@ -254,11 +254,15 @@ __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
         gelu_lookup<OUT, HAS_BIAS, TJ, 0>(acc, sscale, wm, wn, l32, g, ga);
         gelu_lookup<OUT, HAS_BIAS, TJ, 1>(acc, sscale, wm, wn, l32, g, gb);
         gelu_store<TJ, FULL, 0>(Y, ga, M, N, m0, n0, wm, wn, l32, g);
-        gelu_lookup<OUT, HAS_BIAS, TJ, 2>(acc, sscale, wm, wn, l32, g, ga);
-        gelu_store<TJ, FULL, 1>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
-        gelu_lookup<OUT, HAS_BIAS, TJ, 3>(acc, sscale, wm, wn, l32, g, gb);
-        gelu_store<TJ, FULL, 2>(Y, ga, M, N, m0, n0, wm, wn, l32, g);
-        gelu_store<TJ, FULL, 3>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
+        if constexpr (TJ == 4) {
+            gelu_lookup<OUT, HAS_BIAS, TJ, 2>(acc, sscale, wm, wn, l32, g, ga);
+            gelu_store<TJ, FULL, 1>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
+            gelu_lookup<OUT, HAS_BIAS, TJ, 3>(acc, sscale, wm, wn, l32, g, gb);
+            gelu_store<TJ, FULL, 2>(Y, ga, M, N, m0, n0, wm, wn, l32, g);
+            gelu_store<TJ, FULL, 3>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
+        } else {
+            gelu_store<TJ, FULL, 1>(Y, gb, M, N, m0, n0, wm, wn, l32, g);
+        }
         return;
     }
 #pragma unroll
@@ -350,56 +354,64 @@ __device__ __forceinline__ TileSrc tile_src(const int8_t *qw, const int8_t *qx, 
     return t;
 }
 
-__device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t (&voff)[4])
+// Copy j of wave w moves rows [(n w + j) 16, +16) of an operand tile of 64 n
+// rows (n = 4 for the 256-row weight tile, TJ for the activation tile).
+template <int NC>
+__device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t (&voff)[NC])
 {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 16 + (lane >> 2);
+    for (int j = 0; j < NC; ++j) {
+        const int r = (wave * NC + j) * 16 + (lane >> 2);
         voff[j] = (uint32_t)r * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
     }
 }
 
-// Half H of K-tile `k` of the copy stream into one stage: copies j = 2H and
-// 2H + 1 of both operands.  Below nk the K-tile belongs to the current tile,
-// from nk on to the next one (the last tile of a workgroup re-reads its own
-// first K-tiles, which no one consumes).
-template <int H>
+// Half H of K-tile `k` of the copy stream into one stage: weight copies
+// j = 2H, 2H + 1 and activation copies j = H TJ/2 .. (H + 1) TJ/2 - 1.  Below
+// nk the K-tile belongs to the current tile, from nk on to the next one (the
+// last tile of a workgroup re-reads its own first K-tiles, which no one
+// consumes).
+template <int TJ, int H>
 __device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nxt,
-                                           const uint32_t (&voff)[4], int k, int nk, int wave,
-                                           int8_t *__restrict__ dst_w, int8_t *__restrict__ dst_x)
+                                           const uint32_t *voffw, const uint32_t *voffx, int k,
+                                           int nk, int wave, int8_t *__restrict__ dst_w,
+                                           int8_t *__restrict__ dst_x)
 {
     const bool next = k >= nk;
     const __amdgpu_buffer_rsrc_t rw = next ? nxt.w : cur.w, rx = next ? nxt.x : cur.x;
     const int soff = (next ? k - nk : k) * kBK;
 #pragma unroll
-    for (int j = 2 * H; j < 2 * H + 2; ++j) {
+    for (int j = 2 * H; j < 2 * H + 2; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rw, (__attribute__((address_space(3))) void *)(dst_w + (wave * 4 + j) * 1024), 16,
-            voff[j], soff, 0, 0);
+            voffw[j], soff, 0, 0);
+#pragma unroll
+    for (int j = H * TJ / 2; j < (H + 1) * TJ / 2; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (__attribute__((address_space(3))) void *)(dst_x + (wave * 4 + j) * 1024), 16,
-            voff[j], soff, 0, 0);
-    }
+            rx, (__attribute__((address_space(3))) void *)(dst_x + (wave * TJ + j) * 1024), 16,
+            voffx[j], soff, 0, 0);
 }
 
+template <int TJ>
 __device__ __forceinline__ void read_frags(const int8_t *__restrict__ sw_,
                                            const int8_t *__restrict__ sx_, int frow_w,
-                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[4])
+                                           int frow_x, int foff, v4i (&a)[4], v4i (&b)[TJ])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         a[i] = *reinterpret_cast<const v4i *>(sw_ + frow_w + 2048 * i + foff);
-        b[i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * i + foff);
+        if (i < TJ) b[i] = *reinterpret_cast<const v4i *>(sx_ + frow_x + 2048 * i + foff);
     }
 }
 
-__device__ __forceinline__ void mfma_block(v16i (&acc)[4][4], const v4i (&a)[4],
-                                           const v4i (&b)[4])
+template <int TJ>
+__device__ __forceinline__ void mfma_block(v16i (&acc)[4][TJ], const v4i (&a)[4],
+                                           const v4i (&b)[TJ])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
@@ -438,34 +450,36 @@ __device__ __forceinline__ void wait_vmcnt_either(bool second)
 // previous tile's stores and this tile's scale loads); stage S-1 is free.
 // On exit: K-tiles 0 .. S-2 of the next tile are in flight.  Requires
 // nk % S == 0.
-template <int S, int EPI>
+template <int TJ, int S, int EPI>
 __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
                                        int8_t *__restrict__ w2, int8_t *__restrict__ w3,
                                        int8_t *__restrict__ x0, int8_t *__restrict__ x1,
                                        int8_t *__restrict__ x2, int8_t *__restrict__ x3,
                                        const TileSrc &cur, const TileSrc &nxt,
-                                       const uint32_t (&voff)[4], int nk, bool first, int wave,
-                                       int frow_w, int frow_x, int foff0, int foff1,
-                                       v16i (&acc)[4][4])
+                                       const uint32_t (&voffw)[4], const uint32_t (&voffx)[TJ],
+                                       int nk, bool first, int wave, int frow_w, int frow_x,
+                                       int foff0, int foff1, v16i (&acc)[4][TJ])
 {
     static_assert(S == 2 || S == 4, "stages");
-    constexpr int C = 8;                     // copy instructions per wave per K-tile
+    static_assert(TJ == 2 || TJ == 4, "activation sub-tiles per wave");
+    constexpr int C = 4 + TJ;                // copy instructions per wave per K-tile
     constexpr int CH = C / 2;                // ... per half
+    constexpr int MF = 4 * TJ, RD = 4 + TJ;  // MFMAs and LDS reads per half
     static_assert((S - 2) * C + CH + EPI < 64, "vmcnt range");
-    v4i a0[4], b0[4], a1[4], b1[4];
+    v4i a0[4], b0[TJ], a1[4], b1[TJ];
     int8_t *const wl = pick<S, S - 1>(w0, w1, w2, w3), *const xl = pick<S, S - 1>(x0, x1, x2, x3);
 
     if (first) {
-        issue_half<0>(cur, nxt, voff, 0, nk, wave, w0, x0);
-        issue_half<1>(cur, nxt, voff, 0, nk, wave, w0, x0);
+        issue_half<TJ, 0>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
+        issue_half<TJ, 1>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
         if constexpr (S == 4) {
-            issue_half<0>(cur, nxt, voff, 1, nk, wave, w1, x1);
-            issue_half<1>(cur, nxt, voff, 1, nk, wave, w1, x1);
-            issue_half<0>(cur, nxt, voff, 2, nk, wave, w2, x2);
-            issue_half<1>(cur, nxt, voff, 2, nk, wave, w2, x2);
+            issue_half<TJ, 0>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
+            issue_half<TJ, 1>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
+            issue_half<TJ, 0>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
+            issue_half<TJ, 1>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
         }
     }
-    issue_half<0>(cur, nxt, voff, S - 1, nk, wave, wl, xl);
+    issue_half<TJ, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
     wait_vmcnt_either<(S - 2) * C + CH + EPI, (S - 2) * C + CH>(first);
     block_barrier();
     read_frags(w0, x0, frow_w, frow_x, foff0, a0, b0);
@@ -478,17 +492,17 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         wait_lds_reads();                                                                \
         __builtin_amdgcn_sched_barrier(0);                                               \
         read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
-        issue_half<1>(cur, nxt, voff, kt + (I) + S - 1, nk, wave, pw_, px_);             \
+        issue_half<TJ, 1>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_);             \
         mfma_block(acc, a0, b0);                                                         \
-        interleave<16, CH, 8>();                                                         \
+        interleave<MF, CH, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         wait_lds_reads();                                                                \
         wait_vmcnt_either<(S - 2) * C, (S - 2) * C + EPI>(!first && kt + (I) < S - 2);   \
         block_barrier();                                                                 \
         read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
-        issue_half<0>(cur, nxt, voff, kt + (I) + S, nk, wave, cw_, cx_);                 \
+        issue_half<TJ, 0>(cur, nxt, voffw, voffx, kt + (I) + S, nk, wave, cw_, cx_);                 \
         mfma_block(acc, a1, b1);                                                         \
-        interleave<16, CH, 8>();                                                         \
+        interleave<MF, CH, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
 
@@ -513,10 +527,10 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         wait_lds_reads();
         __builtin_amdgcn_sched_barrier(0);
         read_frags(wl, xl, frow_w, frow_x, foff1, a1, b1);
-        issue_half<1>(cur, nxt, voff, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
+        issue_half<TJ, 1>(cur, nxt, voffw, voffx, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
                       pick<S, S - 2>(x0, x1, x2, x3));
         mfma_block(acc, a0, b0);
-        interleave<16, CH, 8>();
+        interleave<MF, CH, RD>();
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, a1, b1);
     }
@@ -528,24 +542,26 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
 // next tile's first K-tiles land while the current one is dequantised and
 // stored, and its stores drain while the next tile computes.
 // S: LDS stages of 2 x 16 KiB (4 when nk % 4 == 0, else 2).
-template <int OUT, bool HAS_BIAS, int S>
+template <int OUT, bool HAS_BIAS, int TJ, int S>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw,
     const float *__restrict__ sx, const float *__restrict__ sw,
     const float *__restrict__ bias, void *__restrict__ Y, int M, int N, int K,
     int tiles_m, int tiles_n, int tiles_per_xcd, int wgs_per_xcd)
 {
-    constexpr int STG = kTile * kBK;   // 16 KiB per operand
+    constexpr int TM = 64 * TJ;            // tile edge in m
+    constexpr int STGW = kTile * kBK;      // 16 KiB of weights per stage
+    constexpr int STGX = TM * kBK;         // 16 or 8 KiB of activations per stage
     constexpr bool BF16_OUT = OUT == int(OutKind::BF16) || OUT == int(OutKind::GELU_BF16);
     constexpr int NSCALE = OUT == int(OutKind::I32) ? 0 : (HAS_BIAS ? 3 : 2);
     // memory operations per wave between a tile's K-tile S-2 copies and its
-    // K-tile S-1 copies: the previous tile's stores (bf16: 4 x 4 x 2 of 16 B)
+    // K-tile S-1 copies: the previous tile's stores (bf16: 4 x TJ x 2 of 16 B)
     // and this tile's scale loads; other outputs drain at the tile boundary
-    constexpr int EPI = (BF16_OUT ? 32 : 0) + NSCALE;
-    __shared__ __attribute__((aligned(1024))) int8_t sw0[STG], sw1[STG], sw2[S == 4 ? STG : 16],
-        sw3[S == 4 ? STG : 16];
-    __shared__ __attribute__((aligned(1024))) int8_t sx0[STG], sx1[STG], sx2[S == 4 ? STG : 16],
-        sx3[S == 4 ? STG : 16];
+    constexpr int EPI = (BF16_OUT ? 8 * TJ : 0) + NSCALE;
+    __shared__ __attribute__((aligned(1024))) int8_t sw0[STGW], sw1[STGW],
+        sw2[S == 4 ? STGW : 16], sw3[S == 4 ? STGW : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t sx0[STGX], sx1[STGX],
+        sx2[S == 4 ? STGX : 16], sx3[S == 4 ? STGX : 16];
     __shared__ __attribute__((aligned(16))) float sscale[3][kTile];   // s_x, s_w, bias
 
     const int tid = threadIdx.x;
@@ -564,7 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         const int width = kGroup * tiles_n;
         const int first_m = (t / width) * kGroup;
         const int gsz = min(tiles_m - first_m, kGroup);
-        m0 = (first_m + (t % width) % gsz) * kTile;
+        m0 = (first_m + (t % width) % gsz) * TM;
         n0 = ((t % width) / gsz) * kTile;
         return true;
     };
@@ -576,7 +592,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int foff0 = ((0 + g) ^ swz(l32)) << 4;
     const int foff1 = ((2 + g) ^ swz(l32)) << 4;
     const int frow_w = (wn * 128 + l32) * kBK;   // + 2048 * i
-    const int frow_x = (wm * 128 + l32) * kBK;   // + 2048 * j
+    const int frow_x = (wm * 32 * TJ + l32) * kBK;   // + 2048 * j
 
     auto load_scales = [&](int m0_, int n0_, float &a, float &b, float &c) {
         if constexpr (OUT != int(OutKind::I32)) {
@@ -588,24 +604,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 
     float sc_x = 0.f, sc_w = 0.f, sc_b = 0.f;
     load_scales(m0, n0, sc_x, sc_w, sc_b);
-    uint32_t voff[4];
-    lane_offsets(K, wave, lane, voff);
+    uint32_t voffw[4], voffx[TJ];
+    lane_offsets(K, wave, lane, voffw);
+    lane_offsets(K, wave, lane, voffx);
     TileSrc cur = tile_src(qw, qx, m0, n0, M, N, K);
     int nm0 = m0, nn0 = n0;
     bool more = tile_at(1, nm0, nn0);
     TileSrc nxt = more ? tile_src(qw, qx, nm0, nn0, M, N, K) : cur;
 
     for (int it = 0;; ++it) {
-        v16i acc[4][4];
+        v16i acc[4][TJ];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < TJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-        k_loop<S, EPI>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voff, nk, it == 0,
-                       wave, frow_w, frow_x, foff0, foff1, acc);
+        k_loop<TJ, S, EPI>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw, voffx, nk,
+                           it == 0, wave, frow_w, frow_x, foff0, foff1, acc);
 
         if constexpr (OUT != int(OutKind::I32)) {
             sscale[0][tid] = sc_x;
@@ -616,11 +633,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         // copies already in flight
         wait_lds_reads();
         block_barrier();
-        const bool full = m0 + kTile <= M && n0 + kTile <= N;
+        const bool full = m0 + TM <= M && n0 + kTile <= N;
         if (full)
-            epilogue<OUT, HAS_BIAS, 4, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+            epilogue<OUT, HAS_BIAS, TJ, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
         else
-            epilogue<OUT, HAS_BIAS, 4, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+            epilogue<OUT, HAS_BIAS, TJ, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
 
         if (!more) break;
         // The next tile's waits count exactly EPI operations issued after its
@@ -639,29 +656,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     wait_vmcnt<0>();
 }
 
+template <int OUT, bool HAS_BIAS, int TJ>
+hipError_t launch_tj(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
+                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K, int cus,
+                     hipStream_t stream)
+{
+    constexpr int TM = 64 * TJ;
+    const int tiles_m = (int)((M + TM - 1) / TM);
+    const int tiles_n = (int)((N + kTile - 1) / kTile);
+    const int tiles = tiles_m * tiles_n;
+    const int per_xcd = (tiles + 7) / 8;
+    const int wgs_per_xcd = std::max(1, std::min(cus / 8, per_xcd));
+    const int nk = (int)(K / kBK);
+    const dim3 grid(8 * wgs_per_xcd), block(kThreads);
+    if (nk % 4 == 0)
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, TJ, 4>), grid, block, 0, stream, qx, qw,
+                           sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
+                           wgs_per_xcd);
+    else
+        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, TJ, 2>), grid, block, 0, stream, qx, qw,
+                           sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
+                           wgs_per_xcd);
+    return hipGetLastError();
+}
+
+// 256 x 256 tiles.  The kernel also builds 256 (n) x 128 (m) tiles (TJ = 2):
+// they fill the last round better when tiles are few (M = 4096, or N = 512),
+// but ran no faster on those shapes and 20% slower on large ones (more LDS
+// reads and copies per MFMA), so only TJ = 4 is launched.
 template <int OUT, bool HAS_BIAS>
 hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream)
 {
-    const int tiles_m = (int)((M + kTile - 1) / kTile);
-    const int tiles_n = (int)((N + kTile - 1) / kTile);
-    const int tiles = tiles_m * tiles_n;
-    const int per_xcd = (tiles + 7) / 8;
-    const int wgs_per_xcd = std::max(1, std::min(device_cu_count() / 8, per_xcd));
-    const int nk = (int)(K / kBK);
-    const dim3 grid(8 * wgs_per_xcd), block(kThreads);
     if constexpr (OUT == int(OutKind::GELU_BF16))
         hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
-    if (nk % 4 == 0)
-        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 4>), grid, block, 0, stream, qx, qw, sx,
-                           sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
-                           wgs_per_xcd);
-    else
-        hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, 2>), grid, block, 0, stream, qx, qw, sx,
-                           sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
-                           wgs_per_xcd);
-    return hipGetLastError();
+    return launch_tj<OUT, HAS_BIAS, 4>(qx, qw, sx, sw, bias, Y, M, N, K, device_cu_count(),
+                                       stream);
 }
 
 } // namespace
