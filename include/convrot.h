@@ -232,6 +232,20 @@ CONVROT_API int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_
                          const convrot_weights *W, const float *bias, void *Y,
                          int y_dtype, uint32_t flags, void *stream);
 
+/* Factor 1 of the low-rank chain and the requantisation of its output, in
+ * one kernel: h = bf16(((float)(q_x . codes(A)^T) * s_x) * s_A) [M, r] with
+ * r = A->N, then (q_h, s_h) = rotate_quantize(h) with block A->block, exactly
+ * as lowrank_convrot_forward feeds factor 2 (low-rank ConvRot linears: the
+ * MLX model card, "Choose a Weight Format").  h itself is never written.
+ * q_x [M, A->K] int8 and s_x [M] F32 come from convrot_rotate_quantize;
+ * q_h [M, r] int8 and s_h [M] F32 are written.  All device pointers, 16-byte
+ * aligned.  Supported for A->block in {64, 128} and r <= 512
+ * (CONVROT_EUNSUPPORTED otherwise; lowrank_convrot_forward then runs the
+ * two stages separately). */
+CONVROT_API int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int64_t M,
+                            const convrot_weights *A, int8_t *q_h, float *s_h,
+                            void *stream);
+
 /* g[i] = bf16(GELU(u[i])) for n bf16 values, exactly as the MLP entry point
  * and CONVROT_FLAG_GELU apply it: GELU in its erf form, 0.5 z (1 + erf(z /
  * sqrt 2)), evaluated in fp64 on the bf16 value z, rounded to fp32 and then

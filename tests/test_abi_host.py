@@ -172,6 +172,15 @@ def test_hook_validation(cr):
     assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, cr.BF16, 2,
                                     None) == cr.EUNSUPPORTED
     assert lib.convrot_gemm_i32(FAKE_ODD, 4, ctypes.byref(d), FAKE, None) == cr.EALIGN
+    f1 = lambda d, M=4, qx=FAKE, sx=FAKE, qh=FAKE, sh=FAKE: lib.convrot_lowrank_factor1(
+        qx, sx, M, ctypes.byref(d), qh, sh, None)
+    assert f1(_desc(cr, N=640)) == cr.EUNSUPPORTED             # r > 512
+    assert f1(_desc(cr, block=256)) == cr.EUNSUPPORTED         # block 256
+    assert f1(_desc(cr, magic=0)) == cr.ELAYOUT
+    assert f1(_desc(cr), M=0, qx=None, sx=None, qh=None, sh=None) == cr.OK
+    assert f1(_desc(cr), qh=None) == cr.EINVAL
+    assert f1(_desc(cr), M=-1) == cr.EINVAL
+    assert f1(_desc(cr, N=256, block=64), sh=FAKE_ODD) == cr.EALIGN
     assert lib.convrot_gelu_bf16(FAKE, -1, FAKE, None) == cr.EINVAL
     assert lib.convrot_gelu_bf16(None, 0, None, None) == cr.OK
     assert lib.convrot_gelu_bf16(None, 4, FAKE, None) == cr.EINVAL

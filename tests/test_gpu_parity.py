@@ -257,6 +257,48 @@ def test_lowrank_small_full(cr):
     assert mism == 0
 
 
+@pytest.mark.parametrize("M,K,r,block", [
+    (520, 1024, 256, 128),      # ragged last tile, two waves idle
+    (1000, 640, 512, 64),       # b = 64: two rotation blocks per wave, S = 2 stages
+    (256, 512, 128, 128),       # one wave active
+    (1, 256, 384, 128),         # a single token
+])
+def test_lowrank_factor1_fused(cr, M, K, r, block):
+    """The fused factor-1 kernel's codes and row scales equal the oracle's
+    rotate_quantize of the oracle's bf16 h bit for bit."""
+    _check_factor1(cr, M, K, r, block)
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("shape", ["one_round", "split_tail"])
+def test_lowrank_factor1_tile_plans(cr, shape):
+    """128-token tiles only (the last round fills more than half the CUs), and
+    whole rounds of 128-token tiles followed by a launch of 64-token tiles."""
+    cus = _cus()
+    M = cus * 64 + 100 if shape == "one_round" else cus * 128 + 300
+    _check_factor1(cr, M, 256, 512, 128)
+
+
+def _check_factor1(cr, M, K, r, block):
+    announce(f"lowrank factor1 M={M} K={K} r={r} b={block}")
+    w = wl.scaled("lowrank_38656", M=M, K=K, N=256, rank=r, block=block)
+    x, A = w.activations(), w.weight("w")
+    pa, qa, sa = _prepare_pair(cr, A, block)
+    qx, sx = oracle.rotate_quantize(x, block, "bf16")
+    q_h, s_h = cr.convrot_lowrank_factor1(to_dev(qx), to_dev(sx), pa)
+    h = oracle.dequant(oracle.gemm_i32(qx, qa), sx, sa, out="bf16")
+    qh_ref, sh_ref = oracle.rotate_quantize(h, block, "bf16")
+    qh, sh = host(q_h), host(s_h)
+    print(f"[parity] factor1: {int((qh != qh_ref).sum())} codes and "
+          f"{int((sh.view(np.uint32) != sh_ref.view(np.uint32)).sum())} scales differ",
+          flush=True)
+    assert np.array_equal(qh, qh_ref)
+    assert np.array_equal(sh.view(np.uint32), sh_ref.view(np.uint32))
+
+
 # ---------------------------------------------------------------- MLP ----
 
 def test_gelu_exhaustive(cr):

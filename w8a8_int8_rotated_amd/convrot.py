@@ -65,6 +65,7 @@ _SIGNATURES = {
     "convrot_gemm_i32": (_c_int, [_c_p, _c_i64, _W, _c_p, _c_p]),
     "convrot_gemm_dequant": (
         _c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_int, ctypes.c_uint32, _c_p]),
+    "convrot_lowrank_factor1": (_c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_p]),
     "convrot_gelu_bf16": (_c_int, [_c_p, _c_i64, _c_p, _c_p]),
 }
 
@@ -299,6 +300,22 @@ def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeight
                                   _stream(stream))
     _check("convrot_gemm_dequant", rc)
     return out
+
+
+def convrot_lowrank_factor1(q_x: torch.Tensor, s_x: torch.Tensor, A: PreparedWeights,
+                            q_h=None, s_h=None, stream=None):
+    """Factor 1 of the low-rank chain with its output rotated and requantised:
+    returns (q_h [M, r] int8, s_h [M] f32)."""
+    lib = library()
+    M = q_x.shape[0]
+    if q_h is None:
+        q_h = torch.empty((M, A.N), dtype=torch.int8, device=q_x.device)
+    if s_h is None:
+        s_h = torch.empty(M, dtype=torch.float32, device=q_x.device)
+    rc = lib.convrot_lowrank_factor1(_ptr(q_x), _ptr(s_x), M, A.ref(), _ptr(q_h), _ptr(s_h),
+                                     _stream(stream))
+    _check("convrot_lowrank_factor1", rc)
+    return q_h, s_h
 
 
 def convrot_gelu_bf16(u: torch.Tensor, out=None, stream=None) -> torch.Tensor:

@@ -46,6 +46,14 @@ hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
                            int64_t ld, int block, float inv_sqrt_b, int8_t *q,
                            float *s, hipStream_t stream);
 
+// Factor 1 of the low-rank chain with the requantisation fused in:
+// (qh, sh) = rotate+quantise(bf16(((float)(qx . qa^T) * sx) * sa)) along the R
+// outputs, for R % 128 == 0, R <= 512 and block 64 or 128 (lowrank_f1_fusable).
+bool lowrank_f1_fusable(int64_t R, int block);
+hipError_t launch_lowrank_f1(const int8_t *qx, const int8_t *qa, const float *sx,
+                             const float *sa, int8_t *qh, float *sh, int64_t M, int64_t R,
+                             int64_t K, int block, float inv_sqrt_b, hipStream_t stream);
+
 // g[i] = bf16(GELU(u[i])) for bf16 u, as the MLP's up projection applies it.
 hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream);
 

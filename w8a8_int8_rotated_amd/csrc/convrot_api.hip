@@ -284,11 +284,20 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
     const float isb = inv_sqrt_block(A->block);
     hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, A->K, A->K, A->block,
                                             isb, qx, sx, s);
-    if (e == hipSuccess)
-        e = convrot::launch_gemm_i8(qx, A->codes, sx, A->scale, nullptr, h,
-                                    convrot::OutKind::BF16, M, r, A->K, s);
-    if (e == hipSuccess)
-        e = convrot::launch_rotquant(h, convrot::InType::BF16, M, r, r, B->block, isb, qh, sh, s);
+    if (convrot::lowrank_f1_fusable(r, A->block)) {
+        // a row of H fits one workgroup tile: factor 1 rotates and
+        // requantises it in its epilogue, H never reaches memory
+        if (e == hipSuccess)
+            e = convrot::launch_lowrank_f1(qx, A->codes, sx, A->scale, qh, sh, M, r, A->K,
+                                           A->block, isb, s);
+    } else {
+        if (e == hipSuccess)
+            e = convrot::launch_gemm_i8(qx, A->codes, sx, A->scale, nullptr, h,
+                                        convrot::OutKind::BF16, M, r, A->K, s);
+        if (e == hipSuccess)
+            e = convrot::launch_rotquant(h, convrot::InType::BF16, M, r, r, B->block, isb, qh,
+                                         sh, s);
+    }
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qh, B->codes, sh, B->scale, bias, Y, out_kind(y_dtype), M,
                                     B->N, r, s);
@@ -386,6 +395,24 @@ int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
         q_x, W->codes, s_x, W->scale, bias, Y,
         gelu ? convrot::OutKind::GELU_BF16 : out_kind(y_dtype), M, W->N, W->K,
         static_cast<hipStream_t>(stream)));
+}
+
+int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int64_t M,
+                            const convrot_weights *A, int8_t *q_h, float *s_h, void *stream)
+{
+    int rc = check_weights(A);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, A->K)) != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, A->N)) != CONVROT_OK) return rc;
+    if (!convrot::lowrank_f1_fusable(A->N, A->block)) return CONVROT_EUNSUPPORTED;
+    if (M == 0) return CONVROT_OK;
+    if (!q_x || !s_x || !q_h || !s_h) return CONVROT_EINVAL;
+    if (!aligned16(q_x) || !aligned16(s_x) || !aligned16(q_h) || !aligned16(s_h))
+        return CONVROT_EALIGN;
+    return hip_status(convrot::launch_lowrank_f1(q_x, A->codes, s_x, A->scale, q_h, s_h, M,
+                                                 A->N, A->K, A->block,
+                                                 inv_sqrt_block(A->block),
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int convrot_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g, void *stream)

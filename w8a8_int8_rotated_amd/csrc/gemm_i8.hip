@@ -58,6 +58,8 @@ constexpr int kThreads = 256;
 constexpr int kGroup = 4;      // tile-rows per L2 group
 // buffer resource word 3: raw (untyped) 32-bit data format, no swizzle
 constexpr int kRsrcWord3 = 0x00020000;
+// rint(t) for |t| < 2^22 lands in the low bits of t + 1.5 * 2^23
+constexpr float kMagicRint = 12582912.0f;
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
@@ -366,12 +368,13 @@ __device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t
     }
 }
 
-// Half H of K-tile `k` of the copy stream into one stage: weight copies
-// j = 2H, 2H + 1 and activation copies j = H TJ/2 .. (H + 1) TJ/2 - 1.  Below
-// nk the K-tile belongs to the current tile, from nk on to the next one (the
-// last tile of a workgroup re-reads its own first K-tiles, which no one
+// Half H of K-tile `k` of the copy stream into one stage: the wave's weight
+// copies j = H CW/2 .. (H + 1) CW/2 - 1 and its activation copies
+// [0, ceil(CX/2)) in half 0, the rest in half 1.
+// Below nk the K-tile belongs to the current tile, from nk on to the next one
+// (the last tile of a workgroup re-reads its own first K-tiles, which no one
 // consumes).
-template <int TJ, int H>
+template <int CW, int CX, int H>
 __device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nxt,
                                            const uint32_t *voffw, const uint32_t *voffx, int k,
                                            int nk, int wave, int8_t *__restrict__ dst_w,
@@ -381,14 +384,14 @@ __device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nx
     const __amdgpu_buffer_rsrc_t rw = next ? nxt.w : cur.w, rx = next ? nxt.x : cur.x;
     const int soff = (next ? k - nk : k) * kBK;
 #pragma unroll
-    for (int j = 2 * H; j < 2 * H + 2; ++j)
+    for (int j = H * CW / 2; j < (H + 1) * CW / 2; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rw, (__attribute__((address_space(3))) void *)(dst_w + (wave * 4 + j) * 1024), 16,
+            rw, (__attribute__((address_space(3))) void *)(dst_w + (wave * CW + j) * 1024), 16,
             voffw[j], soff, 0, 0);
 #pragma unroll
-    for (int j = H * TJ / 2; j < (H + 1) * TJ / 2; ++j)
+    for (int j = H ? (CX + 1) / 2 : 0; j < (H ? CX : (CX + 1) / 2); ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (__attribute__((address_space(3))) void *)(dst_x + (wave * TJ + j) * 1024), 16,
+            rx, (__attribute__((address_space(3))) void *)(dst_x + (wave * CX + j) * 1024), 16,
             voffx[j], soff, 0, 0);
 }
 
@@ -450,37 +453,38 @@ __device__ __forceinline__ void wait_vmcnt_either(bool second)
 // previous tile's stores and this tile's scale loads); stage S-1 is free.
 // On exit: K-tiles 0 .. S-2 of the next tile are in flight.  Requires
 // nk % S == 0.
-template <int TJ, int S, int EPI>
+template <int TJ, int CW, int CX, int S, int EPI>
 __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
                                        int8_t *__restrict__ w2, int8_t *__restrict__ w3,
                                        int8_t *__restrict__ x0, int8_t *__restrict__ x1,
                                        int8_t *__restrict__ x2, int8_t *__restrict__ x3,
                                        const TileSrc &cur, const TileSrc &nxt,
-                                       const uint32_t (&voffw)[4], const uint32_t (&voffx)[TJ],
+                                       const uint32_t *voffw, const uint32_t *voffx,
                                        int nk, bool first, int wave, int frow_w, int frow_x,
                                        int foff0, int foff1, v16i (&acc)[4][TJ])
 {
     static_assert(S == 2 || S == 4, "stages");
     static_assert(TJ == 2 || TJ == 4, "activation sub-tiles per wave");
-    constexpr int C = 4 + TJ;                // copy instructions per wave per K-tile
-    constexpr int CH = C / 2;                // ... per half
+    static_assert(CW % 2 == 0, "weight copies split evenly over two halves");
+    constexpr int C = CW + CX;               // copy instructions per wave per K-tile
+    constexpr int CH0 = CW / 2 + (CX + 1) / 2, CH1 = C - CH0;   // ... in each half
     constexpr int MF = 4 * TJ, RD = 4 + TJ;  // MFMAs and LDS reads per half
-    static_assert((S - 2) * C + CH + EPI < 64, "vmcnt range");
+    static_assert((S - 2) * C + CH0 + EPI < 64, "vmcnt range");
     v4i a0[4], b0[TJ], a1[4], b1[TJ];
     int8_t *const wl = pick<S, S - 1>(w0, w1, w2, w3), *const xl = pick<S, S - 1>(x0, x1, x2, x3);
 
     if (first) {
-        issue_half<TJ, 0>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
-        issue_half<TJ, 1>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
+        issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
+        issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
         if constexpr (S == 4) {
-            issue_half<TJ, 0>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
-            issue_half<TJ, 1>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
-            issue_half<TJ, 0>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
-            issue_half<TJ, 1>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
+            issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
+            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
+            issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
+            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
         }
     }
-    issue_half<TJ, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
-    wait_vmcnt_either<(S - 2) * C + CH + EPI, (S - 2) * C + CH>(first);
+    issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+    wait_vmcnt_either<(S - 2) * C + CH0 + EPI, (S - 2) * C + CH0>(first);
     block_barrier();
     read_frags(w0, x0, frow_w, frow_x, foff0, a0, b0);
 
@@ -492,17 +496,17 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         wait_lds_reads();                                                                \
         __builtin_amdgcn_sched_barrier(0);                                               \
         read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
-        issue_half<TJ, 1>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_);             \
+        issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_);             \
         mfma_block(acc, a0, b0);                                                         \
-        interleave<MF, CH, RD>();                                                         \
+        interleave<MF, CH1, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         wait_lds_reads();                                                                \
         wait_vmcnt_either<(S - 2) * C, (S - 2) * C + EPI>(!first && kt + (I) < S - 2);   \
         block_barrier();                                                                 \
         read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
-        issue_half<TJ, 0>(cur, nxt, voffw, voffx, kt + (I) + S, nk, wave, cw_, cx_);                 \
+        issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, kt + (I) + S, nk, wave, cw_, cx_);                 \
         mfma_block(acc, a1, b1);                                                         \
-        interleave<MF, CH, RD>();                                                         \
+        interleave<MF, CH0, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
 
@@ -527,10 +531,10 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         wait_lds_reads();
         __builtin_amdgcn_sched_barrier(0);
         read_frags(wl, xl, frow_w, frow_x, foff1, a1, b1);
-        issue_half<TJ, 1>(cur, nxt, voffw, voffx, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
+        issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
                       pick<S, S - 2>(x0, x1, x2, x3));
         mfma_block(acc, a0, b0);
-        interleave<MF, CH, RD>();
+        interleave<MF, CH1, RD>();
         __builtin_amdgcn_sched_barrier(0);
         mfma_block(acc, a1, b1);
     }
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-        k_loop<TJ, S, EPI>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw, voffx, nk,
+        k_loop<TJ, 4, TJ, S, EPI>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw, voffx, nk,
                            it == 0, wave, frow_w, frow_x, foff0, foff1, acc);
 
         if constexpr (OUT != int(OutKind::I32)) {
@@ -680,6 +684,295 @@ hipError_t launch_tj(const int8_t *qx, const int8_t *qw, const float *sx, const 
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Factor 1 of the low-rank chain with the requantisation of its output fused
+// into the epilogue.  The chain is h = bf16(linear(X; A)) followed by the
+// rotate + per-token quantise of h along r (low-rank ConvRot linears: the MLX
+// card, "Choose a Weight Format" and "Standalone Transformer"); since a row of
+// h has only r <= 512 entries, a 128-token x 512-output tile holds whole rows,
+// so the rotation, the row amax and the codes are computed here and h never
+// reaches memory.
+//
+// Wave w owns outputs [128 w, 128 w + 128): one Hadamard block of 128 (or two
+// of 64) for each of the tile's 128 tokens.  In the accumulator layout lane
+// (l32, g) holds, for token 32 j + l32, the outputs n = 32 i + 8 q + 4 g + r
+// (i, q, r = 0..3): index bits 0-1 are r, bit 2 is g, bits 3-4 q, bits 5-6 i.
+// Butterfly stages on r, q and i stay in the lane; the stage on g pairs lane
+// l32 with lane l32 + 32 through v_permlane32_swap.  Stages run in ascending
+// stride, each as (a + b, a - b), exactly the order of the reading.
+// ---------------------------------------------------------------------------
+
+// v_accvgpr_write: keep a value in the accumulator registers (the rotated
+// outputs wait there between the amax pass and the quantise pass).
+__device__ __forceinline__ int to_acc(float v)
+{
+    int a;
+    asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+    return a;
+}
+
+// One stage of stride H over the 64 values [i][q][r] a lane holds for one token.
+template <int H>
+__device__ __forceinline__ void f1_stage(float (&v)[4][4][4], int g)
+{
+    if constexpr (H == 4) {
+        // across the lane halves: the lower lane (g = 0) gets a + b, the upper
+        // one a - b; an fma by +-1 rounds exactly like the add or subtract
+        const float c = g ? -1.0f : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const auto pr = __builtin_amdgcn_permlane32_swap(
+                        __float_as_int(v[i][q][r]), __float_as_int(v[i][q][r]), false, false);
+                    // pr[0]: the lower lane's value, pr[1]: the upper lane's
+                    v[i][q][r] = __builtin_fmaf(c, __int_as_float(pr[1]), __int_as_float(pr[0]));
+                }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = 32 * i + 8 * q + r;   // bit 2 (g) is 0 here
+                    if ((n & H) != 0) continue;
+                    const int n2 = n + H;
+                    float &a = v[i][q][r];
+                    float &b = v[n2 >> 5][(n2 >> 3) & 3][n2 & 3];
+                    const float s0 = __fadd_rn(a, b), d0 = __fsub_rn(a, b);
+                    a = s0;
+                    b = d0;
+                }
+    }
+}
+
+template <int BLK, int TJ>
+__device__ __forceinline__ void f1_epilogue(v16i (&acc)[4][TJ], const float *s_x,
+                                            const float *s_a, float *red, int8_t *qh, float *sh,
+                                            int m0, int M, int R, float inv_sqrt_b, int wave,
+                                            int l32, int g)
+{
+    constexpr int TM = 32 * TJ;
+    // pass 1: h = bf16(((float)acc * s_x) * s_a), rotated, kept in the
+    // accumulators; partial |max| of each token's row
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        float v[4][4][4];
+        const float sxm = s_x[32 * j + l32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v16i av = acc_frag(acc[i][j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 sav =
+                    *reinterpret_cast<const float4 *>(&s_a[wave * 128 + 32 * i + 8 * q + 4 * g]);
+                const float sa4[4] = {sav.x, sav.y, sav.z, sav.w};
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    const uint32_t p = cvt_pk_bf16(
+                        __fmul_rn(__fmul_rn((float)av[4 * q + r], sxm), sa4[r]),
+                        __fmul_rn(__fmul_rn((float)av[4 * q + r + 1], sxm), sa4[r + 1]));
+                    v[i][q][r] = __uint_as_float(p << 16);
+                    v[i][q][r + 1] = __uint_as_float(p & 0xffff0000u);
+                }
+            }
+        }
+        f1_stage<1>(v, g);
+        f1_stage<2>(v, g);
+        f1_stage<4>(v, g);
+        f1_stage<8>(v, g);
+        f1_stage<16>(v, g);
+        f1_stage<32>(v, g);
+        if constexpr (BLK == 128) f1_stage<64>(v, g);
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    m = fmaxf(m, fabsf(v[i][q][r]));
+                    acc[i][j][4 * q + r] = to_acc(v[i][q][r]);
+                }
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (g == 0) red[wave * TM + 32 * j + l32] = m;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lds_reads();
+    block_barrier();
+
+    // pass 2: the row amax over the four waves, codes and scales
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(qh + (int64_t)m0 * R), (short)0, (M - m0) * R, kRsrcWord3);
+    const bool active = wave * 128 < R;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int row = 32 * j + l32;
+        const float amax = fmaxf(fmaxf(red[row], red[TM + row]),
+                                 fmaxf(red[2 * TM + row], red[3 * TM + row]));
+        const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
+        if (wave == 0 && g == 0 && m0 + row < M)
+            sh[m0 + row] = __fmul_rn(__fdiv_rn(amax, 127.0f), inv_sqrt_b);
+        if (!active) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v16i av = acc_frag(acc[i][j]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t c[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    c[r] = __float_as_uint(__fadd_rn(__fmul_rn(__int_as_float(av[4 * q + r]), inv),
+                                                     kMagicRint));
+                const uint32_t w01 = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);
+                const uint32_t w23 = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    (int)__builtin_amdgcn_perm(w23, w01, 0x05040100u), qr,
+                    row * R + wave * 128 + 32 * i + 8 * q + 4 * g, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int BLK, int S, int TJ>
+__global__ __launch_bounds__(kThreads, 1) void lowrank_f1_kernel(
+    const int8_t *__restrict__ qx, const int8_t *__restrict__ qa,
+    const float *__restrict__ sx, const float *__restrict__ sa, int8_t *__restrict__ qh,
+    float *__restrict__ sh, int M, int R, int K, float inv_sqrt_b)
+{
+    constexpr int TM = 32 * TJ;             // tokens per tile: 128 or 64
+    constexpr int CX = TJ / 2;              // activation copies per wave per K-tile
+    constexpr int STGW = 512 * kBK;         // 32 KiB of A codes per stage
+    constexpr int STGX = TM * kBK;          // 8 or 4 KiB of activation codes per stage
+    constexpr int NSCALE = 3;               // per thread: a token scale, two channel scales
+    __shared__ __attribute__((aligned(1024))) int8_t sw0[STGW], sw1[STGW],
+        sw2[S == 4 ? STGW : 16], sw3[S == 4 ? STGW : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t sx0[STGX], sx1[STGX],
+        sx2[S == 4 ? STGX : 16], sx3[S == 4 ? STGX : 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, g = lane >> 5;
+    const int tiles = (M + TM - 1) / TM;
+    const int nk = K / kBK;
+    const int foff0 = ((0 + g) ^ swz(l32)) << 4;
+    const int foff1 = ((2 + g) ^ swz(l32)) << 4;
+    const int frow_w = (wave * 128 + l32) * kBK;   // + 2048 * i
+    const int frow_x = l32 * kBK;                  // + 2048 * j
+    uint32_t voffw[8], voffx[CX];
+    lane_offsets(K, wave, lane, voffw);
+    lane_offsets(K, wave, lane, voffx);
+
+    auto src_of = [&](int t) {
+        TileSrc ts;
+        ts.w = __builtin_amdgcn_make_buffer_rsrc((void *)qa, (short)0, R * K, kRsrcWord3);
+        ts.x = __builtin_amdgcn_make_buffer_rsrc((void *)(qx + (int64_t)t * TM * K), (short)0,
+                                                 (M - t * TM) * K, kRsrcWord3);
+        return ts;
+    };
+    float c_x, c_a0, c_a1;
+    auto load_scales = [&](int t) {
+        c_x = sx[min(t * TM + (tid & (TM - 1)), M - 1)];
+        c_a0 = tid < R ? sa[tid] : 0.0f;
+        c_a1 = tid + 256 < R ? sa[tid + 256] : 0.0f;
+    };
+
+    // epilogue scratch in stage S-1 (free from the end of the K loop until the
+    // next tile's first copy into it): token scales, channel scales, row maxima
+    int8_t *scratch = pick<S, S - 1>(sw0, sw1, sw2, sw3);
+    float *s_x = reinterpret_cast<float *>(scratch);
+    float *s_a = s_x + TM;
+    float *red = s_a + 512;
+
+    int t = blockIdx.x;                     // grid <= tiles
+    load_scales(t);
+    TileSrc cur = src_of(t);
+    int tn = t + gridDim.x;
+    bool more = tn < tiles;
+    TileSrc nxt = more ? src_of(tn) : cur;
+
+    for (int it = 0;; ++it) {
+        v16i acc[4][TJ];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+        k_loop<TJ, 8, CX, S, NSCALE>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw,
+                                   voffx, nk, it == 0, wave, frow_w, frow_x, foff0, foff1, acc);
+
+        // every wave is done reading stage S-1 before it becomes scratch
+        wait_lds_reads();
+        block_barrier();
+        if (tid < TM) s_x[tid] = c_x;
+        s_a[tid] = c_a0;
+        s_a[tid + 256] = c_a1;
+        wait_lds_reads();
+        block_barrier();
+        f1_epilogue<BLK, TJ>(acc, s_x, s_a, red, qh, sh, t * TM, M, R, inv_sqrt_b, wave, l32, g);
+        // the codes drained (so the next tile's waits count exactly) and the
+        // scratch read by everyone before the next tile's copies reuse it
+        wait_vmcnt<0>();
+        wait_lds_reads();
+        block_barrier();
+        if (!more) break;
+        t = tn;
+        cur = nxt;
+        load_scales(t);
+        tn = t + gridDim.x;
+        more = tn < tiles;
+        if (more) nxt = src_of(tn);
+    }
+    wait_vmcnt<0>();
+}
+
+template <int BLK, int TJ>
+hipError_t launch_f1_tj(const int8_t *qx, const int8_t *qa, const float *sx, const float *sa,
+                        int8_t *qh, float *sh, int64_t M, int64_t R, int64_t K,
+                        float inv_sqrt_b, int64_t max_grid, hipStream_t stream)
+{
+    const int64_t tiles = (M + 32 * TJ - 1) / (32 * TJ);
+    const dim3 grid((unsigned)std::min<int64_t>(tiles, max_grid)), block(kThreads);
+    if ((K / kBK) % 4 == 0)
+        hipLaunchKernelGGL((lowrank_f1_kernel<BLK, 4, TJ>), grid, block, 0, stream, qx, qa, sx,
+                           sa, qh, sh, (int)M, (int)R, (int)K, inv_sqrt_b);
+    else
+        hipLaunchKernelGGL((lowrank_f1_kernel<BLK, 2, TJ>), grid, block, 0, stream, qx, qa, sx,
+                           sa, qh, sh, (int)M, (int)R, (int)K, inv_sqrt_b);
+    return hipGetLastError();
+}
+
+// 128-token tiles, one per CU at a time.  When the last round of them would
+// keep at most half the CUs busy, its rows go to a second launch of 64-token
+// tiles (at most one per CU), which finishes in about half the time.
+template <int BLK>
+hipError_t launch_f1_blk(const int8_t *qx, const int8_t *qa, const float *sx, const float *sa,
+                         int8_t *qh, float *sh, int64_t M, int64_t R, int64_t K,
+                         float inv_sqrt_b, hipStream_t stream)
+{
+    const int64_t cus = device_cu_count();
+    const int64_t tiles = (M + 127) / 128;
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const int64_t last = tiles - (rounds - 1) * cus;
+    if (2 * last > cus)
+        return launch_f1_tj<BLK, 4>(qx, qa, sx, sa, qh, sh, M, R, K, inv_sqrt_b, cus, stream);
+    const int64_t m1 = (rounds - 1) * cus * 128;   // rows in whole rounds of 128
+    if (m1 > 0) {
+        const hipError_t e =
+            launch_f1_tj<BLK, 4>(qx, qa, sx, sa, qh, sh, m1, R, K, inv_sqrt_b, cus, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_f1_tj<BLK, 2>(qx + m1 * K, qa, sx + m1, sa, qh + m1 * R, sh + m1, M - m1, R, K,
+                                inv_sqrt_b, cus, stream);
+}
+
 // 256 x 256 tiles.  The kernel also builds 256 (n) x 128 (m) tiles (TJ = 2):
 // they fill the last round better when tiles are few (M = 4096, or N = 512),
 // but ran no faster on those shapes and 20% slower on large ones (more LDS
@@ -727,6 +1020,22 @@ hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream
     hipLaunchKernelGGL(gelu_apply_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                        u, g, n);
     return hipGetLastError();
+}
+
+bool lowrank_f1_fusable(int64_t R, int block)
+{
+    return (block == 64 || block == 128) && R % 128 == 0 && R > 0 && R <= 512;
+}
+
+hipError_t launch_lowrank_f1(const int8_t *qx, const int8_t *qa, const float *sx,
+                             const float *sa, int8_t *qh, float *sh, int64_t M, int64_t R,
+                             int64_t K, int block, float inv_sqrt_b, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    if (!lowrank_f1_fusable(R, block)) return hipErrorInvalidValue;
+    return block == 128
+               ? launch_f1_blk<128>(qx, qa, sx, sa, qh, sh, M, R, K, inv_sqrt_b, stream)
+               : launch_f1_blk<64>(qx, qa, sx, sa, qh, sh, M, R, K, inv_sqrt_b, stream);
 }
 
 } // namespace convrot
