@@ -141,7 +141,7 @@ def setup(w, cr, torch, np, dev):
         Y = torch.empty((M, N), dtype=out_dt, device=dev)
         ws = torch.empty(cr.convrot_linear_workspace_bytes(M, K, N, b), dtype=torch.uint8,
                          device=dev)
-        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        qx = torch.empty((cr.padded_rows(M), K), dtype=torch.int8, device=dev)
         sx = torch.empty(M, dtype=torch.float32, device=dev)
 
         def step():
@@ -164,10 +164,10 @@ def setup(w, cr, torch, np, dev):
         Y = torch.empty((M, N), dtype=out_dt, device=dev)
         ws = torch.empty(cr.lowrank_convrot_workspace_bytes(M, K, r, N, b), dtype=torch.uint8,
                          device=dev)
-        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        qx = torch.empty((cr.padded_rows(M), K), dtype=torch.int8, device=dev)
         sx = torch.empty(M, dtype=torch.float32, device=dev)
         H = torch.empty((M, r), dtype=torch.bfloat16, device=dev)
-        qh = torch.empty((M, r), dtype=torch.int8, device=dev)
+        qh = torch.empty((cr.padded_rows(M), r), dtype=torch.int8, device=dev)
         sh = torch.empty(M, dtype=torch.float32, device=dev)
 
         def step():
@@ -208,10 +208,10 @@ def setup(w, cr, torch, np, dev):
         Y = torch.empty((M, N), dtype=out_dt, device=dev)
         ws = torch.empty(cr.convrot_mlp_workspace_bytes(M, K, F, N, b), dtype=torch.uint8,
                          device=dev)
-        qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+        qx = torch.empty((cr.padded_rows(M), K), dtype=torch.int8, device=dev)
         sx = torch.empty(M, dtype=torch.float32, device=dev)
         G = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
-        qg = torch.empty((M, F), dtype=torch.int8, device=dev)
+        qg = torch.empty((cr.padded_rows(M), F), dtype=torch.int8, device=dev)
         sg = torch.empty(M, dtype=torch.float32, device=dev)
 
         def step():

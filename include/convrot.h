@@ -39,14 +39,27 @@
  *     calls on different streams may overlap if they use separate workspaces.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls are asynchronous on that stream; the host never synchronises.
- *   - Matrices are row-major and dense.  bf16 tensors hold raw bfloat16 bits.
- *     Every pointer must be 16-byte aligned.
+ *   - Float matrices (X, Y, weights, intermediates in bf16) are row-major and
+ *     dense; bf16 tensors hold raw bfloat16 bits.  INT8 code matrices (the
+ *     test hooks' q_x and q_h, prepared weight codes) use the K-tiled layout
+ *     below.  Every pointer must be 16-byte aligned.
  *   - Arguments are validated before anything is launched.  A call that
  *     returns an error has launched nothing and written nothing.  Device
  *     faults surface at the caller's next synchronisation.
  *   - Non-finite inputs give unspecified (but memory-safe) results.
- *   - Shape limits: K % 128 == 0, N % 16 == 0, K <= 65536, M*K < 2^31,
- *     N*K < 2^31 (EUNSUPPORTED otherwise).  M == 0 is a no-op returning OK.
+ *   - Shape limits: K % 128 == 0, N % 16 == 0, K <= 65536, Mp*K < 2^31 with
+ *     Mp = M rounded up to a multiple of 16, N*K < 2^31 (EUNSUPPORTED
+ *     otherwise).  M == 0 is a no-op returning OK.
+ *
+ * K-tiled INT8 layout of a code matrix with M rows of K codes (K % 64 == 0):
+ * rows are padded to Mp (a multiple of 16) and the code (m, k) sits at byte
+ *   ((m / 16) * (K / 64) + k / 64) * 1024 + (m % 16) * 64
+ *     + (((k / 16) % 4) XOR ((m / 4) % 4)) * 16 + k % 16,
+ * i.e. each block of 16 rows is K/64 consecutive 1 KiB tiles of 16 rows x 64
+ * codes, with the four 16-byte chunks of a row permuted by its row index.  A
+ * GEMM K-step of 16 rows is then one contiguous 1 KiB read that lands in LDS
+ * in bank-conflict-free order.  The buffer holds Mp * K bytes; the padding
+ * rows are never read into an output.
  */
 #ifndef CONVROT_H
 #define CONVROT_H
@@ -91,17 +104,18 @@ typedef enum convrot_layout {
 } convrot_layout;
 
 #define CONVROT_WEIGHTS_MAGIC 0x38545243u /* "CRT8" little-endian */
-#define CONVROT_WEIGHTS_VERSION 1u
+#define CONVROT_WEIGHTS_VERSION 2u
 
 /* Prepared (pre-rotated, quantised, packed) weights of one linear layer.
  * A host struct holding caller-owned device pointers.  `codes` and `scale`
  * must be allocated by the caller before convrot_linear_prepare_weights
  * (sizes: convrot_weights_packed_bytes(N, K, block) and 4*N bytes); the
- * prepare call fills every other field.  The packed code layout is private to
- * this library and tagged by magic/version: forward calls reject a descriptor
- * whose tag does not match (CONVROT_ELAYOUT), the way a runtime validates a
- * versioned layout marker before building its pipeline (PulpCut input-major
- * README, "Input-major checkpoint"). */
+ * prepare call fills every other field.  The codes are stored K-tiled (N is a
+ * multiple of 16, so there are no padding rows); the layout is tagged by
+ * magic/version: forward calls reject a descriptor whose tag does not match
+ * (CONVROT_ELAYOUT), the way a runtime validates a versioned layout marker
+ * before building its pipeline (PulpCut input-major README, "Input-major
+ * checkpoint"). */
 typedef struct convrot_weights {
     uint32_t magic;            /* CONVROT_WEIGHTS_MAGIC once prepared */
     uint32_t version;          /* CONVROT_WEIGHTS_VERSION */
@@ -109,7 +123,7 @@ typedef struct convrot_weights {
     int64_t K;                 /* input channels */
     int32_t block;             /* Hadamard block b the codes were rotated with */
     int32_t flags;             /* reserved, 0 */
-    int8_t *codes;             /* device, packed INT8 codes of W . R^T */
+    int8_t *codes;             /* device, K-tiled INT8 codes of W . R^T [N, K] */
     float *scale;              /* device, [N] per-output F32 scales */
 } convrot_weights;
 
@@ -133,8 +147,9 @@ CONVROT_API size_t convrot_weights_packed_bytes(int64_t N, int64_t K, int block)
 CONVROT_API size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block,
                                        int w_dtype, int layout);
 
-/* Workspace for convrot_linear_forward: INT8 codes [M, K] and F32 row scales
- * [M] of the rotated activations, each region 256-byte aligned. */
+/* Workspace for convrot_linear_forward: K-tiled INT8 codes (Mp x K bytes) and
+ * F32 row scales [M] of the rotated activations, each region 256-byte
+ * aligned. */
 CONVROT_API size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block);
 
 /* Workspace for lowrank_convrot_forward (codes of X, bf16 intermediate
@@ -165,8 +180,8 @@ CONVROT_API size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, 
  *             (may be NULL when that query returns 0).
  * Float weights: row n of W becomes codes/scale of FWHT_b(W[n, :]) quantised
  * per output channel, i.e. the INT8 image of W . R^T.  Import mode copies the
- * codes (transposing IN_MAJOR input) and scales without changing any value,
- * as the input-major repack does. */
+ * codes (row-major [N, K], or [K, N] for IN_MAJOR) into the K-tiled layout and
+ * the scales without changing any value, as the input-major repack does. */
 CONVROT_API int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
                                    const float *src_scale, int64_t N, int64_t K,
                                    int block, convrot_weights *out, void *ws,
@@ -212,13 +227,15 @@ CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weig
 /* tests.  Same validation and error behaviour as the entry points.    */
 /* ------------------------------------------------------------------ */
 
-/* Rotate and quantise rows: X [M, K] (x_dtype F32 or BF16) -> q [M, K] int8
+/* Rotate and quantise rows: X [M, K] row-major (x_dtype F32 or BF16) -> q
+ * K-tiled int8 codes (Mp x K bytes; the padding rows are left as they were)
  * and s [M] F32.  flags must be 0. */
 CONVROT_API int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K,
                             int block, uint32_t flags, int8_t *q, float *s,
                             void *stream);
 
-/* Exact INT32 contraction acc[M, N] = q_x [M, K] . codes(W)^T. */
+/* Exact INT32 contraction acc[M, N] (row-major) = q_x . codes(W)^T, q_x the
+ * K-tiled codes of M rows (Mp x W->K bytes). */
 CONVROT_API int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W,
                      int32_t *acc, void *stream);
 
@@ -237,9 +254,10 @@ CONVROT_API int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_
  * r = A->N, then (q_h, s_h) = rotate_quantize(h) with block A->block, exactly
  * as lowrank_convrot_forward feeds factor 2 (low-rank ConvRot linears: the
  * MLX model card, "Choose a Weight Format").  h itself is never written.
- * q_x [M, A->K] int8 and s_x [M] F32 come from convrot_rotate_quantize;
- * q_h [M, r] int8 and s_h [M] F32 are written.  All device pointers, 16-byte
- * aligned.  Supported for A->block in {64, 128} and r <= 512
+ * q_x (K-tiled, Mp x A->K bytes) and s_x [M] F32 come from
+ * convrot_rotate_quantize; q_h (K-tiled, Mp x r bytes; its padding rows get
+ * unspecified codes) and s_h [M] F32 are written.  All device pointers,
+ * 16-byte aligned.  Supported for A->block in {64, 128} and r <= 512
  * (CONVROT_EUNSUPPORTED otherwise; lowrank_convrot_forward then runs the
  * two stages separately). */
 CONVROT_API int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int64_t M,

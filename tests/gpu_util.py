@@ -36,6 +36,53 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+# The library's INT8 code matrices are K-tiled: code (m, k) at byte
+#   ((m // 16) * (K // 64) + k // 64) * 1024 + (m % 16) * 64
+#     + (((k // 16) % 4) ^ ((m // 4) % 4)) * 16 + k % 16
+# of a buffer of Mp * K bytes, Mp = M rounded up to 16 (the public header's
+# definition, restated here so the tests check the kernels against it).
+
+def padded_rows(M: int) -> int:
+    return (M + 15) // 16 * 16
+
+
+def tiled_index(M: int, K: int) -> np.ndarray:
+    m = np.arange(M, dtype=np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    return (((m // 16) * (K // 64) + k // 64) * 1024 + (m % 16) * 64
+            + (((k // 16) % 4) ^ ((m // 4) % 4)) * 16 + k % 16)
+
+
+def _chunk_perm():
+    # slot of chunk c in tile row r: c ^ ((r // 4) % 4)
+    return np.array([[c ^ ((r // 4) % 4) for c in range(4)] for r in range(16)])
+
+
+def untile(buf, M: int, K: int) -> np.ndarray:
+    """Row-major [M, K] codes from a K-tiled buffer (device tensor or array).
+    Same map as tiled_index, done on the (block, K-tile, row, slot, byte)
+    view so that full-size matrices need no index array."""
+    if isinstance(buf, torch.Tensor):
+        buf = host(buf)
+    Mp = padded_rows(M)
+    b = np.asarray(buf).reshape(-1)[:Mp * K].reshape(Mp // 16, K // 64, 16, 4, 16)
+    r = np.arange(16)[:, None]
+    rows = b[:, :, r, _chunk_perm(), :]                # [block, ktile, row, chunk, byte]
+    return rows.transpose(0, 2, 1, 3, 4).reshape(Mp, K)[:M]
+
+
+def tile(q: np.ndarray) -> np.ndarray:
+    """The K-tiled buffer (Mp, K) of row-major codes q [M, K]; padding rows 0."""
+    M, K = q.shape
+    Mp = padded_rows(M)
+    full = np.zeros((Mp, K), dtype=np.int8)
+    full[:M] = q
+    rows = full.reshape(Mp // 16, 16, K // 64, 4, 16).transpose(0, 2, 1, 3, 4)
+    out = np.empty_like(rows)                          # [block, ktile, row, slot, byte]
+    out[:, :, np.arange(16)[:, None], _chunk_perm(), :] = rows
+    return out.reshape(Mp, K)
+
+
 def as_f64(y, kind):
     if kind == "bf16":
         return (np.asarray(y, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -9,8 +9,8 @@ import torch
 
 import oracle
 from w8a8_int8_rotated_amd import workloads as wl
-from gpu_util import (announce, assert_output_parity, bf16_bits, host, sample_rows,
-                      to_dev, to_dev_bf16)
+from gpu_util import (announce, assert_output_parity, bf16_bits, host, sample_rows, tile,
+                      to_dev, to_dev_bf16, untile)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,7 @@ def cr():
 def _prep(cr, W, b):
     pw = cr.convrot_linear_prepare_weights(to_dev(W), b)
     q_ref, s_ref = oracle.prepare_weights(W, b)
-    assert np.array_equal(host(pw.codes).reshape(q_ref.shape), q_ref), "weight codes"
+    assert np.array_equal(untile(pw.codes, *q_ref.shape), q_ref), "weight codes"
     assert np.array_equal(host(pw.scale), s_ref), "weight scales"
     return pw, q_ref, s_ref
 
@@ -42,12 +42,12 @@ def test_qkv_38656_fullsize(cr):
     torch.cuda.synchronize()
     qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
     assert np.array_equal(host(sx), sx_ref), "row scales, all rows"
-    assert np.array_equal(host(qx), qx_ref), "codes, all rows"
+    assert np.array_equal(untile(qx, w.M, w.K), qx_ref), "codes, all rows"
     rows = sample_rows(w.M, 64)
     y_ref = oracle.linear_forward(x[rows], qw, sw, w.block, out="bf16")
     yr = bf16_bits(y[torch.from_numpy(rows).cuda()])
     assert assert_output_parity(yr, y_ref, "bf16", "qkv_38656 sampled rows") == 0
-    acc = cr.convrot_gemm_i32(qx[torch.from_numpy(rows[:16]).cuda()].contiguous(), pw)
+    acc = cr.convrot_gemm_i32(to_dev(tile(qx_ref[rows[:16]])), 16, pw)
     assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref[rows[:16]], qw))
 
 
@@ -92,10 +92,10 @@ def test_qk_38656_small_k(cr):
     qx, sx = cr.convrot_rotate_quantize(X, w.block)
     torch.cuda.synchronize()
     qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
-    assert np.array_equal(host(qx), qx_ref) and np.array_equal(host(sx), sx_ref)
+    assert np.array_equal(untile(qx, w.M, w.K), qx_ref) and np.array_equal(host(sx), sx_ref)
     rows = sample_rows(w.M, 48)
     y_ref = oracle.linear_forward(x[rows], qw, sw, w.block, out="bf16")
     yr = bf16_bits(y[torch.from_numpy(rows).cuda()])
     assert assert_output_parity(yr, y_ref, "bf16", "qk_38656 sampled rows") == 0
-    acc = cr.convrot_gemm_i32(qx[torch.from_numpy(rows[:8]).cuda()].contiguous(), pw)
+    acc = cr.convrot_gemm_i32(to_dev(tile(qx_ref[rows[:8]])), 8, pw)
     assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref[rows[:8]], qw))

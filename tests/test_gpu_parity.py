@@ -7,8 +7,8 @@ import torch
 
 import oracle
 from w8a8_int8_rotated_amd import workloads as wl
-from gpu_util import (announce, assert_output_parity, bf16_bits, host, sample_rows,
-                      to_dev, to_dev_bf16)
+from gpu_util import (announce, assert_output_parity, bf16_bits, host, sample_rows, tile,
+                      to_dev, to_dev_bf16, untile)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def test_rotquant_codes_bitexact(cr, b, M, K):
     q, s = cr.convrot_rotate_quantize(to_dev_bf16(x), b)
     torch.cuda.synchronize()
     q_ref, s_ref = oracle.rotate_quantize(x, b, "bf16")
-    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(untile(q, M, K), q_ref)
     assert np.array_equal(host(s), s_ref)
 
 
@@ -52,9 +52,10 @@ def test_rotquant_f32_rows_bitexact(cr, b):
     W[9, 100] = 5.0                              # lone spike
     q, s = cr.convrot_rotate_quantize(to_dev(W), b)
     q_ref, s_ref = oracle.rotate_quantize(W, b, "f32")
-    assert np.array_equal(host(q), q_ref)
+    qh = untile(q, *W.shape)
+    assert np.array_equal(qh, q_ref)
     assert np.array_equal(host(s), s_ref)
-    assert not host(q)[7].any() and host(s)[7] == 0
+    assert not qh[7].any() and host(s)[7] == 0
 
 
 def test_rotquant_special_rows(cr):
@@ -71,7 +72,7 @@ def test_rotquant_special_rows(cr):
     xb = wl.f32_to_bf16_bits(x)
     q, s = cr.convrot_rotate_quantize(to_dev_bf16(xb), 128)
     q_ref, s_ref = oracle.rotate_quantize(xb, 128, "bf16")
-    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(untile(q, 6, K), q_ref)
     assert np.array_equal(host(s), s_ref)
 
 
@@ -90,7 +91,7 @@ def test_prepare_weights_bitexact(cr, dtype, layout):
     t = to_dev(src) if dtype == "f32" else to_dev_bf16(src)
     pw = cr.convrot_linear_prepare_weights(t, b, cr.IN_MAJOR if layout == "in_major" else cr.OUT_MAJOR)
     q_ref, s_ref = oracle.prepare_weights(src, b, dtype=dtype, layout=layout)
-    assert np.array_equal(host(pw.codes).reshape(N, K), q_ref)
+    assert np.array_equal(untile(pw.codes, N, K), q_ref)
     assert np.array_equal(host(pw.scale), s_ref)
 
 
@@ -106,7 +107,7 @@ def test_prepare_import_int8_unchanged(cr, layout):
     pw = cr.convrot_linear_prepare_weights(
         to_dev(src), 128, cr.IN_MAJOR if layout == "in_major" else cr.OUT_MAJOR,
         src_scale=to_dev(s))
-    assert np.array_equal(host(pw.codes).reshape(N, K), q)
+    assert np.array_equal(untile(pw.codes, N, K), q)
     assert np.array_equal(host(pw.scale), s)
 
 
@@ -125,7 +126,7 @@ def test_gemm_i32_bitexact(cr, M, N, K):
     qw[0] = -127                                 # extreme accumulator
     pw = cr.convrot_linear_prepare_weights(to_dev(qw), 128, src_scale=to_dev(
         np.ones(N, np.float32)))
-    acc = cr.convrot_gemm_i32(to_dev(qx), pw)
+    acc = cr.convrot_gemm_i32(to_dev(tile(qx)), M, pw)
     ref = oracle.gemm_i32(qx, qw)
     assert np.array_equal(host(acc), ref)
 
@@ -135,7 +136,7 @@ def test_gemm_i32_bitexact(cr, M, N, K):
 def _prepare_pair(cr, W, b):
     pw = cr.convrot_linear_prepare_weights(to_dev(W), b)
     q_ref, s_ref = oracle.prepare_weights(W, b)
-    assert np.array_equal(host(pw.codes).reshape(q_ref.shape), q_ref)
+    assert np.array_equal(untile(pw.codes, *q_ref.shape), q_ref)
     assert np.array_equal(host(pw.scale), s_ref)
     return pw, q_ref, s_ref
 
@@ -150,9 +151,9 @@ def test_linear_tiny_config(cr):
     X = to_dev_bf16(x)
     y = cr.convrot_linear_forward(X, pw, out_dtype=torch.float32)
     qx, sx = cr.convrot_rotate_quantize(X, w.block)
-    acc = cr.convrot_gemm_i32(qx, pw)
+    acc = cr.convrot_gemm_i32(qx, w.M, pw)
     qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
-    assert np.array_equal(host(qx), qx_ref) and np.array_equal(host(sx), sx_ref)
+    assert np.array_equal(untile(qx, w.M, w.K), qx_ref) and np.array_equal(host(sx), sx_ref)
     assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref, qw))
     y_ref = oracle.linear_forward(x, qw, sw, w.block, out="f32")
     mism = assert_output_parity(host(y), y_ref, "f32", "tiny fp32")
@@ -190,12 +191,12 @@ def test_linear_4096_config_sampled(cr):
     y = cr.convrot_linear_forward(X, pw, bias=to_dev(bias))
     qx, sx = cr.convrot_rotate_quantize(X, w.block)
     qx_ref, sx_ref = oracle.rotate_quantize(x, w.block, "bf16")
-    assert np.array_equal(host(qx), qx_ref) and np.array_equal(host(sx), sx_ref)
+    assert np.array_equal(untile(qx, w.M, w.K), qx_ref) and np.array_equal(host(sx), sx_ref)
     rows = sample_rows(w.M, 96)
     y_ref = oracle.linear_forward(x[rows], qw, sw, w.block, bias=bias, out="bf16")
     mism = assert_output_parity(bf16_bits(y)[rows], y_ref, "bf16", "linear_4096 sampled")
     assert mism == 0
-    acc = cr.convrot_gemm_i32(qx, pw)
+    acc = cr.convrot_gemm_i32(qx, w.M, pw)
     assert np.array_equal(host(acc)[rows], oracle.gemm_i32(qx_ref[rows], qw))
 
 
@@ -288,10 +289,10 @@ def _check_factor1(cr, M, K, r, block):
     x, A = w.activations(), w.weight("w")
     pa, qa, sa = _prepare_pair(cr, A, block)
     qx, sx = oracle.rotate_quantize(x, block, "bf16")
-    q_h, s_h = cr.convrot_lowrank_factor1(to_dev(qx), to_dev(sx), pa)
+    q_h, s_h = cr.convrot_lowrank_factor1(to_dev(tile(qx)), to_dev(sx), pa)
     h = oracle.dequant(oracle.gemm_i32(qx, qa), sx, sa, out="bf16")
     qh_ref, sh_ref = oracle.rotate_quantize(h, block, "bf16")
-    qh, sh = host(q_h), host(s_h)
+    qh, sh = untile(q_h, M, r), host(s_h)
     print(f"[parity] factor1: {int((qh != qh_ref).sum())} codes and "
           f"{int((sh.view(np.uint32) != sh_ref.view(np.uint32)).sum())} scales differ",
           flush=True)

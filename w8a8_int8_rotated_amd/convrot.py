@@ -19,7 +19,7 @@ OK, EINVAL, EALIGN, EWORKSPACE, ELAYOUT, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4,
 F32, BF16, I8, I32 = 0, 1, 2, 3
 OUT_MAJOR, IN_MAJOR = 0, 1
 WEIGHTS_MAGIC = 0x38545243
-WEIGHTS_VERSION = 1
+WEIGHTS_VERSION = 2
 FLAG_GELU = 1
 
 _c_i64 = ctypes.c_int64
@@ -265,11 +265,27 @@ def convrot_mlp_forward(X: torch.Tensor, W_up: PreparedWeights, W_down: Prepared
 
 # ------------------------------------------------------------- hooks ----
 
+def padded_rows(M: int) -> int:
+    """Rows of a K-tiled INT8 code buffer holding M rows (a multiple of 16)."""
+    return (M + 15) // 16 * 16
+
+
+def _codes(q, M: int, K: int, device):
+    """A K-tiled code buffer for M rows of K codes: allocated as (Mp, K) int8,
+    or a caller tensor checked to hold Mp * K bytes."""
+    Mp = padded_rows(M)
+    if q is None:
+        return torch.empty((Mp, K), dtype=torch.int8, device=device)
+    if q.dtype != torch.int8 or not q.is_contiguous() or q.numel() < Mp * K:
+        raise ValueError(f"K-tiled codes need a contiguous int8 tensor of {Mp * K} elements")
+    return q
+
+
 def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=None):
+    """Rotate + quantise the rows of X: (q, s), q the K-tiled codes (Mp, K)."""
     lib = library()
     M, K = X.shape
-    if q is None:
-        q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    q = _codes(q, M, K, X.device)
     if s is None:
         s = torch.empty(M, dtype=torch.float32, device=X.device)
     rc = lib.convrot_rotate_quantize(_ptr(X), _dtype_tag(X.dtype), M, K, block, 0, _ptr(q),
@@ -278,9 +294,10 @@ def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=
     return q, s
 
 
-def convrot_gemm_i32(q_x: torch.Tensor, W: PreparedWeights, out=None, stream=None):
+def convrot_gemm_i32(q_x: torch.Tensor, M: int, W: PreparedWeights, out=None, stream=None):
+    """acc [M, N] int32 from K-tiled codes q_x of M rows."""
     lib = library()
-    M = q_x.shape[0]
+    _codes(q_x, M, W.K, None)
     if out is None:
         out = torch.empty((M, W.N), dtype=torch.int32, device=q_x.device)
     rc = lib.convrot_gemm_i32(_ptr(q_x), M, W.ref(), _ptr(out), _stream(stream))
@@ -291,8 +308,10 @@ def convrot_gemm_i32(q_x: torch.Tensor, W: PreparedWeights, out=None, stream=Non
 def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeights, bias=None,
                          out_dtype: torch.dtype = torch.bfloat16, out=None, gelu: bool = False,
                          stream=None):
+    """Y [M, N] from K-tiled codes q_x and row scales s_x [M]."""
     lib = library()
-    M = q_x.shape[0]
+    M = s_x.shape[0]
+    _codes(q_x, M, W.K, None)
     if out is None:
         out = torch.empty((M, W.N), dtype=out_dtype, device=q_x.device)
     rc = lib.convrot_gemm_dequant(_ptr(q_x), _ptr(s_x), M, W.ref(), _ptr(bias), _ptr(out),
@@ -305,11 +324,11 @@ def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeight
 def convrot_lowrank_factor1(q_x: torch.Tensor, s_x: torch.Tensor, A: PreparedWeights,
                             q_h=None, s_h=None, stream=None):
     """Factor 1 of the low-rank chain with its output rotated and requantised:
-    returns (q_h [M, r] int8, s_h [M] f32)."""
+    returns (q_h, s_h), q_h the K-tiled codes (Mp, r), s_h [M] f32."""
     lib = library()
-    M = q_x.shape[0]
-    if q_h is None:
-        q_h = torch.empty((M, A.N), dtype=torch.int8, device=q_x.device)
+    M = s_x.shape[0]
+    _codes(q_x, M, A.K, None)
+    q_h = _codes(q_h, M, A.N, q_x.device)
     if s_h is None:
         s_h = torch.empty(M, dtype=torch.float32, device=q_x.device)
     rc = lib.convrot_lowrank_factor1(_ptr(q_x), _ptr(s_x), M, A.ref(), _ptr(q_h), _ptr(s_h),

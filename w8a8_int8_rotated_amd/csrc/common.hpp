@@ -34,6 +34,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 namespace convrot {
 
+// ------------------------------------------------ INT8 code layout ----
+// Every INT8 code matrix of the library (activation codes, weight codes, the
+// low-rank intermediate) is stored K-tiled: rows in blocks of 16, a block as
+// K/64 consecutive 1 KiB tiles of 16 rows x 64 bytes, and inside a tile the
+// 16-byte chunk c of row r at slot c ^ ((r >> 2) & 3).  The GEMM's copy of one
+// 16-row K-tile is then a single contiguous 1 KiB read (8 whole cache lines
+// instead of 16 half lines, twice the copy rate on gfx950), and it lands in
+// LDS already in the order whose fragment reads are free of bank conflicts.
+// Rows are padded to a multiple of 16; the block of rows m0 .. m0+15 starts
+// at byte m0 * K as in row-major order.  Requires K % 64 == 0.
+__host__ __device__ inline int64_t tiled_offset(int64_t m, int64_t k, int64_t K)
+{
+    return ((m >> 4) * (K >> 6) + (k >> 6)) * 1024 + (m & 15) * 64 +
+           ((((k >> 4) & 3) ^ ((m >> 2) & 3)) << 4) + (k & 15);
+}
+__host__ __device__ inline int64_t padded_rows(int64_t M) { return (M + 15) & ~int64_t(15); }
+
 enum class InType { F32 = 0, BF16 = 1 };
 
 // Compute units of the current device (queried once; 256 if the query fails).
@@ -41,7 +58,8 @@ int device_cu_count();
 enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3 };
 
 // Rotate (blockwise FWHT) + rowwise INT8 quantise.  src rows have stride ld
-// elements; q rows have stride K bytes.
+// elements; q is K-tiled with padded_rows(M) rows (the padding rows are not
+// written).
 hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
                            int64_t ld, int block, float inv_sqrt_b, int8_t *q,
                            float *s, hipStream_t stream);
@@ -57,11 +75,16 @@ hipError_t launch_lowrank_f1(const int8_t *qx, const int8_t *qa, const float *sx
 // g[i] = bf16(GELU(u[i])) for bf16 u, as the MLP's up projection applies it.
 hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream);
 
+// INT8 codes [R, C] into the K-tiled layout (R % 16 == 0, C % 64 == 0); the
+// source is row-major [R, C] (ld = C) or, with transposed, [C, R].
+hipError_t launch_tile_codes(const int8_t *src, bool transposed, int8_t *dst, int64_t R,
+                             int64_t C, hipStream_t stream);
+
 // Transpose an [R, C] matrix of 1-, 2- or 4-byte elements into [C, R].
 hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream);
 
-// acc/Y[M, N] = epilogue(qx[M, K] . qw[N, K]^T).
+// acc/Y[M, N] = epilogue(qx[M, K] . qw[N, K]^T), both code matrices K-tiled.
 hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
                           const float *sw, const float *bias, void *Y,
                           OutKind out, int64_t M, int64_t N, int64_t K,

@@ -83,10 +83,12 @@ int check_weights(const convrot_weights *W)
     return rc == CONVROT_EINVAL ? CONVROT_ELAYOUT : rc;
 }
 
+// M rows of K: the K-tiled codes hold padded_rows(M) rows, and every byte
+// offset the kernels form must fit in 32 bits.
 int check_rows(int64_t M, int64_t K)
 {
     if (M < 0) return CONVROT_EINVAL;
-    if (M * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    if (convrot::padded_rows(M) * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
     return CONVROT_OK;
 }
 
@@ -113,7 +115,10 @@ struct Carve {
     }
 };
 
-size_t codes_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)K, kAlign); }
+size_t codes_bytes(int64_t M, int64_t K)
+{
+    return round_up((size_t)convrot::padded_rows(M) * (size_t)K, kAlign);
+}
 size_t scales_bytes(int64_t M) { return round_up((size_t)M * 4u, kAlign); }
 
 } // namespace
@@ -199,10 +204,8 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (import) {
-        if (layout == CONVROT_OUT_MAJOR)
-            e = hipMemcpyAsync(out->codes, W, (size_t)N * (size_t)K, hipMemcpyDeviceToDevice, s);
-        else
-            e = convrot::launch_transpose(W, out->codes, K, N, 1, s);
+        e = convrot::launch_tile_codes(static_cast<const int8_t *>(W),
+                                       layout == CONVROT_IN_MAJOR, out->codes, N, K, s);
         if (e == hipSuccess)
             e = hipMemcpyAsync(out->scale, src_scale, (size_t)N * 4u, hipMemcpyDeviceToDevice, s);
     } else {
@@ -243,8 +246,10 @@ int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
     const size_t need = convrot_linear_workspace_bytes(M, W->K, W->N, W->block);
     if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
 
+    // code regions are K-tiled with padded rows: the last 16-row block spans
+    // padded_rows(M) * K bytes, not M * K
     Carve c(ws);
-    int8_t *qx = static_cast<int8_t *>(c.take((size_t)M * (size_t)W->K));
+    int8_t *qx = static_cast<int8_t *>(c.take(codes_bytes(M, W->K)));
     float *sx = static_cast<float *>(c.take((size_t)M * 4u));
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W->K, W->K, W->block,
@@ -275,10 +280,10 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
     if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
 
     Carve c(ws);
-    int8_t *qx = static_cast<int8_t *>(c.take((size_t)M * (size_t)A->K));
+    int8_t *qx = static_cast<int8_t *>(c.take(codes_bytes(M, A->K)));
     float *sx = static_cast<float *>(c.take((size_t)M * 4u));
     void *h = c.take((size_t)M * (size_t)r * 2u);
-    int8_t *qh = static_cast<int8_t *>(c.take((size_t)M * (size_t)r));
+    int8_t *qh = static_cast<int8_t *>(c.take(codes_bytes(M, r)));
     float *sh = static_cast<float *>(c.take((size_t)M * 4u));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float isb = inv_sqrt_block(A->block);
@@ -326,10 +331,10 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
     if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
 
     Carve c(ws);
-    int8_t *qx = static_cast<int8_t *>(c.take((size_t)M * (size_t)W_up->K));
+    int8_t *qx = static_cast<int8_t *>(c.take(codes_bytes(M, W_up->K)));
     float *sx = static_cast<float *>(c.take((size_t)M * 4u));
     void *g = c.take((size_t)M * (size_t)F * 2u);
-    int8_t *qg = static_cast<int8_t *>(c.take((size_t)M * (size_t)F));
+    int8_t *qg = static_cast<int8_t *>(c.take(codes_bytes(M, F)));
     float *sg = static_cast<float *>(c.take((size_t)M * 4u));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float isb = inv_sqrt_block(W_up->block);
@@ -353,7 +358,7 @@ int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, in
     if (M < 0 || K <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
     if (flags != 0) return CONVROT_EUNSUPPORTED;
     if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
-    if (K > kMaxK || M * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    if (K > kMaxK || convrot::padded_rows(M) * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!X || !q || !s_out) return CONVROT_EINVAL;
     if (!aligned16(X) || !aligned16(q) || !aligned16(s_out)) return CONVROT_EALIGN;

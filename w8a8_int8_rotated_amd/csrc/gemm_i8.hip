@@ -7,8 +7,10 @@
 // are per token (s_x) and per output channel (s_w; PulpCut input-major README,
 // "Input-major checkpoint").
 //
-// Operands: qx [M, K] and qw [N, K], both row-major with K contiguous, so each
-// MFMA lane reads 16 consecutive bytes of one row for either operand.
+// Operands: qx [M, K] and qw [N, K], both in the library's K-tiled code
+// layout (blocks of 16 rows stored as 1 KiB tiles of 16 rows x 64 B, chunk c
+// of row r at slot c ^ ((r >> 2) & 3)), so each MFMA lane reads 16
+// consecutive bytes of one row for either operand.
 //
 // Tiling: a 256-thread workgroup (4 waves, one per SIMD) owns a 256 (n) x 256
 // (m) output tile; wave (wn, wm) owns 128 x 128 of it as 4 x 4 tiles of
@@ -26,17 +28,20 @@
 // tiles, 256 rows x 64 B each) live in LDS.  Global -> LDS copies use the
 // direct-to-LDS buffer load (buffer_load_dwordx4 ... lds: each lane fetches
 // 16 bytes and the wave's 1 KiB lands contiguously in LDS), so no registers
-// stage the tiles and no LDS write instructions are issued.  The copies of
+// stage the tiles and no LDS write instructions are issued.  In the K-tiled
+// layout one copy instruction moves one 16-row tile, a contiguous 1 KiB.  The copies of
 // each K-tile are split over the two halves of a step and spread between the
 // MFMAs, which keeps the texture-address queue from filling.  Every wait on a
 // copy is explicit: s_waitcnt vmcnt(n) for this wave's copies, then a barrier
 // for the other waves'.
 //
 // LDS rows are 64 bytes; chunk c (16 B) of tile row r sits at slot
-// c ^ f(r), f(r) = ((r >> 1) ^ (r >> 3)) & 3.  A copy instruction writes 16
-// consecutive rows, so lane i fetches chunk (i & 3) ^ f(row) of its row; the
-// column-wise MFMA fragment reads (32 rows, one chunk) then hit distinct banks
-// for 32- and 64-bank LDS alike.
+// c ^ f(r), f(r) = (r >> 2) & 3, as in the global layout.  The fragment
+// reads (ds_read_b128 of 32 rows x one chunk per half-wave) then run without
+// bank conflicts on gfx950: measured with SQ_LDS_BANK_CONFLICT, they take the
+// 4 cycles of a linear read, where f(r) = ((r >> 1) ^ (r >> 3)) & 3 took 8
+// and no swizzle 16.  Copies of 16 half cache lines per instruction (row-major
+// operands) moved half as many bytes per cycle as the contiguous 1 KiB tiles.
 //
 // Workgroups are renumbered so each of the 8 XCDs walks a contiguous range of
 // tiles, grouped 4 tile-rows high, for L2 reuse of both operands (4 rows
@@ -61,7 +66,7 @@ constexpr int kRsrcWord3 = 0x00020000;
 // rint(t) for |t| < 2^22 lands in the low bits of t + 1.5 * 2^23
 constexpr float kMagicRint = 12582912.0f;
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding).
 template <int N>
@@ -351,21 +356,22 @@ __device__ __forceinline__ TileSrc tile_src(const int8_t *qw, const int8_t *qx, 
     TileSrc t;
     t.w = __builtin_amdgcn_make_buffer_rsrc((void *)(qw + (int64_t)n0 * K), (short)0,
                                             (N - n0) * K, kRsrcWord3);
+    // rows up to the 16-row padding: the last block's tiles hold real rows
+    // throughout its K range
     t.x = __builtin_amdgcn_make_buffer_rsrc((void *)(qx + (int64_t)m0 * K), (short)0,
-                                            (M - m0) * K, kRsrcWord3);
+                                            (int)(padded_rows(M) - m0) * K, kRsrcWord3);
     return t;
 }
 
 // Copy j of wave w moves rows [(n w + j) 16, +16) of an operand tile of 64 n
-// rows (n = 4 for the 256-row weight tile, TJ for the activation tile).
+// rows (n = 4 for the 256-row weight tile, TJ for the activation tile): the
+// 1 KiB tile of that row block, lane i its i-th 16 bytes.
 template <int NC>
 __device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t (&voff)[NC])
 {
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-        const int r = (wave * NC + j) * 16 + (lane >> 2);
-        voff[j] = (uint32_t)r * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
-    }
+    for (int j = 0; j < NC; ++j)
+        voff[j] = (uint32_t)((wave * NC + j) * 16) * (uint32_t)K + (uint32_t)lane * 16u;
 }
 
 // Half H of K-tile `k` of the copy stream into one stage: the wave's weight
@@ -382,7 +388,7 @@ __device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nx
 {
     const bool next = k >= nk;
     const __amdgpu_buffer_rsrc_t rw = next ? nxt.w : cur.w, rx = next ? nxt.x : cur.x;
-    const int soff = (next ? k - nk : k) * kBK;
+    const int soff = (next ? k - nk : k) * 1024;   // K-tile k of a row block
 #pragma unroll
     for (int j = H * CW / 2; j < (H + 1) * CW / 2; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -805,9 +811,11 @@ __device__ __forceinline__ void f1_epilogue(v16i (&acc)[4][TJ], const float *s_x
     wait_lds_reads();
     block_barrier();
 
-    // pass 2: the row amax over the four waves, codes and scales
+    // pass 2: the row amax over the four waves, codes and scales.  The codes
+    // go out K-tiled (m0 is a multiple of 16); rows between M and the 16-row
+    // padding get codes too, which no reader uses.
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(qh + (int64_t)m0 * R), (short)0, (M - m0) * R, kRsrcWord3);
+        (void *)(qh + (int64_t)m0 * R), (short)0, (int)(padded_rows(M) - m0) * R, kRsrcWord3);
     const bool active = wave * 128 < R;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -832,7 +840,7 @@ __device__ __forceinline__ void f1_epilogue(v16i (&acc)[4][TJ], const float *s_x
                 const uint32_t w23 = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
                 __builtin_amdgcn_raw_buffer_store_b32(
                     (int)__builtin_amdgcn_perm(w23, w01, 0x05040100u), qr,
-                    row * R + wave * 128 + 32 * i + 8 * q + 4 * g, 0, 0);
+                    (int)tiled_offset(row, wave * 128 + 32 * i + 8 * q + 4 * g, R), 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -872,7 +880,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowrank_f1_kernel(
         TileSrc ts;
         ts.w = __builtin_amdgcn_make_buffer_rsrc((void *)qa, (short)0, R * K, kRsrcWord3);
         ts.x = __builtin_amdgcn_make_buffer_rsrc((void *)(qx + (int64_t)t * TM * K), (short)0,
-                                                 (M - t * TM) * K, kRsrcWord3);
+                                                 (int)(padded_rows(M) - t * TM) * K, kRsrcWord3);
         return ts;
     };
     float c_x, c_a0, c_a1;

@@ -43,6 +43,7 @@ namespace convrot {
 namespace {
 
 constexpr int kStep = 512;      // elements per wave step
+constexpr int kTiledStep = 16 * kStep;   // bytes a step spans in a K-tiled row block
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
 __device__ __forceinline__ int chunk_of_lane(int i)
@@ -204,14 +205,18 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
     // steps of this wave: part, part + WPR, ... below `steps`
     const int my_steps = (steps - part + WPR - 1) / WPR;
 
-    __amdgpu_buffer_rsrc_t src_row[RPW], q_row[RPW];
+    // codes: the row's 16-row block of the K-tiled layout as the range (so
+    // elements past K fall outside it) and this lane's offset in the block
+    __amdgpu_buffer_rsrc_t src_row[RPW], q_blk[RPW];
+    int q_off[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         const int64_t row = row0 + r;
         const bool in = row < M;
         src_row[r] = row_rsrc(reinterpret_cast<const char *>(src) + (in ? row : 0) * ld * ESIZE,
                               in ? K * ESIZE : 0);
-        q_row[r] = row_rsrc(q + (in ? row : 0) * (int64_t)K, in ? K : 0);
+        q_blk[r] = row_rsrc(q + (in ? (row & ~int64_t(15)) : 0) * (int64_t)K, in ? 16 * K : 0);
+        q_off[r] = (int)tiled_offset(row & 15, lane_off, K);
     }
 
     float v[RPW][SPR][8];
@@ -271,9 +276,9 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
         for (int t = 0; t < SPR; ++t) {
             if (t < my_steps) {
                 const uint2 c = quantise_chunk(v[r][t], invs);
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    (v2i){(int)c.x, (int)c.y}, q_row[r], (part + WPR * t) * kStep + lane_off,
-                    0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)c.x, (int)c.y}, q_blk[r],
+                                                      (part + WPR * t) * kTiledStep + q_off[r],
+                                                      0, 0);
             }
         }
     }
@@ -411,12 +416,14 @@ __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
         __builtin_amdgcn_raw_buffer_store_b32(
             __float_as_int(__fmul_rn(__fdiv_rn(mx, 127.0f), inv_sqrt_b)), srs,
             (part == 0 && lane == 0 && in) ? (int)(row * 4) : 0x7ffffff0, 0, 0);
-        const __amdgpu_buffer_rsrc_t qr = row_rsrc(q + (in ? row : 0) * (int64_t)K, in ? K : 0);
+        const __amdgpu_buffer_rsrc_t qb =
+            row_rsrc(q + (in ? (row & ~int64_t(15)) : 0) * (int64_t)K, in ? 16 * K : 0);
+        const int q_off = (int)tiled_offset(row & 15, lane_off, K);
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
             const uint2 c = quantise_chunk(v[t], invs);
-            __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)c.x, (int)c.y}, qr,
-                                                  (part + WPR * t) * kStep + lane_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)c.x, (int)c.y}, qb,
+                                                  (part + WPR * t) * kTiledStep + q_off, 0, 0);
         }
     }
 }
@@ -464,6 +471,36 @@ hipError_t launch_in(const void *src, int64_t M, int64_t K, int64_t ld, int bloc
     }
 }
 
+// ---------------------------------------------------------- tile codes ----
+
+// One thread per 16-byte chunk of the K-tiled output: row n, columns
+// 16 c .. 16 c + 15, gathered from row-major [R, C] or transposed [C, R] codes.
+__global__ __launch_bounds__(256) void tile_codes_kernel(const int8_t *__restrict__ src,
+                                                         bool transposed,
+                                                         int8_t *__restrict__ dst, int64_t R,
+                                                         int64_t C)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t chunks = C / 16;
+    if (i >= R * chunks) return;
+    const int64_t n = i / chunks, k = (i % chunks) * 16;
+    uint32_t w[4];
+    if (!transposed) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(src + n * C + k);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t x = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                x |= (uint32_t)(uint8_t)src[(k + 4 * j + b) * R + n] << (8 * b);
+            w[j] = x;
+        }
+    }
+    *reinterpret_cast<uint4 *>(dst + tiled_offset(n, k, C)) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ------------------------------------------------------------ transpose ----
 
 template <typename T>
@@ -497,6 +534,16 @@ hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
     if (in == InType::BF16)
         return launch_in<int(InType::BF16)>(src, M, K, ld, block, inv_sqrt_b, q, s, stream);
     return launch_in<int(InType::F32)>(src, M, K, ld, block, inv_sqrt_b, q, s, stream);
+}
+
+hipError_t launch_tile_codes(const int8_t *src, bool transposed, int8_t *dst, int64_t R,
+                             int64_t C, hipStream_t stream)
+{
+    const int64_t n = R * (C / 16);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       stream, src, transposed, dst, R, C);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
