@@ -455,11 +455,15 @@ __device__ __forceinline__ void wait_vmcnt_either(bool second)
 //
 // On entry: first == true -> nothing is in flight and every stage is free;
 // first == false -> K-tiles 0 .. S-2 of this tile are in flight, issued during
-// the previous tile, followed by EPI younger memory operations per wave (the
-// previous tile's stores and this tile's scale loads); stage S-1 is free.
+// the previous tile, then (EARLY) K-tile S-1, issued by the caller once
+// stage S-1 was free, then EPI younger memory operations per wave (the
+// previous tile's stores and this tile's scale loads).  Without EARLY, stage
+// S-1 is free and K-tile S-1 is issued here, after the EPI operations.
+// Issuing it ahead of the stores gives them one more K-step to complete
+// before a wait (vmcnt retires in order) has to cover them.
 // On exit: K-tiles 0 .. S-2 of the next tile are in flight.  Requires
 // nk % S == 0.
-template <int TJ, int CW, int CX, int S, int EPI>
+template <int TJ, int CW, int CX, int S, int EPI, bool EARLY>
 __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
                                        int8_t *__restrict__ w2, int8_t *__restrict__ w3,
                                        int8_t *__restrict__ x0, int8_t *__restrict__ x1,
@@ -475,7 +479,7 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
     constexpr int C = CW + CX;               // copy instructions per wave per K-tile
     constexpr int CH0 = CW / 2 + (CX + 1) / 2, CH1 = C - CH0;   // ... in each half
     constexpr int MF = 4 * TJ, RD = 4 + TJ;  // MFMAs and LDS reads per half
-    static_assert((S - 2) * C + CH0 + EPI < 64, "vmcnt range");
+    static_assert((S - 1) * C + EPI < 64, "vmcnt range");
     v4i a0[4], b0[TJ], a1[4], b1[TJ];
     int8_t *const wl = pick<S, S - 1>(w0, w1, w2, w3), *const xl = pick<S, S - 1>(x0, x1, x2, x3);
 
@@ -489,8 +493,16 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
             issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
         }
     }
-    issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
-    wait_vmcnt_either<(S - 2) * C + CH0 + EPI, (S - 2) * C + CH0>(first);
+    if constexpr (EARLY) {
+        if (first) {
+            issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+        }
+        wait_vmcnt_either<(S - 1) * C + EPI, (S - 1) * C>(first);
+    } else {
+        issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+        wait_vmcnt_either<(S - 2) * C + CH0 + EPI, (S - 2) * C + CH0>(first);
+    }
     block_barrier();
     read_frags(w0, x0, frow_w, frow_x, foff0, a0, b0);
 
@@ -502,12 +514,14 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         wait_lds_reads();                                                                \
         __builtin_amdgcn_sched_barrier(0);                                               \
         read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
-        issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_);             \
+        if (!EARLY || (I) != 0 || kt != 0)                                               \
+            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_); \
         mfma_block(acc, a0, b0);                                                         \
         interleave<MF, CH1, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         wait_lds_reads();                                                                \
-        wait_vmcnt_either<(S - 2) * C, (S - 2) * C + EPI>(!first && kt + (I) < S - 2);   \
+        wait_vmcnt_either<(S - 2) * C, (S - 2) * C + EPI>(                               \
+            !first && kt + (I) < (EARLY ? S - 1 : S - 2));                               \
         block_barrier();                                                                 \
         read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
         issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, kt + (I) + S, nk, wave, cw_, cx_);                 \
@@ -631,8 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-        k_loop<TJ, 4, TJ, S, EPI>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw, voffx, nk,
-                           it == 0, wave, frow_w, frow_x, foff0, foff1, acc);
+        k_loop<TJ, 4, TJ, S, EPI, true>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw,
+                                        voffx, nk, it == 0, wave, frow_w, frow_x, foff0, foff1,
+                                        acc);
 
         if constexpr (OUT != int(OutKind::I32)) {
             sscale[0][tid] = sc_x;
@@ -643,6 +658,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         // copies already in flight
         wait_lds_reads();
         block_barrier();
+        // stage S-1 is read by no one now: the next tile's K-tile S-1 goes
+        // out ahead of this tile's stores (the last tile re-reads its own,
+        // which no one consumes)
+        {
+            int8_t *const wl = pick<S, S - 1>(sw0, sw1, sw2, sw3);
+            int8_t *const xl = pick<S, S - 1>(sx0, sx1, sx2, sx3);
+            issue_half<4, TJ, 0>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
+            issue_half<4, TJ, 1>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
+        }
         const bool full = m0 + TM <= M && n0 + kTile <= N;
         if (full)
             epilogue<OUT, HAS_BIAS, TJ, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
@@ -913,7 +937,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowrank_f1_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-        k_loop<TJ, 8, CX, S, NSCALE>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw,
+        k_loop<TJ, 8, CX, S, NSCALE, false>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw,
                                    voffx, nk, it == 0, wave, frow_w, frow_x, foff0, foff1, acc);
 
         // every wave is done reading stage S-1 before it becomes scratch
