@@ -1005,10 +1005,17 @@ hipError_t launch_f1_blk(const int8_t *qx, const int8_t *qa, const float *sx, co
                                 inv_sqrt_b, cus, stream);
 }
 
-// 256 x 256 tiles.  The kernel also builds 256 (n) x 128 (m) tiles (TJ = 2):
-// they fill the last round better when tiles are few (M = 4096, or N = 512),
-// but ran no faster on those shapes and 20% slower on large ones (more LDS
-// reads and copies per MFMA), so only TJ = 4 is launched.
+// 256 x 256 tiles, one per CU at a time.  When the last round of them would
+// leave CUs idle, the last tile-rows can go to a second launch of 256 (n) x
+// 128 (m) tiles (TJ = 2), which take about 0.6 of a 256 x 256 tile each (they
+// move more bytes per MFMA, so a whole launch of them runs at 0.8 of the
+// rate).  The split is chosen from that estimate when K >= 1024; it pays
+// when tiles are few (M = 4096: 336 tiles for 256 CUs, 10% faster).  With
+// short K (the low-rank factor 2, K = 512) the launch is bound by its output
+// stores and the split measured slower.
+constexpr double kHalfTileCost = 0.625;   // TJ = 2 tile time / TJ = 4 tile time
+constexpr double kLaunchCost = 0.05;      // a second launch, in tile times
+
 template <int OUT, bool HAS_BIAS>
 hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
@@ -1016,8 +1023,28 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
 {
     if constexpr (OUT == int(OutKind::GELU_BF16))
         hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
-    return launch_tj<OUT, HAS_BIAS, 4>(qx, qw, sx, sw, bias, Y, M, N, K, device_cu_count(),
-                                       stream);
+    const int cus = device_cu_count();
+    const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
+    auto rounds = [&](int64_t tiles) { return (double)((tiles + cus - 1) / cus); };
+    int64_t best_a = tm;
+    double best = rounds(tm * tn);
+    for (int64_t a = tm - 1; K >= 1024 && a >= 0 && a >= tm - 16; --a) {
+        const double t = rounds(a * tn) + kHalfTileCost * rounds(2 * (tm - a) * tn) + kLaunchCost;
+        if (t < best - 0.1) {
+            best = t;
+            best_a = a;
+        }
+    }
+    const int64_t m1 = std::min<int64_t>(M, best_a * kTile);
+    if (m1 > 0) {
+        const hipError_t e =
+            launch_tj<OUT, HAS_BIAS, 4>(qx, qw, sx, sw, bias, Y, m1, N, K, cus, stream);
+        if (e != hipSuccess || m1 == M) return e;
+    }
+    constexpr size_t ysize = OUT == int(OutKind::F32) || OUT == int(OutKind::I32) ? 4 : 2;
+    return launch_tj<OUT, HAS_BIAS, 2>(qx + m1 * K, qw, sx ? sx + m1 : nullptr, sw, bias,
+                                       static_cast<char *>(Y) + (size_t)(m1 * N) * ysize,
+                                       M - m1, N, K, cus, stream);
 }
 
 } // namespace
