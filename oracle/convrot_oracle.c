@@ -24,6 +24,10 @@
  *    package is W8A8 and also holds low-rank factorised linears;
  *    "Standalone Transformer (AutoModel)": low-rank ranks get padded to a
  *    multiple of 64.
+ *  - MiniMax-H3-Rung-Omega README, "Technical Architecture Overview", item 1:
+ *    a rotation by the regular ("DC-balanced") orthogonal Hadamard
+ *    H_256 = H_4 (x) H_4 (x) H_4 (x) H_4 on 256-element blocks, offered here as
+ *    the second rotation kind (orders 64 and 256).
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *  R1 Sylvester Hadamard in natural order, unnormalised; 1/sqrt(b) is folded
@@ -36,6 +40,10 @@
  *  R5 bf16 outputs are round-to-nearest-even of the fp32 value.
  *  R6 Low-rank: bf16 intermediate, requantised with the same block b along r.
  *  R7 MLP pair: g = bf16(GELU_erf(float(u))) with GELU evaluated in fp64.
+ *  R8 Regular rotation: H_4 = J - 2I (diagonal -1, every other entry +1, so
+ *     every row sums to 2), applied along the base-4 digits of the index in
+ *     ascending order; a group (v0, v1, v2, v3) becomes S - 2 v_j with
+ *     S = (v0 + v1) + (v2 + v3), in fp32.  The scale folds 1/sqrt(b) as in R1.
  *
  * Precision: every step that decides an INT8 code is evaluated in fp32 (the
  * precision the GPU kernels take those decisions in), with the butterfly order
@@ -116,6 +124,50 @@ int oracle_fwht_f32(float *v, int64_t K, int b)
     return OR_OK;
 }
 
+static int is_pow4(long long b) { return is_pow2(b) && (b & 0x55555555LL) != 0; }
+
+/* In place on v[0..K): each length-b block (b a power of 4) becomes
+ * (H_4 (x) ... (x) H_4) . block with the regular H_4 = J - 2I of R8: for each
+ * base-4 digit of the index, lowest first, every group of four elements that
+ * differ only in that digit (v_j at digit value j) becomes S - 2 v_j with
+ * S = (v0 + v1) + (v2 + v3).  2 v_j is exact, so each output is one rounding
+ * of S - 2 v_j. */
+int oracle_fwht_regular_f32(float *v, int64_t K, int b)
+{
+    if (!is_pow4(b) || K < 0 || K % b != 0)
+        return OR_EINVAL;
+    for (int64_t j0 = 0; j0 < K; j0 += b) {
+        float *blk = v + j0;
+        for (int h = 1; h < b; h *= 4) {
+            for (int i = 0; i < b; ++i) {
+                if ((i / h) % 4 != 0)
+                    continue;
+                float a0 = blk[i], a1 = blk[i + h], a2 = blk[i + 2 * h], a3 = blk[i + 3 * h];
+                float S = (a0 + a1) + (a2 + a3);
+                blk[i] = S - 2.0f * a0;
+                blk[i + h] = S - 2.0f * a1;
+                blk[i + 2 * h] = S - 2.0f * a2;
+                blk[i + 3 * h] = S - 2.0f * a3;
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Rotation kinds: 0 = the Sylvester blocks of R1, 1 = the regular blocks of
+ * R8. */
+#define OR_ROT_SYLVESTER 0
+#define OR_ROT_REGULAR 1
+
+int oracle_rotate_f32(float *v, int64_t K, int b, int rot)
+{
+    if (rot == OR_ROT_SYLVESTER)
+        return oracle_fwht_f32(v, K, b);
+    if (rot == OR_ROT_REGULAR)
+        return oracle_fwht_regular_f32(v, K, b);
+    return OR_EINVAL;
+}
+
 /* The fp32 value of 1/sqrt(b), rounded once from double. */
 float oracle_inv_sqrt_b(int b) { return (float)(1.0 / sqrt((double)b)); }
 
@@ -156,12 +208,15 @@ int oracle_rowquant(const float *v, int64_t K, int b, int8_t *q, float *s)
 /* ------------------------------------------------------------------ */
 
 /* Rows of `src` (fp32 or bf16, row stride `ld` elements) -> codes [rows, K]
- * and one scale per row.  Rows are independent; OpenMP splits them. */
-int oracle_rotate_quantize_rows(const void *src, int dtype, int64_t rows,
-                                int64_t K, int64_t ld, int b, int8_t *q,
-                                float *s)
+ * and one scale per row, rotated with rotation kind `rot`.  Rows are
+ * independent; OpenMP splits them. */
+int oracle_rotate_quantize_rows_rot(const void *src, int dtype, int64_t rows,
+                                    int64_t K, int64_t ld, int b, int rot, int8_t *q,
+                                    float *s)
 {
     if (!is_pow2(b) || K <= 0 || K % b != 0 || rows < 0 || ld < K)
+        return OR_EINVAL;
+    if (rot != OR_ROT_SYLVESTER && (rot != OR_ROT_REGULAR || !is_pow4(b)))
         return OR_EINVAL;
     if (dtype != OR_F32 && dtype != OR_BF16)
         return OR_EINVAL;
@@ -177,7 +232,7 @@ int oracle_rotate_quantize_rows(const void *src, int dtype, int64_t rows,
                 else
                     row[k] = oracle_bf16_to_f32(((const uint16_t *)src)[m * ld + k]);
             }
-            oracle_fwht_f32(row, K, b);
+            oracle_rotate_f32(row, K, b, rot);
             if (oracle_rowquant(row, K, b, q + m * K, s + m) != OR_OK) {
 #pragma omp atomic write
                 bad = 1;
@@ -188,9 +243,16 @@ int oracle_rotate_quantize_rows(const void *src, int dtype, int64_t rows,
     return bad ? OR_ENONFINITE : OR_OK;
 }
 
+int oracle_rotate_quantize_rows(const void *src, int dtype, int64_t rows,
+                                int64_t K, int64_t ld, int b, int8_t *q,
+                                float *s)
+{
+    return oracle_rotate_quantize_rows_rot(src, dtype, rows, K, ld, b, OR_ROT_SYLVESTER, q, s);
+}
+
 /* O3 for an input-major [K, N] weight: row n of W is column n. */
-int oracle_prepare_weights_in_major(const void *src, int dtype, int64_t N,
-                                    int64_t K, int b, int8_t *q, float *s)
+int oracle_prepare_weights_in_major_rot(const void *src, int dtype, int64_t N,
+                                        int64_t K, int b, int rot, int8_t *q, float *s)
 {
     if (!is_pow2(b) || K <= 0 || K % b != 0 || N < 0)
         return OR_EINVAL;
@@ -204,9 +266,15 @@ int oracle_prepare_weights_in_major(const void *src, int dtype, int64_t N,
             tmp[n * K + k] = (dtype == OR_F32)
                                  ? ((const float *)src)[k * N + n]
                                  : oracle_bf16_to_f32(((const uint16_t *)src)[k * N + n]);
-    int rc = oracle_rotate_quantize_rows(tmp, OR_F32, N, K, K, b, q, s);
+    int rc = oracle_rotate_quantize_rows_rot(tmp, OR_F32, N, K, K, b, rot, q, s);
     free(tmp);
     return rc;
+}
+
+int oracle_prepare_weights_in_major(const void *src, int dtype, int64_t N,
+                                    int64_t K, int b, int8_t *q, float *s)
+{
+    return oracle_prepare_weights_in_major_rot(src, dtype, N, K, b, OR_ROT_SYLVESTER, q, s);
 }
 
 /* ------------------------------------------------------------------ */
@@ -272,10 +340,11 @@ int oracle_dequant(const int32_t *acc, const float *sx, const float *sw,
 /* Whole linear: O4 -> O5 -> O6/O7                                     */
 /* ------------------------------------------------------------------ */
 
-/* X is bf16 [M, K]; qw/sw are the prepared weights [N, K] / [N]. */
-int oracle_linear_forward(const uint16_t *X, int64_t M, int64_t K, int b,
-                          const int8_t *qw, const float *sw, int64_t N,
-                          const float *bias, int out_dtype, void *out)
+/* X is bf16 [M, K]; qw/sw are the prepared weights [N, K] / [N], rotated
+ * with kind `rot` (the activations get the same rotation). */
+int oracle_linear_forward_rot(const uint16_t *X, int64_t M, int64_t K, int b, int rot,
+                              const int8_t *qw, const float *sw, int64_t N,
+                              const float *bias, int out_dtype, void *out)
 {
     if (M == 0)
         return OR_OK;
@@ -284,7 +353,7 @@ int oracle_linear_forward(const uint16_t *X, int64_t M, int64_t K, int b,
     int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)M * (size_t)N);
     int rc = OR_EINVAL;
     if (qx && sx && acc) {
-        rc = oracle_rotate_quantize_rows(X, OR_BF16, M, K, K, b, qx, sx);
+        rc = oracle_rotate_quantize_rows_rot(X, OR_BF16, M, K, K, b, rot, qx, sx);
         if (rc == OR_OK)
             rc = oracle_gemm_i32(qx, qw, M, N, K, acc);
         if (rc == OR_OK)
@@ -296,6 +365,14 @@ int oracle_linear_forward(const uint16_t *X, int64_t M, int64_t K, int b,
     return rc;
 }
 
+int oracle_linear_forward(const uint16_t *X, int64_t M, int64_t K, int b,
+                          const int8_t *qw, const float *sw, int64_t N,
+                          const float *bias, int out_dtype, void *out)
+{
+    return oracle_linear_forward_rot(X, M, K, b, OR_ROT_SYLVESTER, qw, sw, N, bias,
+                                     out_dtype, out);
+}
+
 /* ------------------------------------------------------------------ */
 /* O8: low-rank chain (R6)                                             */
 /* ------------------------------------------------------------------ */
@@ -303,11 +380,11 @@ int oracle_linear_forward(const uint16_t *X, int64_t M, int64_t K, int b,
 /* h = bf16(linear(X; A)) with A [r, K] and no bias, then
  * y = linear(h; B) with B [N, r] and the bias.  If h_out is not NULL the bf16
  * intermediate is returned too. */
-int oracle_lowrank_forward(const uint16_t *X, int64_t M, int64_t K, int b,
-                           const int8_t *qa, const float *sa, int64_t r,
-                           const int8_t *qb, const float *sb, int64_t N,
-                           const float *bias, int out_dtype, void *out,
-                           uint16_t *h_out)
+int oracle_lowrank_forward_rot(const uint16_t *X, int64_t M, int64_t K, int b, int rot,
+                               const int8_t *qa, const float *sa, int64_t r,
+                               const int8_t *qb, const float *sb, int64_t N,
+                               const float *bias, int out_dtype, void *out,
+                               uint16_t *h_out)
 {
     if (r <= 0 || r % b != 0)
         return OR_EINVAL;
@@ -316,13 +393,23 @@ int oracle_lowrank_forward(const uint16_t *X, int64_t M, int64_t K, int b,
     uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)M * (size_t)r);
     if (!h)
         return OR_EINVAL;
-    int rc = oracle_linear_forward(X, M, K, b, qa, sa, r, NULL, OR_BF16, h);
+    int rc = oracle_linear_forward_rot(X, M, K, b, rot, qa, sa, r, NULL, OR_BF16, h);
     if (rc == OR_OK)
-        rc = oracle_linear_forward(h, M, r, b, qb, sb, N, bias, out_dtype, out);
+        rc = oracle_linear_forward_rot(h, M, r, b, rot, qb, sb, N, bias, out_dtype, out);
     if (rc == OR_OK && h_out)
         memcpy(h_out, h, sizeof(uint16_t) * (size_t)M * (size_t)r);
     free(h);
     return rc;
+}
+
+int oracle_lowrank_forward(const uint16_t *X, int64_t M, int64_t K, int b,
+                           const int8_t *qa, const float *sa, int64_t r,
+                           const int8_t *qb, const float *sb, int64_t N,
+                           const float *bias, int out_dtype, void *out,
+                           uint16_t *h_out)
+{
+    return oracle_lowrank_forward_rot(X, M, K, b, OR_ROT_SYLVESTER, qa, sa, r, qb, sb, N,
+                                      bias, out_dtype, out, h_out);
 }
 
 /* ------------------------------------------------------------------ */
@@ -344,11 +431,11 @@ void oracle_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g)
 
 /* u = bf16(linear(X; W_up, bias_up)); g = GELU(u); y = linear(g; W_down,
  * bias_down).  u_out / g_out, when not NULL, receive the intermediates. */
-int oracle_mlp_forward(const uint16_t *X, int64_t M, int64_t K, int b,
-                       const int8_t *qu, const float *su, int64_t F,
-                       const float *bias_up, const int8_t *qd, const float *sd,
-                       int64_t N, const float *bias_down, int out_dtype,
-                       void *out, uint16_t *u_out, uint16_t *g_out)
+int oracle_mlp_forward_rot(const uint16_t *X, int64_t M, int64_t K, int b, int rot,
+                           const int8_t *qu, const float *su, int64_t F,
+                           const float *bias_up, const int8_t *qd, const float *sd,
+                           int64_t N, const float *bias_down, int out_dtype,
+                           void *out, uint16_t *u_out, uint16_t *g_out)
 {
     if (F <= 0 || F % b != 0)
         return OR_EINVAL;
@@ -359,11 +446,11 @@ int oracle_mlp_forward(const uint16_t *X, int64_t M, int64_t K, int b,
     uint16_t *g = (uint16_t *)malloc(sizeof(uint16_t) * n);
     int rc = OR_EINVAL;
     if (u && g) {
-        rc = oracle_linear_forward(X, M, K, b, qu, su, F, bias_up, OR_BF16, u);
+        rc = oracle_linear_forward_rot(X, M, K, b, rot, qu, su, F, bias_up, OR_BF16, u);
         if (rc == OR_OK) {
             oracle_gelu_bf16(u, (int64_t)n, g);
-            rc = oracle_linear_forward(g, M, F, b, qd, sd, N, bias_down,
-                                       out_dtype, out);
+            rc = oracle_linear_forward_rot(g, M, F, b, rot, qd, sd, N, bias_down,
+                                           out_dtype, out);
         }
         if (rc == OR_OK && u_out)
             memcpy(u_out, u, sizeof(uint16_t) * n);
@@ -373,4 +460,14 @@ int oracle_mlp_forward(const uint16_t *X, int64_t M, int64_t K, int b,
     free(u);
     free(g);
     return rc;
+}
+
+int oracle_mlp_forward(const uint16_t *X, int64_t M, int64_t K, int b,
+                       const int8_t *qu, const float *su, int64_t F,
+                       const float *bias_up, const int8_t *qd, const float *sd,
+                       int64_t N, const float *bias_down, int out_dtype,
+                       void *out, uint16_t *u_out, uint16_t *g_out)
+{
+    return oracle_mlp_forward_rot(X, M, K, b, OR_ROT_SYLVESTER, qu, su, F, bias_up, qd, sd, N,
+                                  bias_down, out_dtype, out, u_out, g_out);
 }

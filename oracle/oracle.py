@@ -65,6 +65,21 @@ def open_library(path):
         "oracle_mlp_forward": (
             _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_p, _c_p, _c_i64, _c_p,
                      _c_p, _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_p]),
+        "oracle_fwht_regular_f32": (_c_int, [_c_p, _c_i64, _c_int]),
+        "oracle_rotate_f32": (_c_int, [_c_p, _c_i64, _c_int, _c_int]),
+        "oracle_rotate_quantize_rows_rot": (
+            _c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p]),
+        "oracle_prepare_weights_in_major_rot": (
+            _c_int, [_c_p, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p]),
+        "oracle_linear_forward_rot": (
+            _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
+                     _c_int, _c_p]),
+        "oracle_lowrank_forward_rot": (
+            _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
+                     _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p]),
+        "oracle_mlp_forward_rot": (
+            _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
+                     _c_p, _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -93,6 +108,17 @@ def _check(rc, what):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+# rotation kinds: the Sylvester blocks (R1) or the regular H_4 Kronecker
+# blocks of the Rung-Omega README (R8)
+ROTATIONS = {"sylvester": 0, "regular": 1}
+
+
+def _rot(rot: str) -> int:
+    if rot not in ROTATIONS:
+        raise ValueError(rot)
+    return ROTATIONS[rot]
 
 
 # ---------------------------------------------------------------- bf16 ----
@@ -126,15 +152,16 @@ def inv_sqrt_b(b: int) -> np.float32:
 
 # -------------------------------------------------------------- O1, O2 ----
 
-def fwht(v, b: int) -> np.ndarray:
-    """O1: blockwise Sylvester FWHT of every row (fp32, ascending strides)."""
+def fwht(v, b: int, rot: str = "sylvester") -> np.ndarray:
+    """O1: blockwise Sylvester FWHT of every row (fp32, ascending strides), or
+    with rot='regular' the regular H_4 Kronecker blocks (R8)."""
     lib = _load()
     out = _c(v, np.float32).copy()
     K = out.shape[-1]
     rows = out.reshape(-1, K)
     for r in range(rows.shape[0]):
         row = np.ascontiguousarray(rows[r])
-        _check(lib.oracle_fwht_f32(_ptr(row), K, int(b)), "fwht")
+        _check(lib.oracle_rotate_f32(_ptr(row), K, int(b), _rot(rot)), "fwht")
         rows[r] = row
     return out
 
@@ -160,7 +187,7 @@ def rowquant(v, b: int):
 
 # -------------------------------------------------------------- O3, O4 ----
 
-def rotate_quantize(x, b: int, dtype: str):
+def rotate_quantize(x, b: int, dtype: str, rot: str = "sylvester"):
     """O4 (activations, dtype='bf16' raw uint16) or O3 (weights, 'f32')."""
     lib = _load()
     if dtype == "bf16":
@@ -174,17 +201,18 @@ def rotate_quantize(x, b: int, dtype: str):
     rows, K = x.shape
     q = np.empty((rows, K), dtype=np.int8)
     s = np.empty(rows, dtype=np.float32)
-    _check(lib.oracle_rotate_quantize_rows(_ptr(x), tag, rows, K, K, int(b),
-                                           _ptr(q), _ptr(s)), "rotate_quantize")
+    _check(lib.oracle_rotate_quantize_rows_rot(_ptr(x), tag, rows, K, K, int(b), _rot(rot),
+                                               _ptr(q), _ptr(s)), "rotate_quantize")
     return q, s
 
 
-def prepare_weights(W, b: int, dtype: str = "f32", layout: str = "out_major"):
+def prepare_weights(W, b: int, dtype: str = "f32", layout: str = "out_major",
+                    rot: str = "sylvester"):
     """O3: codes and per-output scales of the rotated weight W . R^T.
 
     ``layout='out_major'`` takes W as [N, K]; ``'in_major'`` as [K, N]."""
     if layout == "out_major":
-        return rotate_quantize(W, b, dtype)
+        return rotate_quantize(W, b, dtype, rot)
     if layout != "in_major":
         raise ValueError(layout)
     lib = _load()
@@ -197,8 +225,8 @@ def prepare_weights(W, b: int, dtype: str = "f32", layout: str = "out_major"):
     K, N = W.shape
     q = np.empty((N, K), dtype=np.int8)
     s = np.empty(N, dtype=np.float32)
-    _check(lib.oracle_prepare_weights_in_major(_ptr(W), tag, N, K, int(b),
-                                               _ptr(q), _ptr(s)), "prepare")
+    _check(lib.oracle_prepare_weights_in_major_rot(_ptr(W), tag, N, K, int(b), _rot(rot),
+                                                   _ptr(q), _ptr(s)), "prepare")
     return q, s
 
 
@@ -236,7 +264,8 @@ def dequant(acc, sx, sw, bias=None, out: str = "f32") -> np.ndarray:
     return y
 
 
-def linear_forward(X_bf16, qw, sw, b: int, bias=None, out: str = "bf16"):
+def linear_forward(X_bf16, qw, sw, b: int, bias=None, out: str = "bf16",
+                   rot: str = "sylvester"):
     """O4 -> O5 -> O6/O7 on bf16 activations [M, K]."""
     lib = _load()
     X = _c(X_bf16, np.uint16)
@@ -246,14 +275,15 @@ def linear_forward(X_bf16, qw, sw, b: int, bias=None, out: str = "bf16"):
     M, K = X.shape
     N = qw.shape[0]
     y = np.empty((M, N), dtype=np.float32 if out == "f32" else np.uint16)
-    _check(lib.oracle_linear_forward(_ptr(X), M, K, int(b), _ptr(qw), _ptr(sw),
-                                     N, _ptr(bias), F32 if out == "f32" else BF16,
-                                     _ptr(y)), "linear_forward")
+    _check(lib.oracle_linear_forward_rot(_ptr(X), M, K, int(b), _rot(rot), _ptr(qw),
+                                         _ptr(sw), N, _ptr(bias),
+                                         F32 if out == "f32" else BF16, _ptr(y)),
+           "linear_forward")
     return y
 
 
 def lowrank_forward(X_bf16, qa, sa, qb, sb, b: int, bias=None,
-                    out: str = "bf16", return_h: bool = False):
+                    out: str = "bf16", return_h: bool = False, rot: str = "sylvester"):
     """O8: h = bf16(linear(X; A)); y = linear(h; B, bias)."""
     lib = _load()
     X = _c(X_bf16, np.uint16)
@@ -266,10 +296,10 @@ def lowrank_forward(X_bf16, qa, sa, qb, sb, b: int, bias=None,
     assert qb.shape[1] == r
     y = np.empty((M, N), dtype=np.float32 if out == "f32" else np.uint16)
     h = np.empty((M, r), dtype=np.uint16)
-    _check(lib.oracle_lowrank_forward(_ptr(X), M, K, int(b), _ptr(qa), _ptr(sa),
-                                      r, _ptr(qb), _ptr(sb), N, _ptr(bias),
-                                      F32 if out == "f32" else BF16, _ptr(y),
-                                      _ptr(h)), "lowrank_forward")
+    _check(lib.oracle_lowrank_forward_rot(_ptr(X), M, K, int(b), _rot(rot), _ptr(qa),
+                                          _ptr(sa), r, _ptr(qb), _ptr(sb), N, _ptr(bias),
+                                          F32 if out == "f32" else BF16, _ptr(y),
+                                          _ptr(h)), "lowrank_forward")
     return (y, h) if return_h else y
 
 
@@ -287,7 +317,8 @@ def gelu_bf16(u_bf16) -> np.ndarray:
 
 
 def mlp_forward(X_bf16, qu, su, qd, sd, b: int, bias_up=None, bias_down=None,
-                out: str = "bf16", return_intermediates: bool = False):
+                out: str = "bf16", return_intermediates: bool = False,
+                rot: str = "sylvester"):
     """O9: u = bf16(linear(X; W_up)); g = GELU(u); y = linear(g; W_down)."""
     lib = _load()
     X = _c(X_bf16, np.uint16)
@@ -302,10 +333,10 @@ def mlp_forward(X_bf16, qu, su, qd, sd, b: int, bias_up=None, bias_down=None,
     y = np.empty((M, N), dtype=np.float32 if out == "f32" else np.uint16)
     u = np.empty((M, F), dtype=np.uint16)
     g = np.empty((M, F), dtype=np.uint16)
-    _check(lib.oracle_mlp_forward(_ptr(X), M, K, int(b), _ptr(qu), _ptr(su), F,
-                                  _ptr(bu), _ptr(qd), _ptr(sd), N, _ptr(bd),
-                                  F32 if out == "f32" else BF16, _ptr(y),
-                                  _ptr(u), _ptr(g)), "mlp_forward")
+    _check(lib.oracle_mlp_forward_rot(_ptr(X), M, K, int(b), _rot(rot), _ptr(qu), _ptr(su),
+                                      F, _ptr(bu), _ptr(qd), _ptr(sd), N, _ptr(bd),
+                                      F32 if out == "f32" else BF16, _ptr(y),
+                                      _ptr(u), _ptr(g)), "mlp_forward")
     return (y, u, g) if return_intermediates else y
 
 

@@ -41,11 +41,15 @@ MUTANTS = [
      ["test_gelu_values", "test_gelu_bf16_and_mlp_chain"]),
     ("stage_stride_skip", "for (int h = 1; h < b; h *= 2)", "for (int h = 1; h < b; h *= 4)",
      ["test_fwht_columns_are_sylvester", "test_hadamard_orthogonality"]),
+    ("regular_sign", "blk[i + 2 * h] = S - 2.0f * a2;", "blk[i + 2 * h] = 2.0f * a2 - S;",
+     ["test_regular_columns", "test_regular_hadamard_properties"]),
+    ("regular_digit_skip", "for (int h = 1; h < b; h *= 4)", "for (int h = 4; h < b; h *= 4)",
+     ["test_regular_columns", "test_regular_hadamard_properties"]),
 ]
 
 CALL = {
     "test_golden_hand_example_b4": lambda: pins.test_golden_hand_example_b4(),
-    "test_rotation_identity_end_to_end": lambda: pins.test_rotation_identity_end_to_end(128),
+    "test_rotation_identity_end_to_end": lambda: pins.test_rotation_identity_end_to_end(128, "sylvester"),
     "test_fwht_columns_are_sylvester": lambda: pins.test_fwht_columns_are_sylvester(8),
     "test_hadamard_orthogonality": lambda: pins.test_hadamard_orthogonality(64),
     "test_rowquant_rne_ties": lambda: pins.test_rowquant_rne_ties(),
@@ -56,6 +60,8 @@ CALL = {
     "test_bf16_narrowing_matches_torch": lambda: pins.test_bf16_narrowing_matches_torch(),
     "test_gelu_values": lambda: pins.test_gelu_values(),
     "test_gelu_bf16_and_mlp_chain": lambda: pins.test_gelu_bf16_and_mlp_chain(),
+    "test_regular_columns": lambda: pins.test_regular_columns(64),
+    "test_regular_hadamard_properties": lambda: pins.test_regular_hadamard_properties(64),
 }
 
 

@@ -82,6 +82,69 @@ def test_fwht_fp32_vs_fp64_dense(b):
     assert np.max(np.abs(got - ref)) <= np.max(bound)
 
 
+# ------------------------------------------ regular H_4 Kronecker blocks ----
+# The Rung-Omega README ("Technical Architecture Overview", item 1) rotates
+# with the regular ("DC-balanced") orthogonal H_256 = H_4 (x) H_4 (x) H_4 (x)
+# H_4; the reading takes H_4 = J - 2I.  These pins build the matrix with
+# numpy.kron, independently of the oracle's digit-by-digit transform.
+
+def regular_h(b):
+    H4 = np.ones((4, 4)) - 2.0 * np.eye(4)
+    H = np.ones((1, 1))
+    while H.shape[0] < b:
+        H = np.kron(H, H4)
+    return H
+
+
+@pytest.mark.parametrize("b", [4, 16, 64, 256])
+def test_regular_columns(b):
+    """Transform of e_i is column i of the Kronecker power of J - 2I (exact)."""
+    cols = oracle.fwht(np.eye(b, dtype=np.float32), b, rot="regular")
+    assert np.array_equal(cols.T.astype(np.float64), regular_h(b))
+
+
+@pytest.mark.parametrize("b", [4, 64, 256])
+def test_regular_hadamard_properties(b):
+    """H H^T = b I, H symmetric, every row sums to sqrt(b) (regular), the
+    all-ones vector maps to sqrt(b) times itself (DC stays DC) and applying
+    the transform twice gives b v, all exact."""
+    H = oracle.fwht(np.eye(b, dtype=np.float32), b, rot="regular").T.astype(np.int64)
+    assert np.array_equal(H @ H.T, b * np.eye(b, dtype=np.int64))
+    assert np.array_equal(H, H.T)
+    root = int(round(math.sqrt(b)))
+    assert np.all(H.sum(axis=1) == root)
+    ones = oracle.fwht(np.ones((1, 2 * b), np.float32), b, rot="regular")
+    assert np.array_equal(ones, np.full((1, 2 * b), root, np.float32))
+    rng = np.random.default_rng(b)
+    v = rng.integers(-8, 9, size=(3, 2 * b)).astype(np.float32)
+    twice = oracle.fwht(oracle.fwht(v, b, rot="regular"), b, rot="regular")
+    assert np.array_equal(twice, b * v)
+
+
+@pytest.mark.parametrize("b", [64, 256])
+def test_regular_fp32_vs_fp64_dense(b):
+    """fp32 digit stages stay within a rounding bound of the fp64 dense
+    product: each stage adds at most 4 roundings of magnitude <= the block's
+    L1 norm, and H_4 amplifies earlier errors at most 4-fold."""
+    rng = np.random.default_rng(5)
+    x = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(
+        rng.standard_normal((8, 2 * b)).astype(np.float32)))
+    got = oracle.fwht(x, b, rot="regular").astype(np.float64)
+    H = regular_h(b)
+    ref = (x.astype(np.float64).reshape(8, -1, b) @ H.T).reshape(8, -1)
+    k = int(round(math.log(b, 4)))
+    l1 = np.abs(x.astype(np.float64)).reshape(8, -1, b).sum(-1)
+    bound = 4 * float(F32_EPS) * 1.01 * (4 ** k - 1) / 3 * np.repeat(l1, b, axis=1)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_regular_rejects_orders_not_powers_of_four():
+    with pytest.raises(ValueError):
+        oracle.fwht(np.zeros((1, 128), np.float32), 128, rot="regular")
+    with pytest.raises(ValueError):
+        oracle.rotate_quantize(np.zeros((1, 128), np.float32), 128, "f32", rot="regular")
+
+
 # --------------------------------------------------- hand-worked example ----
 
 def _rat(p):
@@ -317,8 +380,9 @@ def _bound_linear(xf64, W64, b, sx, sw):
     return bound
 
 
-@pytest.mark.parametrize("b", [64, 128, 256])
-def test_rotation_identity_end_to_end(b):
+@pytest.mark.parametrize("b,rot", [(64, "sylvester"), (128, "sylvester"), (256, "sylvester"),
+                                   (64, "regular"), (256, "regular")])
+def test_rotation_identity_end_to_end(b, rot):
     """(W R^T)(R x) = W x: the oracle's output stays within the closed-form
     quantisation bound of the fp64 product W x, and is far tighter than what a
     missing 1/sqrt(b), a sign slip or a transposed operand would give."""
@@ -327,9 +391,9 @@ def test_rotation_identity_end_to_end(b):
     W = w.weight()
     xf = wl.bf16_bits_to_f32(x).astype(np.float64)
     ref = xf @ W.astype(np.float64).T
-    qw, sw = oracle.prepare_weights(W, b)
-    qx, sx = oracle.rotate_quantize(x, b, "bf16")
-    y = oracle.linear_forward(x, qw, sw, b, out="f32").astype(np.float64)
+    qw, sw = oracle.prepare_weights(W, b, rot=rot)
+    qx, sx = oracle.rotate_quantize(x, b, "bf16", rot=rot)
+    y = oracle.linear_forward(x, qw, sw, b, out="f32", rot=rot).astype(np.float64)
     bound = _bound_linear(xf, W.astype(np.float64), b, sx, sw)
     assert np.all(np.abs(y - ref) <= bound + 1e-6 * np.abs(ref))
     # the worst-case bound is loose; the typical error is what an 8-bit grid
