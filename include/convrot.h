@@ -104,6 +104,16 @@ typedef enum convrot_layout {
 } convrot_layout;
 
 #define CONVROT_WEIGHTS_MAGIC 0x38545243u /* "CRT8" little-endian */
+
+/* Rotation kind, in convrot_weights.flags and in convrot_rotate_quantize's
+ * flags.  0: the Sylvester blocks H_b (b in {64, 128, 256}).
+ * CONVROT_ROT_REGULAR: the regular ("DC-balanced") orthogonal Hadamard
+ * H_4 (x) ... (x) H_4 with H_4 = J - 2I (every row sums to 2), b in {64, 256}
+ * (MiniMax-H3-Rung-Omega README, "Technical Architecture Overview", item 1:
+ * H_256 = H_4^(x)4).  It is applied along the base-4 digits of the in-block
+ * index, lowest first; a group (v0..v3) becomes S - 2 v_j with
+ * S = (v0 + v1) + (v2 + v3) in fp32.  The scale folds 1/sqrt(b) either way. */
+#define CONVROT_ROT_REGULAR 0x100u
 #define CONVROT_WEIGHTS_VERSION 2u
 
 /* Prepared (pre-rotated, quantised, packed) weights of one linear layer.
@@ -122,7 +132,7 @@ typedef struct convrot_weights {
     int64_t N;                 /* output channels */
     int64_t K;                 /* input channels */
     int32_t block;             /* Hadamard block b the codes were rotated with */
-    int32_t flags;             /* reserved, 0 */
+    int32_t flags;             /* rotation kind: 0 or CONVROT_ROT_REGULAR */
     int8_t *codes;             /* device, K-tiled INT8 codes of W . R^T [N, K] */
     float *scale;              /* device, [N] per-output F32 scales */
 } convrot_weights;
@@ -175,7 +185,9 @@ CONVROT_API size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, 
  *   block     Hadamard block b in {64, 128, 256}; K % block == 0.
  *   out       host struct; out->codes and out->scale must point to caller
  *             allocations of convrot_weights_packed_bytes(N, K, block) and 4*N
- *             bytes.  On success every other field is filled in.
+ *             bytes, and out->flags selects the rotation kind (0 or
+ *             CONVROT_ROT_REGULAR; EINVAL for other bits or for the regular
+ *             kind at b = 128).  On success every other field is filled in.
  *   ws        device workspace of convrot_prepare_workspace_bytes(...) bytes
  *             (may be NULL when that query returns 0).
  * Float weights: row n of W becomes codes/scale of FWHT_b(W[n, :]) quantised
@@ -206,7 +218,8 @@ CONVROT_API int convrot_linear_forward(const void *X, int64_t M, const convrot_w
 /* Low-rank ConvRot linear: h = bf16(linear(X; A)) with A [r, K] and no bias,
  * then Y = linear(h; B) with B [N, r] and the bias; h is re-rotated along r
  * with the same block and requantised per token.  Requires A->N == B->K (= r),
- * A->block == B->block and r % 128 == 0 (pad the rank with zero rows of A and
+ * A->block == B->block, the same rotation kind (A->flags == B->flags) and
+ * r % 128 == 0 (pad the rank with zero rows of A and
  * zero columns of B, which leaves the product unchanged). */
 CONVROT_API int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
                             const convrot_weights *B, const float *bias,
@@ -215,7 +228,7 @@ CONVROT_API int lowrank_convrot_forward(const void *X, int64_t M, const convrot_
 
 /* MLP pair: u = bf16(linear(X; W_up) + bias_up); g = bf16(GELU(u)) with the
  * erf form of GELU (see convrot_gelu_bf16); Y = linear(g; W_down) + bias_down.
- * Requires W_up->N == W_down->K (= F).  GELU is applied in the epilogue of the
+ * Requires W_up->N == W_down->K (= F) and the same block and rotation kind.  GELU is applied in the epilogue of the
  * up projection, so u is never written. */
 CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
                         const float *bias_up, const convrot_weights *W_down,
@@ -229,7 +242,7 @@ CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weig
 
 /* Rotate and quantise rows: X [M, K] row-major (x_dtype F32 or BF16) -> q
  * K-tiled int8 codes (Mp x K bytes; the padding rows are left as they were)
- * and s [M] F32.  flags must be 0. */
+ * and s [M] F32.  flags: 0 or CONVROT_ROT_REGULAR (the rotation kind). */
 CONVROT_API int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K,
                             int block, uint32_t flags, int8_t *q, float *s,
                             void *stream);
@@ -257,9 +270,9 @@ CONVROT_API int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_
  * q_x (K-tiled, Mp x A->K bytes) and s_x [M] F32 come from
  * convrot_rotate_quantize; q_h (K-tiled, Mp x r bytes; its padding rows get
  * unspecified codes) and s_h [M] F32 are written.  All device pointers,
- * 16-byte aligned.  Supported for A->block in {64, 128} and r <= 512
- * (CONVROT_EUNSUPPORTED otherwise; lowrank_convrot_forward then runs the
- * two stages separately). */
+ * 16-byte aligned.  Supported for the Sylvester rotation with A->block in
+ * {64, 128} and r <= 512 (CONVROT_EUNSUPPORTED otherwise;
+ * lowrank_convrot_forward then runs the two stages separately). */
 CONVROT_API int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int64_t M,
                             const convrot_weights *A, int8_t *q_h, float *s_h,
                             void *stream);

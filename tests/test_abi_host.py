@@ -182,6 +182,44 @@ def test_hook_validation(cr):
     assert f1(_desc(cr), M=-1) == cr.EINVAL
     assert f1(_desc(cr, N=256, block=64), sh=FAKE_ODD) == cr.EALIGN
     assert lib.convrot_gelu_bf16(FAKE, -1, FAKE, None) == cr.EINVAL
+
+
+def test_rotation_kind_validation(cr):
+    """The regular H_4 rotation exists for b = 64 and 256 only; unknown kind
+    bits are rejected; chained weights must share the kind."""
+    lib = cr.library()
+    R = cr.ROT_REGULAR
+    rq = lambda flags, block, M=0: lib.convrot_rotate_quantize(
+        None, cr.BF16, M, 512, block, flags, None, None, None)
+    assert rq(R, 64) == cr.OK and rq(R, 256) == cr.OK
+    assert rq(R, 128) == cr.EINVAL
+    assert rq(0x200, 64) == cr.EUNSUPPORTED
+    # descriptors
+    reg = lambda **kw: _flag(_desc(cr, **kw), R)
+    assert _fwd(cr, reg(block=128)) == cr.ELAYOUT
+    assert _fwd(cr, _flag(_desc(cr), 0x200)) == cr.ELAYOUT
+    assert _fwd(cr, reg(block=64), M=0) == cr.OK
+    A, B = reg(N=256, K=512, block=64), _desc(cr, N=512, K=256, block=64)
+    assert lib.lowrank_convrot_forward(FAKE, 8, ctypes.byref(A), ctypes.byref(B), None, FAKE,
+                                       1, FAKE, 1 << 30, None) == cr.ELAYOUT
+    up, down = reg(N=256, K=512, block=64), _desc(cr, N=512, K=256, block=64)
+    assert lib.convrot_mlp_forward(FAKE, 8, ctypes.byref(up), None, ctypes.byref(down), None,
+                                   FAKE, 1, FAKE, 1 << 30, None) == cr.ELAYOUT
+    assert lib.convrot_lowrank_factor1(FAKE, FAKE, 4, ctypes.byref(reg(N=256, block=64)), FAKE,
+                                       FAKE, None) == cr.EUNSUPPORTED
+    # prepare: the kind is requested through out->flags
+    d = cr.convrot_weights()
+    d.codes, d.scale, d.flags = FAKE, FAKE + 4096, R
+    assert lib.convrot_linear_prepare_weights(FAKE, cr.F32, cr.OUT_MAJOR, None, 64, 512, 128,
+                                              ctypes.byref(d), None, 0, None) == cr.EINVAL
+    d.flags = 0x200
+    assert lib.convrot_linear_prepare_weights(FAKE, cr.F32, cr.OUT_MAJOR, None, 64, 512, 64,
+                                              ctypes.byref(d), None, 0, None) == cr.EINVAL
+
+
+def _flag(d, flags):
+    d.flags = flags
+    return d
     assert lib.convrot_gelu_bf16(None, 0, None, None) == cr.OK
     assert lib.convrot_gelu_bf16(None, 4, FAKE, None) == cr.EINVAL
 

@@ -76,6 +76,67 @@ def test_rotquant_special_rows(cr):
     assert np.array_equal(host(s), s_ref)
 
 
+# --------------------------------------------- regular H_4 rotation ----
+
+@pytest.mark.parametrize("b", [64, 256])
+@pytest.mark.parametrize("M,K", [(1, 512), (37, 512), (300, 5376), (5, 21504), (2, 65536),
+                                 (130, 768)])
+def test_rotquant_regular_bitexact(cr, b, M, K):
+    """The regular rotation (H_4 = J - 2I Kronecker blocks): codes and scales
+    bit-exact, one-shot and streaming kernels alike."""
+    announce(f"rotquant regular b={b} M={M} K={K}")
+    x = _x(M, K, seed=M + K + 1, outliers=3, gain=30.0)
+    q, s = cr.convrot_rotate_quantize(to_dev_bf16(x), b, rotation="regular")
+    q_ref, s_ref = oracle.rotate_quantize(x, b, "bf16", rot="regular")
+    assert np.array_equal(untile(q, M, K), q_ref)
+    assert np.array_equal(host(s), s_ref)
+
+
+@pytest.mark.parametrize("b", [64, 256])
+def test_regular_prepare_and_linear(cr, b):
+    """Weights prepared with the regular rotation (f32 rows, both layouts) and
+    a ragged forward (bias, bf16 out) against the oracle."""
+    announce(f"regular prepare + linear b={b}")
+    M, K, N = 600, 1280, 784
+    w = wl.Workload("g", "linear", M=M, K=K, N=N, block=b, out="bf16", x_dist="student_t4",
+                    bias_std=0.01, seed=13)
+    x, W, bias = w.activations(), w.weight(), w.bias()
+    pw = cr.convrot_linear_prepare_weights(to_dev(W), b, rotation="regular")
+    qw, sw = oracle.prepare_weights(W, b, rot="regular")
+    assert np.array_equal(untile(pw.codes, N, K), qw)
+    assert np.array_equal(host(pw.scale), sw)
+    pwi = cr.convrot_linear_prepare_weights(to_dev(np.ascontiguousarray(W.T)), b, cr.IN_MAJOR,
+                                            rotation="regular")
+    assert np.array_equal(untile(pwi.codes, N, K), qw)
+    y = cr.convrot_linear_forward(to_dev_bf16(x), pw, bias=to_dev(bias))
+    y_ref = oracle.linear_forward(x, qw, sw, b, bias=bias, out="bf16", rot="regular")
+    assert assert_output_parity(bf16_bits(y), y_ref, "bf16", f"regular b={b}") == 0
+
+
+def test_regular_lowrank_and_mlp(cr):
+    """Low-rank chain (two-stage path: the fused factor 1 is Sylvester-only)
+    and the MLP pair with the regular rotation at b = 64."""
+    announce("regular lowrank + mlp b=64")
+    w = wl.scaled("lowrank_38656", M=520, K=1024, N=784, rank=256, block=64)
+    x, A, B = w.activations(), w.weight("w"), w.weight("w2")
+    pa = cr.convrot_linear_prepare_weights(to_dev(A), 64, rotation="regular")
+    pb = cr.convrot_linear_prepare_weights(to_dev(B), 64, rotation="regular")
+    qa, sa = oracle.prepare_weights(A, 64, rot="regular")
+    qb, sb = oracle.prepare_weights(B, 64, rot="regular")
+    y = cr.lowrank_convrot_forward(to_dev_bf16(x), pa, pb)
+    y_ref = oracle.lowrank_forward(x, qa, sa, qb, sb, 64, out="bf16", rot="regular")
+    assert assert_output_parity(bf16_bits(y), y_ref, "bf16", "regular lowrank") == 0
+    m = wl.scaled("mlp_16384", M=300, K=1024, N=512, ffn=2048, block=64)
+    x, Wu, Wd = m.activations(), m.weight("w"), m.weight("w2")
+    pu = cr.convrot_linear_prepare_weights(to_dev(Wu), 64, rotation="regular")
+    pd = cr.convrot_linear_prepare_weights(to_dev(Wd), 64, rotation="regular")
+    qu, su = oracle.prepare_weights(Wu, 64, rot="regular")
+    qd, sd = oracle.prepare_weights(Wd, 64, rot="regular")
+    y = cr.convrot_mlp_forward(to_dev_bf16(x), pu, pd)
+    y_ref = oracle.mlp_forward(x, qu, su, qd, sd, 64, out="bf16", rot="regular")
+    assert assert_output_parity(bf16_bits(y), y_ref, "bf16", "regular mlp") == 0
+
+
 # -------------------------------------------------------- weight prep ----
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

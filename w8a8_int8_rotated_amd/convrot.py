@@ -20,6 +20,8 @@ F32, BF16, I8, I32 = 0, 1, 2, 3
 OUT_MAJOR, IN_MAJOR = 0, 1
 WEIGHTS_MAGIC = 0x38545243
 WEIGHTS_VERSION = 2
+ROT_REGULAR = 0x100          # rotation kind: regular H_4 Kronecker blocks
+ROTATIONS = {"sylvester": 0, "regular": ROT_REGULAR}
 FLAG_GELU = 1
 
 _c_i64 = ctypes.c_int64
@@ -183,8 +185,9 @@ class PreparedWeights:
 
 def convrot_linear_prepare_weights(W: torch.Tensor, block: int, layout: int = OUT_MAJOR,
                                    src_scale: torch.Tensor | None = None,
-                                   stream=None) -> PreparedWeights:
-    """Rotate + quantise + pack a weight (``[N, K]`` or ``[K, N]`` per layout)."""
+                                   stream=None, rotation: str = "sylvester") -> PreparedWeights:
+    """Rotate + quantise + pack a weight (``[N, K]`` or ``[K, N]`` per layout)
+    with the rotation kind ``'sylvester'`` or ``'regular'``."""
     lib = library()
     if W.dim() != 2:
         raise ValueError("W must be 2-D")
@@ -202,6 +205,7 @@ def convrot_linear_prepare_weights(W: torch.Tensor, block: int, layout: int = OU
     desc = convrot_weights()
     desc.codes = codes.data_ptr()
     desc.scale = scale.data_ptr()
+    desc.flags = ROTATIONS[rotation]
     wsb = lib.convrot_prepare_workspace_bytes(N, K, block, tag, layout)
     ws = _workspace(wsb, W.device, None)
     rc = lib.convrot_linear_prepare_weights(
@@ -281,15 +285,16 @@ def _codes(q, M: int, K: int, device):
     return q
 
 
-def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=None):
+def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=None,
+                            rotation: str = "sylvester"):
     """Rotate + quantise the rows of X: (q, s), q the K-tiled codes (Mp, K)."""
     lib = library()
     M, K = X.shape
     q = _codes(q, M, K, X.device)
     if s is None:
         s = torch.empty(M, dtype=torch.float32, device=X.device)
-    rc = lib.convrot_rotate_quantize(_ptr(X), _dtype_tag(X.dtype), M, K, block, 0, _ptr(q),
-                                     _ptr(s), _stream(stream))
+    rc = lib.convrot_rotate_quantize(_ptr(X), _dtype_tag(X.dtype), M, K, block,
+                                     ROTATIONS[rotation], _ptr(q), _ptr(s), _stream(stream))
     _check("convrot_rotate_quantize", rc)
     return q, s
 

@@ -57,11 +57,12 @@ enum class InType { F32 = 0, BF16 = 1 };
 int device_cu_count();
 enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3 };
 
-// Rotate (blockwise FWHT) + rowwise INT8 quantise.  src rows have stride ld
-// elements; q is K-tiled with padded_rows(M) rows (the padding rows are not
-// written).
+// Rotate (blockwise Sylvester FWHT, or with `regular` the H_4 = J - 2I
+// Kronecker blocks for block 64 or 256) + rowwise INT8 quantise.  src rows
+// have stride ld elements; q is K-tiled with padded_rows(M) rows (the
+// padding rows are not written).
 hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
-                           int64_t ld, int block, float inv_sqrt_b, int8_t *q,
+                           int64_t ld, int block, bool regular, float inv_sqrt_b, int8_t *q,
                            float *s, hipStream_t stream);
 
 // Factor 1 of the low-rank chain with the requantisation fused in:

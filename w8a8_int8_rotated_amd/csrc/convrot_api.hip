@@ -51,6 +51,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_block(int b) { return b == 64 || b == 128 || b == 256; }
 
+// Rotation kinds (convrot_weights.flags, convrot_rotate_quantize flags): the
+// Sylvester blocks, or CONVROT_ROT_REGULAR, the H_4 Kronecker blocks, which
+// exist for b = 64 and 256 only.
+bool valid_rotation(uint32_t rot, int b)
+{
+    if (rot == 0) return true;
+    return rot == CONVROT_ROT_REGULAR && (b == 64 || b == 256);
+}
+
+bool is_regular(const convrot_weights *W) { return (W->flags & CONVROT_ROT_REGULAR) != 0; }
+
 // fp32 1/sqrt(b), rounded once from double.
 float inv_sqrt_block(int b) { return (float)(1.0 / std::sqrt((double)b)); }
 
@@ -80,6 +91,7 @@ int check_weights(const convrot_weights *W)
     if (!W->codes || !W->scale) return CONVROT_EINVAL;
     if (!aligned16(W->codes) || !aligned16(W->scale)) return CONVROT_EALIGN;
     int rc = check_linear_shape(W->N, W->K, W->block);
+    if (rc == CONVROT_OK && !valid_rotation((uint32_t)W->flags, W->block)) return CONVROT_ELAYOUT;
     return rc == CONVROT_EINVAL ? CONVROT_ELAYOUT : rc;
 }
 
@@ -194,6 +206,8 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
         return CONVROT_EUNSUPPORTED;
     const bool import = (w_dtype == CONVROT_I8);
     if (import != (src_scale != nullptr)) return CONVROT_EINVAL;
+    const uint32_t rot = (uint32_t)out->flags;
+    if (!valid_rotation(rot, block)) return CONVROT_EINVAL;
     if (!aligned16(W) || !aligned16(out->codes) || !aligned16(out->scale) ||
         (src_scale && !aligned16(src_scale)))
         return CONVROT_EALIGN;
@@ -217,8 +231,8 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
             rows = ws;
         }
         if (e == hipSuccess)
-            e = convrot::launch_rotquant(rows, in, N, K, K, block, inv_sqrt_block(block),
-                                         out->codes, out->scale, s);
+            e = convrot::launch_rotquant(rows, in, N, K, K, block, rot != 0,
+                                         inv_sqrt_block(block), out->codes, out->scale, s);
     }
     rc = hip_status(e);
     if (rc != CONVROT_OK) return rc;
@@ -227,7 +241,7 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
     out->N = N;
     out->K = K;
     out->block = block;
-    out->flags = 0;
+    out->flags = (int32_t)rot;
     return CONVROT_OK;
 }
 
@@ -253,6 +267,7 @@ int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
     float *sx = static_cast<float *>(c.take((size_t)M * 4u));
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W->K, W->K, W->block,
+                                            is_regular(W),
                                             inv_sqrt_block(W->block), qx, sx, s);
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qx, W->codes, sx, W->scale, bias, Y, out_kind(y_dtype), M,
@@ -267,7 +282,7 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
     int rc = check_weights(A);
     if (rc != CONVROT_OK) return rc;
     if ((rc = check_weights(B)) != CONVROT_OK) return rc;
-    if (A->N != B->K || A->block != B->block) return CONVROT_ELAYOUT;
+    if (A->N != B->K || A->block != B->block || A->flags != B->flags) return CONVROT_ELAYOUT;
     if ((rc = check_rows(M, A->K)) != CONVROT_OK) return rc;
     if ((rc = check_rows(M, A->N)) != CONVROT_OK) return rc;
     if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
@@ -288,8 +303,8 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float isb = inv_sqrt_block(A->block);
     hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, A->K, A->K, A->block,
-                                            isb, qx, sx, s);
-    if (convrot::lowrank_f1_fusable(r, A->block)) {
+                                            is_regular(A), isb, qx, sx, s);
+    if (!is_regular(A) && convrot::lowrank_f1_fusable(r, A->block)) {
         // a row of H fits one workgroup tile: factor 1 rotates and
         // requantises it in its epilogue, H never reaches memory
         if (e == hipSuccess)
@@ -300,8 +315,8 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
             e = convrot::launch_gemm_i8(qx, A->codes, sx, A->scale, nullptr, h,
                                         convrot::OutKind::BF16, M, r, A->K, s);
         if (e == hipSuccess)
-            e = convrot::launch_rotquant(h, convrot::InType::BF16, M, r, r, B->block, isb, qh,
-                                         sh, s);
+            e = convrot::launch_rotquant(h, convrot::InType::BF16, M, r, r, B->block,
+                                         is_regular(B), isb, qh, sh, s);
     }
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qh, B->codes, sh, B->scale, bias, Y, out_kind(y_dtype), M,
@@ -317,7 +332,8 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
     int rc = check_weights(W_up);
     if (rc != CONVROT_OK) return rc;
     if ((rc = check_weights(W_down)) != CONVROT_OK) return rc;
-    if (W_up->N != W_down->K || W_up->block != W_down->block) return CONVROT_ELAYOUT;
+    if (W_up->N != W_down->K || W_up->block != W_down->block || W_up->flags != W_down->flags)
+        return CONVROT_ELAYOUT;
     if ((rc = check_rows(M, W_up->K)) != CONVROT_OK) return rc;
     if ((rc = check_rows(M, W_up->N)) != CONVROT_OK) return rc;
     if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
@@ -339,13 +355,13 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float isb = inv_sqrt_block(W_up->block);
     hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W_up->K, W_up->K,
-                                            W_up->block, isb, qx, sx, s);
+                                            W_up->block, is_regular(W_up), isb, qx, sx, s);
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qx, W_up->codes, sx, W_up->scale, bias_up, g,
                                     convrot::OutKind::GELU_BF16, M, F, W_up->K, s);
     if (e == hipSuccess)
-        e = convrot::launch_rotquant(g, convrot::InType::BF16, M, F, F, W_down->block, isb, qg,
-                                     sg, s);
+        e = convrot::launch_rotquant(g, convrot::InType::BF16, M, F, F, W_down->block,
+                                     is_regular(W_down), isb, qg, sg, s);
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qg, W_down->codes, sg, W_down->scale, bias_down, Y,
                                     out_kind(y_dtype), M, W_down->N, F, s);
@@ -356,14 +372,16 @@ int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, in
                             uint32_t flags, int8_t *q, float *s_out, void *stream)
 {
     if (M < 0 || K <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
-    if (flags != 0) return CONVROT_EUNSUPPORTED;
+    if ((flags & ~CONVROT_ROT_REGULAR) != 0) return CONVROT_EUNSUPPORTED;
+    if (!valid_rotation(flags, block)) return CONVROT_EINVAL;
     if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
     if (K > kMaxK || convrot::padded_rows(M) * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!X || !q || !s_out) return CONVROT_EINVAL;
     if (!aligned16(X) || !aligned16(q) || !aligned16(s_out)) return CONVROT_EALIGN;
     const convrot::InType in = x_dtype == CONVROT_F32 ? convrot::InType::F32 : convrot::InType::BF16;
-    return hip_status(convrot::launch_rotquant(X, in, M, K, K, block, inv_sqrt_block(block), q,
+    return hip_status(convrot::launch_rotquant(X, in, M, K, K, block, flags != 0,
+                                               inv_sqrt_block(block), q,
                                                s_out, static_cast<hipStream_t>(stream)));
 }
 
@@ -409,7 +427,8 @@ int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int64_t M,
     if (rc != CONVROT_OK) return rc;
     if ((rc = check_rows(M, A->K)) != CONVROT_OK) return rc;
     if ((rc = check_rows(M, A->N)) != CONVROT_OK) return rc;
-    if (!convrot::lowrank_f1_fusable(A->N, A->block)) return CONVROT_EUNSUPPORTED;
+    if (is_regular(A) || !convrot::lowrank_f1_fusable(A->N, A->block))
+        return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!q_x || !s_x || !q_h || !s_h) return CONVROT_EINVAL;
     if (!aligned16(q_x) || !aligned16(s_x) || !aligned16(q_h) || !aligned16(s_h))

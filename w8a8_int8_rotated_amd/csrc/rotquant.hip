@@ -110,6 +110,106 @@ __device__ __forceinline__ void inlane_fwht8(float (&v)[8])
     }
 }
 
+// d = s + (s of the lane holding the partner chunk of stage STAGE), for the
+// regular rotation's pair sums.  fp32 addition is commutative, so both lanes
+// of a pair get the same bits.
+#define CR_DPP_ADD(CTRL, d, s)                                                \
+    asm volatile("s_nop 1\n\t"                                                \
+                 "v_add_f32_dpp %0, %8, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %1, %9, %9 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %2, %10, %10 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %3, %11, %11 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %4, %12, %12 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %5, %13, %13 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %6, %14, %14 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+                 "v_add_f32_dpp %7, %15, %15 " CTRL " row_mask:0xf bank_mask:0xf"   \
+                 : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]),         \
+                   "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7])          \
+                 : "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3]),                 \
+                   "v"(s[4]), "v"(s[5]), "v"(s[6]), "v"(s[7]))
+
+template <int STAGE>
+__device__ __forceinline__ void partner_add(float (&d)[8], const float (&s)[8])
+{
+    if constexpr (STAGE == 0) {
+        CR_DPP_ADD("quad_perm:[1,0,3,2]", d, s);
+    } else if constexpr (STAGE == 1) {
+        CR_DPP_ADD("quad_perm:[2,3,0,1]", d, s);
+    } else if constexpr (STAGE == 2) {
+        CR_DPP_ADD("row_half_mirror", d, s);
+    } else if constexpr (STAGE == 3) {
+        CR_DPP_ADD("row_mirror", d, s);
+    } else {
+        static_assert(STAGE == 4, "b <= 256");
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            d[j] = __fadd_rn(s[j], __int_as_float(__builtin_amdgcn_ds_swizzle(
+                                       __float_as_int(s[j]), 0x401F)));
+    }
+}
+
+// The regular rotation of one chunk: H_4 = J - 2I along every base-4 digit
+// of the in-block index, lowest digit first (the Rung-Omega README's
+// H_256 = H_4 (x) H_4 (x) H_4 (x) H_4, and its order-64 counterpart).  A group
+// (v0, v1, v2, v3) of one digit becomes S - 2 v_j with S = (v0 + v1) + (v2 +
+// v3).  Digit 0 lies inside the lane; digit 1 pairs elements e, e + 4 of the
+// lane and of the chunk across chunk bit 0; digit d >= 2 is chunk bits
+// 2d - 3 and 2d - 2, whose partner lanes are the Sylvester stages' DPP
+// patterns.  2 v_j is exact, so each output is one rounding of S - 2 v_j.
+template <int B>
+__device__ __forceinline__ void rotate_regular(float (&v)[8])
+{
+#pragma unroll
+    for (int g = 0; g < 8; g += 4) {
+        const float S = __fadd_rn(__fadd_rn(v[g], v[g + 1]), __fadd_rn(v[g + 2], v[g + 3]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[g + j] = __fsub_rn(S, 2.0f * v[g + j]);
+    }
+    {
+        float p[8], S[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __fadd_rn(v[i], v[i + 4]);
+            p[i + 4] = p[i];
+        }
+        partner_add<0>(S, p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __fsub_rn(S[j], 2.0f * v[j]);
+    }
+    {
+        float a[8], S[8];
+        partner_add<1>(a, v);
+        partner_add<2>(S, a);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __fsub_rn(S[j], 2.0f * v[j]);
+    }
+    if constexpr (B == 256) {
+        float a[8], S[8];
+        partner_add<3>(a, v);
+        partner_add<4>(S, a);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __fsub_rn(S[j], 2.0f * v[j]);
+    }
+}
+
+// Rotation kinds: 0 = Sylvester blocks (butterflies with the sign trick),
+// 1 = regular H_4 Kronecker blocks (B = 64 or 256).
+template <int B, int ROT, int NSTAGE>
+__device__ __forceinline__ void rotate_chunk(float (&v)[8], const float (&csign)[NSTAGE])
+{
+    if constexpr (ROT == 1) {
+        static_assert(B == 64 || B == 256, "regular blocks are powers of 4");
+        rotate_regular<B>(v);
+    } else {
+        inlane_fwht8(v);
+        cross_stage<0>(v, csign[0]);
+        cross_stage<1>(v, csign[1]);
+        cross_stage<2>(v, csign[2]);
+        if constexpr (NSTAGE > 3) cross_stage<3>(v, csign[3]);
+        if constexpr (NSTAGE > 4) cross_stage<4>(v, csign[4]);
+    }
+}
+
 // buffer resource word 3: raw (untyped) 32-bit data format, no swizzle
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -179,7 +279,7 @@ __device__ __forceinline__ float wave_max(float m)
 // IN: input type; B: Hadamard block; SPR: wave steps held per wave (an upper
 // bound: steps past the end of the row are skipped by a wave-uniform branch);
 // RPW: rows per wave (when WPR == 1); WPR: waves per row; NW: waves per WG.
-template <int IN, int B, int SPR, int RPW, int WPR, int NW>
+template <int IN, int B, int ROT, int SPR, int RPW, int WPR, int NW>
 __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
     const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
     int8_t *__restrict__ q, float *__restrict__ s)
@@ -243,19 +343,15 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
             if (t < my_steps) {
-                inlane_fwht8(v[r][t]);
-                cross_stage<0>(v[r][t], csign[0]);
-                cross_stage<1>(v[r][t], csign[1]);
-                cross_stage<2>(v[r][t], csign[2]);
-                if constexpr (NSTAGE > 3) cross_stage<3>(v[r][t], csign[3]);
-                if constexpr (NSTAGE > 4) cross_stage<4>(v[r][t], csign[4]);
+                rotate_chunk<B, ROT>(v[r][t], csign);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) m[r] = fmaxf(m[r], fabsf(v[r][t][j]));
             }
         }
     }
 
-    const bool negated = (__builtin_popcount(chunk) & 1) != 0;
+    // the Sylvester sign trick leaves the upper lanes' values negated
+    const bool negated = ROT == 0 && (__builtin_popcount(chunk) & 1) != 0;
 
     // ---- per row: amax, scale, codes ----
 #pragma unroll
@@ -284,13 +380,13 @@ __global__ __launch_bounds__(NW * 64) void rotquant_kernel(
     }
 }
 
-template <int IN, int B, int SPR, int RPW, int WPR, int NW>
+template <int IN, int B, int ROT, int SPR, int RPW, int WPR, int NW>
 hipError_t launch_cfg(const void *src, int64_t M, int64_t K, int64_t ld,
                       float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
 {
     constexpr int rows_per_wg = (NW / WPR) * RPW;
     const int64_t grid = (M + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL((rotquant_kernel<IN, B, SPR, RPW, WPR, NW>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((rotquant_kernel<IN, B, ROT, SPR, RPW, WPR, NW>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, src, M, (int)K, ld, inv_sqrt_b, q, s);
     return hipGetLastError();
 }
@@ -299,7 +395,7 @@ hipError_t launch_cfg(const void *src, int64_t M, int64_t K, int64_t ld,
 // workgroup per CU walks row groups, and each wave loads the raw input of
 // its next group before rotating the current one, so memory and the rotation
 // overlap inside the wave as well as across waves.
-template <int IN, int B, int SPR, int WPR, int NW>
+template <int IN, int B, int ROT, int SPR, int WPR, int NW>
 __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
     const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
     int8_t *__restrict__ q, float *__restrict__ s)
@@ -328,7 +424,8 @@ __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
 #pragma unroll
     for (int k = 0; k < NSTAGE; ++k)
         csign[k] = ((chunk >> k) & 1) ? -1.0f : 1.0f;
-    const bool negated = (__builtin_popcount(chunk) & 1) != 0;
+    // the Sylvester sign trick leaves the upper lanes' values negated
+    const bool negated = ROT == 0 && (__builtin_popcount(chunk) & 1) != 0;
 
     // Every memory instruction is unconditional (steps past the row end fall
     // outside the buffer range: loads read zero, stores are dropped), so the
@@ -391,12 +488,7 @@ __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
             if (t < my_steps) {
-                inlane_fwht8(v[t]);
-                cross_stage<0>(v[t], csign[0]);
-                cross_stage<1>(v[t], csign[1]);
-                cross_stage<2>(v[t], csign[2]);
-                if constexpr (NSTAGE > 3) cross_stage<3>(v[t], csign[3]);
-                if constexpr (NSTAGE > 4) cross_stage<4>(v[t], csign[4]);
+                rotate_chunk<B, ROT>(v[t], csign);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[t][j]));
             }
@@ -428,14 +520,14 @@ __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
     }
 }
 
-template <int IN, int B, int SPR, int WPR, int NW>
+template <int IN, int B, int ROT, int SPR, int WPR, int NW>
 hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
                          float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
 {
     constexpr int rows_per_wg = NW / WPR;
     const int64_t groups = (M + rows_per_wg - 1) / rows_per_wg;
     const int64_t grid = std::min<int64_t>(groups, device_cu_count());
-    hipLaunchKernelGGL((rotquant_stream_kernel<IN, B, SPR, WPR, NW>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((rotquant_stream_kernel<IN, B, ROT, SPR, WPR, NW>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, src, M, (int)K, ld, inv_sqrt_b, q, s);
     return hipGetLastError();
 }
@@ -444,29 +536,36 @@ hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
 // per wave when they are short.  Longer rows are split over 2..16 waves of
 // at most 6 steps each and streamed by one 16-wave workgroup per CU; beyond
 // 96 steps the one-shot kernel holds 8 steps per wave.
-template <int IN, int B>
+template <int IN, int B, int ROT>
 hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
 {
     const int64_t steps = (K + kStep - 1) / kStep;
-    if (steps <= 1) return launch_cfg<IN, B, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 2) return launch_cfg<IN, B, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 4) return launch_cfg<IN, B, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 12) return launch_stream<IN, B, 6, 2, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 24) return launch_stream<IN, B, 6, 4, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 48) return launch_stream<IN, B, 6, 8, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 96) return launch_stream<IN, B, 6, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    return launch_cfg<IN, B, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 1) return launch_cfg<IN, B, ROT, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 2) return launch_cfg<IN, B, ROT, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 4) return launch_cfg<IN, B, ROT, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 12) return launch_stream<IN, B, ROT, 6, 2, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 24) return launch_stream<IN, B, ROT, 6, 4, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 48) return launch_stream<IN, B, ROT, 6, 8, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 96) return launch_stream<IN, B, ROT, 6, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    return launch_cfg<IN, B, ROT, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
 }
 
 template <int IN>
 hipError_t launch_in(const void *src, int64_t M, int64_t K, int64_t ld, int block,
-                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+                     bool regular, float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
 {
+    if (regular) {
+        switch (block) {
+        case 64: return launch_b<IN, 64, 1>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+        case 256: return launch_b<IN, 256, 1>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (block) {
-    case 64: return launch_b<IN, 64>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    case 128: return launch_b<IN, 128>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    case 256: return launch_b<IN, 256>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    case 64: return launch_b<IN, 64, 0>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    case 128: return launch_b<IN, 128, 0>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    case 256: return launch_b<IN, 256, 0>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -527,13 +626,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ sr
 } // namespace
 
 hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
-                           int64_t ld, int block, float inv_sqrt_b, int8_t *q,
+                           int64_t ld, int block, bool regular, float inv_sqrt_b, int8_t *q,
                            float *s, hipStream_t stream)
 {
     if (M == 0) return hipSuccess;
     if (in == InType::BF16)
-        return launch_in<int(InType::BF16)>(src, M, K, ld, block, inv_sqrt_b, q, s, stream);
-    return launch_in<int(InType::F32)>(src, M, K, ld, block, inv_sqrt_b, q, s, stream);
+        return launch_in<int(InType::BF16)>(src, M, K, ld, block, regular, inv_sqrt_b, q, s,
+                                            stream);
+    return launch_in<int(InType::F32)>(src, M, K, ld, block, regular, inv_sqrt_b, q, s, stream);
 }
 
 hipError_t launch_tile_codes(const int8_t *src, bool transposed, int8_t *dst, int64_t R,
