@@ -320,6 +320,31 @@ def test_lowrank_small_full(cr):
     assert mism == 0
 
 
+@pytest.mark.parametrize("r,block", [(192, 64), (64, 64), (320, 128)])
+def test_lowrank_rank_padding(cr, r, block):
+    """Ranks that are multiples of 64 but not of 128 (the checkpoint's own
+    padding unit) are padded with zero rows of A and zero columns of B.  When
+    b divides r the result equals the unpadded chain bit for bit; otherwise it
+    equals the chain on the explicitly padded factors."""
+    announce(f"lowrank rank padding r={r} b={block}")
+    w = wl.scaled("lowrank_38656", M=300, K=1024, N=272, rank=r, block=block)
+    x, A, B = w.activations(), w.weight("w"), w.weight("w2")
+    pa, pb = cr.convrot_lowrank_prepare(to_dev(A), to_dev(B), block)
+    rp = cr.lowrank_padded_rank(r, block)
+    assert pa.N == rp and pb.K == rp
+    y = cr.lowrank_convrot_forward(to_dev_bf16(x), pa, pb)
+    if r % block == 0:
+        qa, sa = oracle.prepare_weights(A, block)
+        qb, sb = oracle.prepare_weights(B, block)
+    else:
+        Ap = np.concatenate([A, np.zeros((rp - r, A.shape[1]), A.dtype)])
+        Bp = np.concatenate([B, np.zeros((B.shape[0], rp - r), B.dtype)], axis=1)
+        qa, sa = oracle.prepare_weights(Ap, block)
+        qb, sb = oracle.prepare_weights(Bp, block)
+    y_ref = oracle.lowrank_forward(x, qa, sa, qb, sb, block, out="bf16")
+    assert assert_output_parity(bf16_bits(y), y_ref, "bf16", "rank padding") == 0
+
+
 @pytest.mark.parametrize("M,K,r,block", [
     (520, 1024, 256, 128),      # ragged last tile, two waves idle
     (1000, 640, 512, 64),       # b = 64: two rotation blocks per wave, S = 2 stages

@@ -217,6 +217,33 @@ def convrot_linear_prepare_weights(W: torch.Tensor, block: int, layout: int = OU
     return pw
 
 
+def lowrank_padded_rank(r: int, block: int) -> int:
+    """The rank a low-rank pair is stored with: r rounded up to a multiple of
+    128 (the contraction's K granularity) and of the Hadamard block b."""
+    m = 256 if block == 256 else 128
+    return (r + m - 1) // m * m
+
+
+def convrot_lowrank_prepare(A: torch.Tensor, B: torch.Tensor, block: int, stream=None,
+                            rotation: str = "sylvester"):
+    """Prepare a low-rank pair W ~ B . A, A [r, K] and B [N, r] (output-major),
+    padding the rank with zero rows of A and zero columns of B to
+    lowrank_padded_rank(r, block), as the checkpoint loader pads ranks to a
+    multiple of 64.  The padding leaves the product B . A unchanged; when r is
+    already a multiple of b, the rotated and requantised intermediate of the
+    real rank positions is unchanged too."""
+    if A.dim() != 2 or B.dim() != 2 or B.shape[1] != A.shape[0]:
+        raise ValueError("A must be [r, K] and B [N, r]")
+    r = A.shape[0]
+    rp = lowrank_padded_rank(r, block)
+    if rp != r:
+        A = torch.cat([A, A.new_zeros((rp - r, A.shape[1]))], dim=0)
+        B = torch.cat([B, B.new_zeros((B.shape[0], rp - r))], dim=1)
+    pa = convrot_linear_prepare_weights(A.contiguous(), block, stream=stream, rotation=rotation)
+    pb = convrot_linear_prepare_weights(B.contiguous(), block, stream=stream, rotation=rotation)
+    return pa, pb
+
+
 # ----------------------------------------------------------- forward ----
 
 def convrot_linear_forward(X: torch.Tensor, W: PreparedWeights, bias=None,
