@@ -345,10 +345,45 @@ def main():
         "cpu_baseline": None,
     }
 
+    if w.kind == "lowrank":
+        result["comparison"] = bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream,
+                                                       ms_per_step)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, w, host, Y)
 
     print(json.dumps(result), flush=True)
+
+
+def bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream, int8_ms):
+    """The same low-rank layer with bf16 factors and no rotation or
+    quantisation (the variant where the low-rank linears stay bf16), timed
+    the same way outside the step, for comparison only."""
+    import numpy as np
+    from w8a8_int8_rotated_amd import workloads as wl
+    to_b = lambda a: torch.from_numpy(wl.f32_to_bf16_bits(a).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    X = torch.from_numpy(host["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    A, B = to_b(host["A"]), to_b(host["B"])
+    Y = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cr.lowrank_bf16_workspace_bytes(w.M, w.rank), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: cr.lowrank_bf16_forward(X, A, B, out=Y, workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        run()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = 2.0 * w.M * w.rank * (w.K + w.N)
+    log(f"bf16 low-rank comparison: {ms:.4f} ms, {flops / ms / 1e9:.1f} TFLOP/s")
+    return {"variant": "bf16 factors, no rotation or quantisation", "ms_per_step": round(ms, 5),
+            "tflops_bf16": round(flops / ms / 1e9, 2),
+            "int8_speedup": round(ms / int8_ms, 3)}
 
 
 def cpu_baseline(args, w, host, Y):

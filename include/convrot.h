@@ -236,6 +236,26 @@ CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weig
                         size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
+/* comparison variant (not the W8A8 path)                              */
+/* ------------------------------------------------------------------ */
+
+/* Low-rank linear whose factors stay bf16: no rotation, no quantisation, as
+ * in the ComfyUI INT8 convrot copies where the low-rank linears stay bf16
+ * (HyperFlow H3 Flash card, "INT8 convrot in ComfyUI").  Kept to compare the
+ * W8A8 low-rank path against.  h = bf16(X . A^T) and Y = bf16(h . B^T + bias),
+ * each product accumulated in fp32 on the matrix cores, the bias added in
+ * fp32, bf16 by round to nearest even.
+ *   X bf16 [M, K], A bf16 [r, K], B bf16 [N, r], all row-major device
+ *   pointers; bias F32 [N] or NULL; Y bf16 [M, N].
+ *   ws: device workspace of lowrank_bf16_workspace_bytes(M, r) bytes (h).
+ * K % 64 == 0, r % 64 == 0 (the checkpoint's rank padding), N % 16 == 0,
+ * K, r <= 65536 and every matrix under 2^31 bytes (EUNSUPPORTED otherwise). */
+CONVROT_API size_t lowrank_bf16_workspace_bytes(int64_t M, int64_t r);
+CONVROT_API int lowrank_bf16_forward(const void *X, int64_t M, int64_t K, const void *A,
+                         int64_t r, const void *B, int64_t N, const float *bias,
+                         void *Y, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* test hooks: the stages of the forward path, exported for parity     */
 /* tests.  Same validation and error behaviour as the entry points.    */
 /* ------------------------------------------------------------------ */

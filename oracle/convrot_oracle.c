@@ -44,6 +44,10 @@
  *     every row sums to 2), applied along the base-4 digits of the index in
  *     ascending order; a group (v0, v1, v2, v3) becomes S - 2 v_j with
  *     S = (v0 + v1) + (v2 + v3), in fp32.  The scale folds 1/sqrt(b) as in R1.
+ *  R9 bf16 low-rank comparison variant (the HyperFlow H3 Flash card, "INT8
+ *     convrot in ComfyUI": there the low-rank linears stay bf16): each
+ *     product is the exact sum over K rounded once to fp32, the bias added in
+ *     fp32, then bf16 by round to nearest even; no rotation, no quantisation.
  *
  * Precision: every step that decides an INT8 code is evaluated in fp32 (the
  * precision the GPU kernels take those decisions in), with the butterfly order
@@ -470,4 +474,50 @@ int oracle_mlp_forward(const uint16_t *X, int64_t M, int64_t K, int b,
 {
     return oracle_mlp_forward_rot(X, M, K, b, OR_ROT_SYLVESTER, qu, su, F, bias_up, qd, sd, N,
                                   bias_down, out_dtype, out, u_out, g_out);
+}
+
+/* ------------------------------------------------------------------ */
+/* R9: the bf16 low-rank comparison variant                            */
+/* ------------------------------------------------------------------ */
+
+/* out[m, n] = bf16(fp32(sum_k x[m, k] w[n, k]) (+ bias[n])) for bf16 x [M, K]
+ * and w [N, K].  The sum is taken in fp64: a product of two bf16 values is
+ * exact there, and so are sums of them over the exponent ranges used. */
+static void bf16_linear(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N,
+                        int64_t K, const float *bias, uint16_t *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (double)oracle_bf16_to_f32(x[m * K + k]) *
+                       (double)oracle_bf16_to_f32(w[n * K + k]);
+            float y = (float)acc;
+            if (bias)
+                y += bias[n];
+            out[m * N + n] = oracle_f32_to_bf16(y);
+        }
+    }
+}
+
+/* h = bf16(X . A^T) [M, r], then y = bf16(h . B^T + bias) [M, N]; h_out, when
+ * not NULL, receives h. */
+int oracle_lowrank_bf16_forward(const uint16_t *X, int64_t M, int64_t K, const uint16_t *A,
+                                int64_t r, const uint16_t *B, int64_t N, const float *bias,
+                                uint16_t *y, uint16_t *h_out)
+{
+    if (M < 0 || K <= 0 || r <= 0 || N <= 0)
+        return OR_EINVAL;
+    if (M == 0)
+        return OR_OK;
+    uint16_t *h = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)M * (size_t)r);
+    if (!h)
+        return OR_EINVAL;
+    bf16_linear(X, A, M, r, K, NULL, h);
+    bf16_linear(h, B, M, N, r, bias, y);
+    if (h_out)
+        memcpy(h_out, h, sizeof(uint16_t) * (size_t)M * (size_t)r);
+    free(h);
+    return OR_OK;
 }

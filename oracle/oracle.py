@@ -77,6 +77,8 @@ def open_library(path):
         "oracle_lowrank_forward_rot": (
             _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
                      _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p]),
+        "oracle_lowrank_bf16_forward": (
+            _c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p]),
         "oracle_mlp_forward_rot": (
             _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
                      _c_p, _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_p]),
@@ -340,8 +342,27 @@ def mlp_forward(X_bf16, qu, su, qd, sd, b: int, bias_up=None, bias_down=None,
     return (y, u, g) if return_intermediates else y
 
 
+def lowrank_bf16_forward(X_bf16, A_bf16, B_bf16, bias=None, return_h: bool = False):
+    """R9, the bf16 low-rank comparison variant: h = bf16(X . A^T),
+    y = bf16(h . B^T + bias), each sum exact then rounded to fp32."""
+    lib = _load()
+    X = _c(X_bf16, np.uint16)
+    A = _c(A_bf16, np.uint16)
+    B = _c(B_bf16, np.uint16)
+    bias = None if bias is None else _c(bias, np.float32)
+    M, K = X.shape
+    r, N = A.shape[0], B.shape[0]
+    assert A.shape[1] == K and B.shape[1] == r
+    y = np.empty((M, N), dtype=np.uint16)
+    h = np.empty((M, r), dtype=np.uint16)
+    _check(lib.oracle_lowrank_bf16_forward(_ptr(X), M, K, _ptr(A), r, _ptr(B), N, _ptr(bias),
+                                           _ptr(y), _ptr(h)), "lowrank_bf16_forward")
+    return (y, h) if return_h else y
+
+
 __all__ = [
     "num_threads", "bf16_to_f32", "f32_to_bf16", "inv_sqrt_b", "fwht", "rowquant",
     "rotate_quantize", "prepare_weights", "gemm_i32", "dequant",
     "linear_forward", "lowrank_forward", "gelu_f64", "gelu_bf16", "mlp_forward",
+    "lowrank_bf16_forward",
 ]

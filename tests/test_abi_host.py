@@ -217,6 +217,22 @@ def test_rotation_kind_validation(cr):
                                               ctypes.byref(d), None, 0, None) == cr.EINVAL
 
 
+def test_lowrank_bf16_validation(cr):
+    lib = cr.library()
+    f = lambda M=8, K=512, r=64, N=256, X=FAKE, ws=FAKE, wsb=1 << 20: lib.lowrank_bf16_forward(
+        X, M, K, FAKE, r, FAKE, N, None, FAKE, ws, wsb, None)
+    assert f(M=0, X=None, ws=None, wsb=0) == cr.OK
+    assert f(M=-1) == cr.EINVAL
+    assert f(K=500) == cr.EUNSUPPORTED
+    assert f(r=96) == cr.EUNSUPPORTED
+    assert f(N=250) == cr.EUNSUPPORTED
+    assert f(X=None) == cr.EINVAL
+    assert f(X=FAKE_ODD) == cr.EALIGN
+    assert f(ws=None) == cr.EWORKSPACE
+    assert f(wsb=100) == cr.EWORKSPACE
+    assert lib.lowrank_bf16_workspace_bytes(8, 64) >= 8 * 64 * 2
+
+
 def _flag(d, flags):
     d.flags = flags
     return d

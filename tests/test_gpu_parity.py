@@ -387,6 +387,49 @@ def _check_factor1(cr, M, K, r, block):
     assert np.array_equal(sh.view(np.uint32), sh_ref.view(np.uint32))
 
 
+# ------------------------------------- bf16 low-rank comparison variant ----
+
+def _bf16_lowrank_bound(x, A, B, h_ref, y_ref, bias):
+    """Elementwise bound for the bf16 variant against its oracle (R9): the
+    oracle rounds the exact sum once to fp32, the matrix cores accumulate in
+    fp32 in their own order (at most K * 2^-24 of sum |x a|), and each bf16
+    rounding can then differ by one bf16 unit (2^-8 relative).  An h that
+    differs feeds into y through |B|."""
+    f = lambda u: wl.bf16_bits_to_f32(u).astype(np.float64)
+    K, r = A.shape[1], A.shape[0]
+    eh = 2.0 ** -8 * np.abs(f(h_ref)) + 2 * K * 2.0 ** -24 * (np.abs(f(x)) @ np.abs(f(A)).T)
+    ey = (2.0 ** -7 * np.abs(f(y_ref)) + eh @ np.abs(f(B)).T
+          + 2 * r * 2.0 ** -24 * (np.abs(f(h_ref)) @ np.abs(f(B)).T))
+    return ey
+
+
+@pytest.mark.parametrize("M,K,r,N,with_bias", [(520, 1024, 192, 784, True),
+                                               (1, 512, 64, 256, False),
+                                               (4100, 2048, 512, 1024, True)])
+def test_lowrank_bf16_variant(cr, M, K, r, N, with_bias):
+    """The bf16 low-rank comparison variant (no rotation, no quantisation)
+    within the derived elementwise bound of its oracle; most outputs equal."""
+    announce(f"lowrank bf16 variant M={M} K={K} r={r} N={N}")
+    rng = np.random.default_rng(M + r)
+    to_b = lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))
+    x = to_b(rng.standard_normal((M, K)))
+    A = to_b(rng.standard_normal((r, K)) * 0.02)
+    B = to_b(rng.standard_normal((N, r)) * 0.02)
+    bias = rng.normal(0, 0.01, N).astype(np.float32) if with_bias else None
+    y = cr.lowrank_bf16_forward(to_dev_bf16(x), to_dev_bf16(A), to_dev_bf16(B),
+                                bias=None if bias is None else to_dev(bias))
+    y_ref, h_ref = oracle.lowrank_bf16_forward(x, A, B, bias, return_h=True)
+    yg = bf16_bits(y)
+    f = lambda u: wl.bf16_bits_to_f32(u).astype(np.float64)
+    err = np.abs(f(yg) - f(y_ref))
+    bound = _bf16_lowrank_bound(x, A, B, h_ref, y_ref, bias)
+    same = float(np.mean(yg == y_ref))
+    print(f"[parity] bf16 low-rank: {100 * same:.2f}% equal, worst err/bound "
+          f"{float(np.max(err / np.maximum(bound, 1e-30))):.3f}", flush=True)
+    assert np.all(err <= bound)
+    assert same > 0.9
+
+
 # ---------------------------------------------------------------- MLP ----
 
 def test_gelu_exhaustive(cr):

@@ -465,6 +465,26 @@ def test_lowrank_rejects_bad_rank():
 
 # ----------------------------------------------------------------- GELU ----
 
+def test_lowrank_bf16_variant_vs_numpy():
+    """R9: the bf16 low-rank variant equals numpy's fp64 matmul of the same
+    bf16 values, rounded to fp32 (plus bias) and then to bf16 by the
+    workloads module's independent RNE narrowing; products of bf16 values and
+    their sums are exact in fp64 at these exponent ranges."""
+    rng = np.random.default_rng(17)
+    M, K, r, N = 7, 256, 64, 48
+    to_b = lambda a: wl.f32_to_bf16_bits(a.astype(np.float32))
+    X = to_b(rng.standard_normal((M, K)))
+    A = to_b(rng.standard_normal((r, K)) * 0.05)
+    B = to_b(rng.standard_normal((N, r)) * 0.05)
+    bias = rng.normal(0, 0.01, N).astype(np.float32)
+    y, h = oracle.lowrank_bf16_forward(X, A, B, bias, return_h=True)
+    f = lambda u: wl.bf16_bits_to_f32(u).astype(np.float64)
+    h_ref = to_b((f(X) @ f(A).T).astype(np.float32))
+    assert np.array_equal(h, h_ref)
+    y_ref = to_b((f(h_ref) @ f(B).T).astype(np.float32) + bias)
+    assert np.array_equal(y, y_ref)
+
+
 def test_gelu_values():
     assert oracle.gelu_f64(0.0) == 0.0
     for z in (-3.0, -1.0, -0.25, 0.5, 1.0, 2.0, 7.0):

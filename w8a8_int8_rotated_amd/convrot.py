@@ -68,6 +68,10 @@ _SIGNATURES = {
     "convrot_gemm_dequant": (
         _c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_int, ctypes.c_uint32, _c_p]),
     "convrot_lowrank_factor1": (_c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_p]),
+    "lowrank_bf16_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "lowrank_bf16_forward": (
+        _c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
+                 ctypes.c_size_t, _c_p]),
     "convrot_gelu_bf16": (_c_int, [_c_p, _c_i64, _c_p, _c_p]),
 }
 
@@ -155,6 +159,10 @@ def lowrank_convrot_workspace_bytes(M, K, r, N, block) -> int:
 
 def convrot_mlp_workspace_bytes(M, K, F, N, block) -> int:
     return library().convrot_mlp_workspace_bytes(M, K, F, N, block)
+
+
+def lowrank_bf16_workspace_bytes(M, r) -> int:
+    return library().lowrank_bf16_workspace_bytes(M, r)
 
 
 # ----------------------------------------------------------- weights ----
@@ -291,6 +299,29 @@ def convrot_mlp_forward(X: torch.Tensor, W_up: PreparedWeights, W_down: Prepared
                                  _ptr(bias_down), _ptr(out), _dtype_tag(out.dtype), _ptr(ws),
                                  ws.numel() if ws is not None else 0, _stream(stream))
     _check("convrot_mlp_forward", rc)
+    return out
+
+
+def lowrank_bf16_forward(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bias=None,
+                         out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Comparison variant: bf16(bf16(X . A^T) . B^T + bias), bf16 factors
+    A [r, K] and B [N, r], no rotation or quantisation."""
+    lib = library()
+    for t in (X, A, B):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("X, A and B must be contiguous bf16")
+    M, K = X.shape
+    r, N = A.shape[0], B.shape[0]
+    if A.shape[1] != K or B.shape[1] != r:
+        raise ValueError("A must be [r, K] and B [N, r]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    wsb = lib.lowrank_bf16_workspace_bytes(M, r)
+    ws = _workspace(wsb, X.device, workspace)
+    rc = lib.lowrank_bf16_forward(_ptr(X), M, K, _ptr(A), r, _ptr(B), N, _ptr(bias), _ptr(out),
+                                  _ptr(ws), ws.numel() if ws is not None else 0,
+                                  _stream(stream))
+    _check("lowrank_bf16_forward", rc)
     return out
 
 

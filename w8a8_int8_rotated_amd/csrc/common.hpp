@@ -55,7 +55,9 @@ enum class InType { F32 = 0, BF16 = 1 };
 
 // Compute units of the current device (queried once; 256 if the query fails).
 int device_cu_count();
-enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3 };
+// BF16_MM: not an INT8 path -- bf16 x bf16 operands, row-major, fp32
+// accumulation, y = bf16(acc (+ bias)); used by the bf16 low-rank variant.
+enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3, BF16_MM = 4 };
 
 // Rotate (blockwise Sylvester FWHT, or with `regular` the H_4 = J - 2I
 // Kronecker blocks for block 64 or 256) + rowwise INT8 quantise.  src rows
@@ -86,6 +88,8 @@ hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream);
 
 // acc/Y[M, N] = epilogue(qx[M, K] . qw[N, K]^T), both code matrices K-tiled.
+// For OutKind::BF16_MM, qx and qw are row-major bf16 matrices, K counts
+// their row bytes (2 x elements), and sx, sw are unused.
 hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
                           const float *sw, const float *bias, void *Y,
                           OutKind out, int64_t M, int64_t N, int64_t K,

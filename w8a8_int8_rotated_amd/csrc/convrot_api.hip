@@ -368,6 +368,40 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
     return hip_status(e);
 }
 
+size_t lowrank_bf16_workspace_bytes(int64_t M, int64_t r)
+{
+    if (M < 0 || r <= 0) return 0;
+    return round_up((size_t)M * (size_t)r * 2u, kAlign);
+}
+
+int lowrank_bf16_forward(const void *X, int64_t M, int64_t K, const void *A, int64_t r,
+                         const void *B, int64_t N, const float *bias, void *Y, void *ws,
+                         size_t ws_bytes, void *stream)
+{
+    if (M < 0 || K <= 0 || r <= 0 || N <= 0) return CONVROT_EINVAL;
+    if (K % 64 != 0 || r % 64 != 0 || N % 16 != 0 || K > kMaxK || r > kMaxK)
+        return CONVROT_EUNSUPPORTED;
+    if (M * 2 * K >= kI32Bound || M * 2 * r >= kI32Bound || N * 2 * K >= kI32Bound ||
+        N * 2 * r >= kI32Bound)
+        return CONVROT_EUNSUPPORTED;
+    if (M == 0) return CONVROT_OK;
+    if (!X || !A || !B || !Y) return CONVROT_EINVAL;
+    if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) ||
+        (bias && !aligned16(bias)) || (ws && !aligned16(ws)))
+        return CONVROT_EALIGN;
+    if (!ws || ws_bytes < lowrank_bf16_workspace_bytes(M, r)) return CONVROT_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the operands are bf16: the contraction counts bytes along K
+    hipError_t e = convrot::launch_gemm_i8(static_cast<const int8_t *>(X),
+                                           static_cast<const int8_t *>(A), nullptr, nullptr,
+                                           nullptr, ws, convrot::OutKind::BF16_MM, M, r, 2 * K, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(static_cast<const int8_t *>(ws),
+                                    static_cast<const int8_t *>(B), nullptr, nullptr, bias, Y,
+                                    convrot::OutKind::BF16_MM, M, N, 2 * r, s);
+    return hip_status(e);
+}
+
 int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, int block,
                             uint32_t flags, int8_t *q, float *s_out, void *stream)
 {

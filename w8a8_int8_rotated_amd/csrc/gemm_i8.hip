@@ -130,10 +130,16 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
 // Dequantise and store a wave's 128 x 128 block.  FULL: the tile lies inside
 // [M, N], so no per-lane bounds checks are needed.
 // fp32 value of one output: ((float)acc * s_x) * s_w (+ bias).
+// For the bf16 x bf16 product (OutKind::BF16_MM) the accumulator already
+// holds the fp32 sum: y = acc (+ bias).
 template <int OUT, bool HAS_BIAS>
 __device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float bn)
 {
-    float f = __fmul_rn(__fmul_rn((float)acc, sxm), swn);
+    float f;
+    if constexpr (OUT == int(OutKind::BF16_MM))
+        f = __int_as_float(acc);
+    else
+        f = __fmul_rn(__fmul_rn((float)acc, sxm), swn);
     if constexpr (HAS_BIAS) f = __fadd_rn(f, bn);
     return f;
 }
@@ -350,6 +356,7 @@ struct TileSrc {
     __amdgpu_buffer_rsrc_t w, x;
 };
 
+template <bool RM = false>
 __device__ __forceinline__ TileSrc tile_src(const int8_t *qw, const int8_t *qx, int m0, int n0,
                                             int M, int N, int K)
 {
@@ -359,19 +366,28 @@ __device__ __forceinline__ TileSrc tile_src(const int8_t *qw, const int8_t *qx, 
     // rows up to the 16-row padding: the last block's tiles hold real rows
     // throughout its K range
     t.x = __builtin_amdgcn_make_buffer_rsrc((void *)(qx + (int64_t)m0 * K), (short)0,
-                                            (int)(padded_rows(M) - m0) * K, kRsrcWord3);
+                                            (int)((RM ? M : padded_rows(M)) - m0) * K,
+                                            kRsrcWord3);
     return t;
 }
 
 // Copy j of wave w moves rows [(n w + j) 16, +16) of an operand tile of 64 n
 // rows (n = 4 for the 256-row weight tile, TJ for the activation tile): the
 // 1 KiB tile of that row block, lane i its i-th 16 bytes.
-template <int NC>
+// RM: row-major operands (the bf16 product): lane i takes row + i/4 and the
+// 16-byte chunk (i & 3) ^ f(row) of it, so the LDS tile has the same layout.
+template <bool RM = false, int NC>
 __device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t (&voff)[NC])
 {
 #pragma unroll
-    for (int j = 0; j < NC; ++j)
-        voff[j] = (uint32_t)((wave * NC + j) * 16) * (uint32_t)K + (uint32_t)lane * 16u;
+    for (int j = 0; j < NC; ++j) {
+        if constexpr (RM) {
+            const int r = (wave * NC + j) * 16 + (lane >> 2);
+            voff[j] = (uint32_t)r * (uint32_t)K + (((lane & 3) ^ swz(r)) << 4);
+        } else {
+            voff[j] = (uint32_t)((wave * NC + j) * 16) * (uint32_t)K + (uint32_t)lane * 16u;
+        }
+    }
 }
 
 // Half H of K-tile `k` of the copy stream into one stage: the wave's weight
@@ -380,7 +396,7 @@ __device__ __forceinline__ void lane_offsets(int K, int wave, int lane, uint32_t
 // Below nk the K-tile belongs to the current tile, from nk on to the next one
 // (the last tile of a workgroup re-reads its own first K-tiles, which no one
 // consumes).
-template <int CW, int CX, int H>
+template <int CW, int CX, int H, bool RM = false>
 __device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nxt,
                                            const uint32_t *voffw, const uint32_t *voffx, int k,
                                            int nk, int wave, int8_t *__restrict__ dst_w,
@@ -388,7 +404,8 @@ __device__ __forceinline__ void issue_half(const TileSrc &cur, const TileSrc &nx
 {
     const bool next = k >= nk;
     const __amdgpu_buffer_rsrc_t rw = next ? nxt.w : cur.w, rx = next ? nxt.x : cur.x;
-    const int soff = (next ? k - nk : k) * 1024;   // K-tile k of a row block
+    // K-tile k: of a 16-row block (K-tiled), or 64 bytes along the row
+    const int soff = (next ? k - nk : k) * (RM ? kBK : 1024);
 #pragma unroll
     for (int j = H * CW / 2; j < (H + 1) * CW / 2; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -413,15 +430,27 @@ __device__ __forceinline__ void read_frags(const int8_t *__restrict__ sw_,
     }
 }
 
-template <int TJ>
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// BF: the operands are bf16 (8 per 16-byte fragment) and the accumulators
+// hold fp32 bits (v_mfma_f32_32x32x16_bf16, the same fragment shapes).
+template <int TJ, bool BF = false>
 __device__ __forceinline__ void mfma_block(v16i (&acc)[4][TJ], const v4i (&a)[4],
                                            const v4i (&b)[TJ])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; ++j) {
+            if constexpr (BF)
+                acc[i][j] = __builtin_bit_cast(
+                    v16i, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                              __builtin_bit_cast(v8bf, a[i]), __builtin_bit_cast(v8bf, b[j]),
+                              __builtin_bit_cast(v16f, acc[i][j]), 0, 0, 0));
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
 }
 
 template <int S, int I>
@@ -463,7 +492,7 @@ __device__ __forceinline__ void wait_vmcnt_either(bool second)
 // before a wait (vmcnt retires in order) has to cover them.
 // On exit: K-tiles 0 .. S-2 of the next tile are in flight.  Requires
 // nk % S == 0.
-template <int TJ, int CW, int CX, int S, int EPI, bool EARLY>
+template <int TJ, int CW, int CX, int S, int EPI, bool EARLY, bool BF = false>
 __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restrict__ w1,
                                        int8_t *__restrict__ w2, int8_t *__restrict__ w3,
                                        int8_t *__restrict__ x0, int8_t *__restrict__ x1,
@@ -484,23 +513,23 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
     int8_t *const wl = pick<S, S - 1>(w0, w1, w2, w3), *const xl = pick<S, S - 1>(x0, x1, x2, x3);
 
     if (first) {
-        issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
-        issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
+        issue_half<CW, CX, 0, BF>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
+        issue_half<CW, CX, 1, BF>(cur, nxt, voffw, voffx, 0, nk, wave, w0, x0);
         if constexpr (S == 4) {
-            issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
-            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
-            issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
-            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
+            issue_half<CW, CX, 0, BF>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
+            issue_half<CW, CX, 1, BF>(cur, nxt, voffw, voffx, 1, nk, wave, w1, x1);
+            issue_half<CW, CX, 0, BF>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
+            issue_half<CW, CX, 1, BF>(cur, nxt, voffw, voffx, 2, nk, wave, w2, x2);
         }
     }
     if constexpr (EARLY) {
         if (first) {
-            issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
-            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+            issue_half<CW, CX, 0, BF>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+            issue_half<CW, CX, 1, BF>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
         }
         wait_vmcnt_either<(S - 1) * C + EPI, (S - 1) * C>(first);
     } else {
-        issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
+        issue_half<CW, CX, 0, BF>(cur, nxt, voffw, voffx, S - 1, nk, wave, wl, xl);
         wait_vmcnt_either<(S - 2) * C + CH0 + EPI, (S - 2) * C + CH0>(first);
     }
     block_barrier();
@@ -515,8 +544,8 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         __builtin_amdgcn_sched_barrier(0);                                               \
         read_frags(cw_, cx_, frow_w, frow_x, foff1, a1, b1);                              \
         if (!EARLY || (I) != 0 || kt != 0)                                               \
-            issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_); \
-        mfma_block(acc, a0, b0);                                                         \
+            issue_half<CW, CX, 1, BF>(cur, nxt, voffw, voffx, kt + (I) + S - 1, nk, wave, pw_, px_); \
+        mfma_block<TJ, BF>(acc, a0, b0);                                                         \
         interleave<MF, CH1, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
         wait_lds_reads();                                                                \
@@ -524,8 +553,8 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
             !first && kt + (I) < (EARLY ? S - 1 : S - 2));                               \
         block_barrier();                                                                 \
         read_frags(nw_, nx_, frow_w, frow_x, foff0, a0, b0);                              \
-        issue_half<CW, CX, 0>(cur, nxt, voffw, voffx, kt + (I) + S, nk, wave, cw_, cx_);                 \
-        mfma_block(acc, a1, b1);                                                         \
+        issue_half<CW, CX, 0, BF>(cur, nxt, voffw, voffx, kt + (I) + S, nk, wave, cw_, cx_);                 \
+        mfma_block<TJ, BF>(acc, a1, b1);                                                         \
         interleave<MF, CH0, RD>();                                                         \
         __builtin_amdgcn_sched_barrier(0);                                               \
     } while (0)
@@ -551,12 +580,12 @@ __device__ __forceinline__ void k_loop(int8_t *__restrict__ w0, int8_t *__restri
         wait_lds_reads();
         __builtin_amdgcn_sched_barrier(0);
         read_frags(wl, xl, frow_w, frow_x, foff1, a1, b1);
-        issue_half<CW, CX, 1>(cur, nxt, voffw, voffx, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
+        issue_half<CW, CX, 1, BF>(cur, nxt, voffw, voffx, nk + S - 2, nk, wave, pick<S, S - 2>(w0, w1, w2, w3),
                       pick<S, S - 2>(x0, x1, x2, x3));
-        mfma_block(acc, a0, b0);
+        mfma_block<TJ, BF>(acc, a0, b0);
         interleave<MF, CH1, RD>();
         __builtin_amdgcn_sched_barrier(0);
-        mfma_block(acc, a1, b1);
+        mfma_block<TJ, BF>(acc, a1, b1);
     }
 }
 
@@ -576,8 +605,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     constexpr int TM = 64 * TJ;            // tile edge in m
     constexpr int STGW = kTile * kBK;      // 16 KiB of weights per stage
     constexpr int STGX = TM * kBK;         // 16 or 8 KiB of activations per stage
-    constexpr bool BF16_OUT = OUT == int(OutKind::BF16) || OUT == int(OutKind::GELU_BF16);
-    constexpr int NSCALE = OUT == int(OutKind::I32) ? 0 : (HAS_BIAS ? 3 : 2);
+    constexpr bool MM = OUT == int(OutKind::BF16_MM);   // bf16 operands, row-major
+    constexpr bool BF16_OUT =
+        OUT == int(OutKind::BF16) || OUT == int(OutKind::GELU_BF16) || MM;
+    constexpr int NSCALE = OUT == int(OutKind::I32) ? 0 : MM ? (HAS_BIAS ? 1 : 0)
+                                                             : (HAS_BIAS ? 3 : 2);
     // memory operations per wave between a tile's K-tile S-2 copies and its
     // K-tile S-1 copies: the previous tile's stores (bf16: 4 x TJ x 2 of 16 B)
     // and this tile's scale loads; other outputs drain at the tile boundary
@@ -619,22 +651,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int frow_x = (wm * 32 * TJ + l32) * kBK;   // + 2048 * j
 
     auto load_scales = [&](int m0_, int n0_, float &a, float &b, float &c) {
-        if constexpr (OUT != int(OutKind::I32)) {
+        if constexpr (OUT != int(OutKind::I32) && !MM) {
             a = sx[min(m0_ + tid, M - 1)];
             b = sw[min(n0_ + tid, N - 1)];
-            if constexpr (HAS_BIAS) c = bias[min(n0_ + tid, N - 1)];
         }
+        if constexpr (OUT != int(OutKind::I32) && HAS_BIAS) c = bias[min(n0_ + tid, N - 1)];
     };
 
     float sc_x = 0.f, sc_w = 0.f, sc_b = 0.f;
     load_scales(m0, n0, sc_x, sc_w, sc_b);
     uint32_t voffw[4], voffx[TJ];
-    lane_offsets(K, wave, lane, voffw);
-    lane_offsets(K, wave, lane, voffx);
-    TileSrc cur = tile_src(qw, qx, m0, n0, M, N, K);
+    lane_offsets<MM>(K, wave, lane, voffw);
+    lane_offsets<MM>(K, wave, lane, voffx);
+    TileSrc cur = tile_src<MM>(qw, qx, m0, n0, M, N, K);
     int nm0 = m0, nn0 = n0;
     bool more = tile_at(1, nm0, nn0);
-    TileSrc nxt = more ? tile_src(qw, qx, nm0, nn0, M, N, K) : cur;
+    TileSrc nxt = more ? tile_src<MM>(qw, qx, nm0, nn0, M, N, K) : cur;
 
     for (int it = 0;; ++it) {
         v16i acc[4][TJ];
@@ -645,9 +677,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-        k_loop<TJ, 4, TJ, S, EPI, true>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt, voffw,
-                                        voffx, nk, it == 0, wave, frow_w, frow_x, foff0, foff1,
-                                        acc);
+        k_loop<TJ, 4, TJ, S, EPI, true, MM>(sw0, sw1, sw2, sw3, sx0, sx1, sx2, sx3, cur, nxt,
+                                            voffw, voffx, nk, it == 0, wave, frow_w, frow_x,
+                                            foff0, foff1, acc);
 
         if constexpr (OUT != int(OutKind::I32)) {
             sscale[0][tid] = sc_x;
@@ -664,8 +696,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         {
             int8_t *const wl = pick<S, S - 1>(sw0, sw1, sw2, sw3);
             int8_t *const xl = pick<S, S - 1>(sx0, sx1, sx2, sx3);
-            issue_half<4, TJ, 0>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
-            issue_half<4, TJ, 1>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
+            issue_half<4, TJ, 0, MM>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
+            issue_half<4, TJ, 1, MM>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
         }
         const bool full = m0 + TM <= M && n0 + kTile <= N;
         if (full)
@@ -683,7 +715,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         cur = nxt;
         load_scales(m0, n0, sc_x, sc_w, sc_b);
         more = tile_at(it + 2, nm0, nn0);
-        if (more) nxt = tile_src(qw, qx, nm0, nn0, M, N, K);
+        if (more) nxt = tile_src<MM>(qw, qx, nm0, nn0, M, N, K);
         // sscale is rewritten only after the next K loop's barriers
     }
     // No copy may still be writing LDS when the workgroup ends.
@@ -1068,6 +1100,9 @@ hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
     case OutKind::GELU_BF16:
         return hb ? launch_t<int(OutKind::GELU_BF16), true>(qx, qw, sx, sw, bias, Y, M, N, K, stream)
                   : launch_t<int(OutKind::GELU_BF16), false>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
+    case OutKind::BF16_MM:
+        return hb ? launch_t<int(OutKind::BF16_MM), true>(qx, qw, sx, sw, bias, Y, M, N, K, stream)
+                  : launch_t<int(OutKind::BF16_MM), false>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
     }
     return hipErrorInvalidValue;
 }
