@@ -176,10 +176,12 @@ def test_prepare_import_int8_unchanged(cr, layout):
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 272, 384), (1, 16, 512),
                                    (513, 528, 1024), (64, 784, 5376), (257, 1040, 256),
-                                   (2048, 8192, 256), (2000, 8000, 384), (4100, 5376, 1024)])
+                                   (2048, 8192, 256), (2000, 8000, 384), (4100, 5376, 1024),
+                                   (17, 48, 65536)])
 def test_gemm_i32_bitexact(cr, M, N, K):
-    """One tile to a full round of 256 tiles, ragged tails in M, N and K, and
-    (M = 4100) whole rounds of 256 x 256 tiles followed by a 256 x 128 tail."""
+    """One tile to a full round of 256 tiles, ragged tails in M, N and K,
+    (M = 4100) whole rounds of 256 x 256 tiles followed by a 256 x 128 tail,
+    and (K = 65536) the largest K with the extreme accumulator -127^2 K."""
     announce(f"gemm_i32 M={M} N={N} K={K}")
     rng = np.random.default_rng(M * 7 + N)
     qx = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
