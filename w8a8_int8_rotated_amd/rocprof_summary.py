@@ -13,6 +13,9 @@
 known size recorded in the same run (FETCH_SIZE and WRITE_SIZE are in KiB per
 dispatch), and records the SHA-256 of the kernel source so a reader (and
 bench.py) can tell whether the figure still applies to the current kernel.
+One call can launch several instantiations of a kernel (the GEMM sends its
+last tile-rows to a second launch); every instantiation matching --kernel is
+listed, and the per-call figure is the sum of their per-dispatch averages.
 """
 from __future__ import annotations
 
@@ -60,13 +63,24 @@ def _pick(agg, needle):
     return sum(vals) / len(vals), len(vals)
 
 
+def _per_call(agg, needle):
+    """[(instantiation, dispatches, average per dispatch)] for every kernel
+    matching `needle`, and the sum of the averages (one call launches each
+    instantiation once)."""
+    rows = [(_short(k), len(vs), sum(vs) / len(vs)) for k, vs in sorted(agg.items())
+            if needle in k]
+    if not rows:
+        raise SystemExit(f"no dispatch of a kernel matching {needle!r}")
+    return rows, sum(r[2] for r in rows)
+
+
 def traffic(args):
     fetch = _counter(args.fetch, "FETCH_SIZE")
     write = _counter(args.write, "WRITE_SIZE")
     cf, _ = _pick(fetch, COPY_KERNEL)
     cw, _ = _pick(write, COPY_KERNEL)
-    kf, nf = _pick(fetch, args.kernel)
-    kw, nw = _pick(write, args.kernel)
+    frows, kf = _per_call(fetch, args.kernel)
+    wrows, kw = _per_call(write, args.kernel)
     sf = args.copy_bytes / (cf * 1024.0)
     sw = args.copy_bytes / (cw * 1024.0)
     rd = kf * 1024.0 * sf
@@ -78,10 +92,12 @@ def traffic(args):
            f"Calibration: the plain device copy `{COPY_KERNEL}` of {args.copy_bytes} bytes reads "
            f"FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB per dispatch, so the scale "
            f"factors are {sf:.4f} (fetch) and {sw:.4f} (write).", "",
-           "| counter | kernel dispatches | KiB per dispatch | scaled bytes per launch |",
-           "|---|---:|---:|---:|",
-           f"| FETCH_SIZE | {nf} | {kf:.0f} | {rd:.4g} |",
-           f"| WRITE_SIZE | {nw} | {kw:.0f} | {wr:.4g} |", "",
+           "| counter | kernel | dispatches | KiB per dispatch | scaled bytes |",
+           "|---|---|---:|---:|---:|",
+           *[f"| FETCH_SIZE | `{n}` | {c} | {v:.0f} | {v * 1024.0 * sf:.4g} |" for n, c, v in frows],
+           *[f"| WRITE_SIZE | `{n}` | {c} | {v:.0f} | {v * 1024.0 * sw:.4g} |" for n, c, v in wrows],
+           "",
+           "Per call (the sum over the instantiations above):", "",
            f"traffic_bytes_per_launch: {rd + wr:.6g}",
            f"read_bytes_per_launch: {rd:.6g}",
            f"write_bytes_per_launch: {wr:.6g}",
@@ -91,45 +107,50 @@ def traffic(args):
 
 
 def counters(args):
-    """Average of every counter per dispatch of the kernel, over one or more
-    counter runs, with the derived figures the GEMM analysis uses."""
-    vals = {}
-    durs = []
+    """Average of every counter per dispatch of each kernel instantiation
+    matching --kernel, over one or more counter runs, with the derived figures
+    the GEMM analysis uses."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    durs = collections.defaultdict(list)
     for path in args.csv:
         for r in csv.DictReader(open(path)):
             if args.kernel not in r["Kernel_Name"]:
                 continue
-            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            name = _short(r["Kernel_Name"])
+            vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            durs[name].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     if not vals:
         raise SystemExit(f"no dispatch of a kernel matching {args.kernel!r}")
-    avg = {k: sum(v) / len(v) for k, v in vals.items()}
     out = [f"# Counters of `{args.kernel}` -- {args.workload}", "",
-           "Commands (run from /tmp, repository at $R):", "", "```", *args.command, "```", "",
-           "| counter | dispatches | average per dispatch |", "|---|---:|---:|"]
-    for k in sorted(avg):
-        out.append(f"| {k} | {len(vals[k])} | {avg[k]:.6g} |")
-    out += ["", "Derived (per dispatch):", ""]
-    if "TCC_EA0_RDREQ_sum" in avg:
-        out.append(f"- L2 read misses to the fabric: {avg['TCC_EA0_RDREQ_sum'] * 128 / 1e9:.3f} GB "
-                   f"(128-byte requests)")
-    if "TCC_EA0_WRREQ_sum" in avg:
-        out.append(f"- L2 write requests: {avg['TCC_EA0_WRREQ_sum'] * 64 / 1e9:.3f} GB (64-byte)")
-    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
-        h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
-        out.append(f"- L2 hit rate: {100 * h / (h + m):.1f}%")
-    if "GRBM_GUI_ACTIVE" in avg and durs:
-        d = sum(durs) / len(durs)
-        clk = avg["GRBM_GUI_ACTIVE"] / args.xcds / d
-        out.append(f"- shader clock: {clk:.3f} GHz (GRBM_GUI_ACTIVE / {args.xcds} XCDs over the "
-                   f"dispatch's {d / 1e3:.1f} us under the profiler)")
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / args.simds
-            out.append(f"- MFMA busy: {100 * busy / (clk * d):.1f}% of the dispatch's cycles per "
-                       f"SIMD ({args.simds} SIMDs)")
-    if "SQ_INSTS_VALU_MFMA_MOPS_I8" in avg:
-        out.append(f"- INT8 MFMA operations: {avg['SQ_INSTS_VALU_MFMA_MOPS_I8'] * 512:.4g}")
-    out.append("")
+           "Commands (run from /tmp, repository at $R):", "", "```", *args.command, "```", ""]
+    for name in sorted(vals, key=lambda n: -sum(durs[n]) / len(durs[n])):
+        avg = {k: sum(v) / len(v) for k, v in vals[name].items()}
+        out += [f"## `{name}`", "", "| counter | dispatches | average per dispatch |",
+                "|---|---:|---:|"]
+        for k in sorted(avg):
+            out.append(f"| {k} | {len(vals[name][k])} | {avg[k]:.6g} |")
+        out += ["", "Derived (per dispatch):", ""]
+        if "TCC_EA0_RDREQ_sum" in avg:
+            out.append(f"- L2 read misses to the fabric: "
+                       f"{avg['TCC_EA0_RDREQ_sum'] * 128 / 1e9:.3f} GB (128-byte requests)")
+        if "TCC_EA0_WRREQ_sum" in avg:
+            out.append(f"- L2 write requests: {avg['TCC_EA0_WRREQ_sum'] * 64 / 1e9:.3f} GB "
+                       f"(64-byte)")
+        if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+            h, m = avg["TCC_HIT_sum"], avg["TCC_MISS_sum"]
+            out.append(f"- L2 hit rate: {100 * h / (h + m):.1f}%")
+        d = sum(durs[name]) / len(durs[name])
+        if "GRBM_GUI_ACTIVE" in avg:
+            clk = avg["GRBM_GUI_ACTIVE"] / args.xcds / d
+            out.append(f"- shader clock: {clk:.3f} GHz (GRBM_GUI_ACTIVE / {args.xcds} XCDs over "
+                       f"the dispatch's {d / 1e3:.1f} us under the profiler)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / args.simds
+                out.append(f"- MFMA busy: {100 * busy / (clk * d):.1f}% of the dispatch's cycles "
+                           f"per SIMD ({args.simds} SIMDs)")
+        if "SQ_INSTS_VALU_MFMA_MOPS_I8" in avg:
+            out.append(f"- INT8 MFMA operations: {avg['SQ_INSTS_VALU_MFMA_MOPS_I8'] * 512:.4g}")
+        out.append("")
     _emit("\n".join(out), args.output)
 
 
