@@ -532,22 +532,182 @@ hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
     return hipGetLastError();
 }
 
+// Streaming variant for long rows (6144 < K <= 24576): rows are taken in
+// pairs, one per half-wave.  A wave step covers 256 elements of each row of
+// the pair (32 lanes x 8 elements; a Hadamard block of b <= 256 lies inside
+// a half-wave, so the rotation is the same code), and a pair is split over
+// WPR = 2..16 waves of at most SPR steps.  Both rows of a pair are
+// neighbours in a 16-row block of the K-tiled codes, so a store instruction
+// writes 4 K-tiles x 2 rows x 64 B = 4 whole 128-byte lines (one row per wave
+// wrote 8 half lines per instruction: 27% slower at K = 21504).  One
+// persistent workgroup per CU walks pair groups, and each wave loads the raw
+// input of its next group before rotating the current one, so memory and the
+// rotation overlap inside the wave as well as across waves.
+template <int IN, int B, int ROT, int SPR, int WPR, int NW>
+__global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
+    const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
+    int8_t *__restrict__ q, float *__restrict__ s)
+{
+    static_assert(NW % WPR == 0 && WPR > 1, "");
+    static_assert(B <= 256, "a block lies inside a half-wave");
+    constexpr int HS = 256;                   // elements per row per step
+    constexpr int LPB = B / 8;
+    constexpr int NSTAGE = (B == 64) ? 3 : (B == 128) ? 4 : 5;
+    constexpr int PAIRS = NW / WPR;           // row pairs per pass
+    constexpr int ESIZE = IN == int(InType::BF16) ? 2 : 4;
+    constexpr int DW = IN == int(InType::BF16) ? 4 : 8;   // raw dwords per lane per step
+
+    __shared__ float red[2][NW][2];
+
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5, hl = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int part = wave % WPR;
+    const int grp = wave / WPR;
+    const int li = hl % LPB;
+    const int chunk = chunk_of_lane(li);
+    const int lane_off = (hl / LPB) * B + chunk * 8;   // inside the 256-element step
+    const int steps = (K + HS - 1) / HS;
+    const int my_steps = (steps - part + WPR - 1) / WPR;
+    const int64_t ngroups = (M + 2 * PAIRS - 1) / (2 * PAIRS);
+
+    float csign[NSTAGE];
+#pragma unroll
+    for (int k = 0; k < NSTAGE; ++k)
+        csign[k] = ((chunk >> k) & 1) ? -1.0f : 1.0f;
+    // the Sylvester sign trick leaves the upper lanes' values negated
+    const bool negated = ROT == 0 && (__builtin_popcount(chunk) & 1) != 0;
+
+    // Every memory instruction is unconditional (steps past the row end fall
+    // outside the buffer range: loads read zero, stores are dropped), so the
+    // compiler can count them and wait for the prefetched loads only.
+    int raw[SPR][DW];
+    auto issue = [&](int64_t gi) {
+        const int64_t row = (gi * PAIRS + grp) * 2 + half;
+        const bool in = row < M;
+        const __amdgpu_buffer_rsrc_t r = row_rsrc(
+            reinterpret_cast<const char *>(src) + (in ? row : 0) * ld * ESIZE, in ? K * ESIZE : 0);
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            const int e = (part + WPR * t) * HS + lane_off;
+            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) raw[t][j] = a[j];
+            if constexpr (DW == 8) {
+                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) raw[t][4 + j] = c[j];
+            }
+        }
+    };
+    const __amdgpu_buffer_rsrc_t srs = row_rsrc(s, (int)(M * 4 < 0x7fffffff ? M * 4 : 0x7fffffff));
+
+    int64_t gi = blockIdx.x;
+    issue(gi);
+    {
+        // the loop's stores, into an empty range: both ways into the loop
+        // then carry the same sequence of memory operations, and the
+        // compiler's waits at the top of the loop cover the loads only
+        const __amdgpu_buffer_rsrc_t none = row_rsrc(q, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(0, none, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < SPR; ++t)
+            __builtin_amdgcn_raw_buffer_store_b64((v2i){0, 0}, none, 0, 0, 0);
+    }
+    int par = 0;
+    for (; gi < ngroups; gi += gridDim.x, par ^= 1) {
+        const int64_t row = (gi * PAIRS + grp) * 2 + half;
+        float v[SPR][8];
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            if constexpr (DW == 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[t][2 * j] = bf16_lo((uint32_t)raw[t][j]);
+                    v[t][2 * j + 1] = bf16_hi((uint32_t)raw[t][j]);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[t][j] = __int_as_float(raw[t][j]);
+            }
+        }
+        // next group (or this one again on the last pass: its loads are
+        // harmless and keep the sequence uniform)
+        issue(gi + gridDim.x < ngroups ? gi + gridDim.x : gi);
+
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            if (t < my_steps) {
+                rotate_chunk<B, ROT>(v[t], csign);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[t][j]));
+            }
+        }
+        // the row's |max|: over the half-wave, then over its WPR waves; red[]
+        // alternates between passes so a fast wave cannot overwrite values a
+        // slow one still reads
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1)
+            m = fmaxf(m, __shfl_xor(m, off, 64));
+        if (hl == 0) red[par][wave][half] = m;
+        __syncthreads();
+        float mx = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) mx = fmaxf(mx, red[par][grp * WPR + w][half]);
+        const float inv = (mx > 0.0f) ? __fdiv_rn(127.0f, mx) : 0.0f;
+        const float invs = negated ? -inv : inv;
+        const bool in = row < M;
+        // the scale: one lane per row writes, every other lane's offset is
+        // out of range
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_int(__fmul_rn(__fdiv_rn(mx, 127.0f), inv_sqrt_b)), srs,
+            (part == 0 && hl == 0 && in) ? (int)(row * 4) : 0x7ffffff0, 0, 0);
+        const __amdgpu_buffer_rsrc_t qb =
+            row_rsrc(q + (in ? (row & ~int64_t(15)) : 0) * (int64_t)K, in ? 16 * K : 0);
+        const int q_off = (int)tiled_offset(row & 15, lane_off, K);
+#pragma unroll
+        for (int t = 0; t < SPR; ++t) {
+            const uint2 c = quantise_chunk(v[t], invs);
+            // step t spans 4 K-tiles of the row block: 4 KiB
+            __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)c.x, (int)c.y}, qb,
+                                                  (part + WPR * t) * 4096 + q_off, 0, 0);
+        }
+    }
+}
+
+template <int IN, int B, int ROT, int SPR, int WPR, int NW>
+hipError_t launch_pair(const void *src, int64_t M, int64_t K, int64_t ld,
+                         float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+{
+    constexpr int rows_per_wg = 2 * (NW / WPR);
+    const int64_t groups = (M + rows_per_wg - 1) / rows_per_wg;
+    const int64_t grid = std::min<int64_t>(groups, device_cu_count());
+    hipLaunchKernelGGL((rotquant_pair_kernel<IN, B, ROT, SPR, WPR, NW>), dim3((unsigned)grid),
+                       dim3(NW * 64), 0, stream, src, M, (int)K, ld, inv_sqrt_b, q, s);
+    return hipGetLastError();
+}
+
 // Rows of up to 4 steps (2048 elements) are held by one wave, several rows
-// per wave when they are short.  Longer rows are split over 2..16 waves of
-// at most 6 steps each and streamed by one 16-wave workgroup per CU; beyond
-// 96 steps the one-shot kernel holds 8 steps per wave.
+// per wave when they are short.  Rows of up to 12 steps go to the streaming
+// kernel, one row over 2 waves of 6 steps, 16 waves per CU (at K = 5376 its
+// K-tiled stores cost nothing: 0.117 ms, as row-major codes).  Rows up to
+// 24576 elements go in pairs to the pair kernel: 4..16 waves per pair of at
+// most 6 steps of 256 elements (at K = 21504 it takes 0.200 ms where one row
+// per wave took 0.244 ms).  Longer rows go to the one-shot kernel with 16
+// waves of up to 8 steps of 512 elements (K <= 65536).
 template <int IN, int B, int ROT>
 hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
 {
     const int64_t steps = (K + kStep - 1) / kStep;
+    const int64_t hsteps = (K + 255) / 256;
     if (steps <= 1) return launch_cfg<IN, B, ROT, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 2) return launch_cfg<IN, B, ROT, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 4) return launch_cfg<IN, B, ROT, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 12) return launch_stream<IN, B, ROT, 6, 2, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 24) return launch_stream<IN, B, ROT, 6, 4, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 48) return launch_stream<IN, B, ROT, 6, 8, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 96) return launch_stream<IN, B, ROT, 6, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (hsteps <= 48) return launch_pair<IN, B, ROT, 6, 8, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (hsteps <= 96) return launch_pair<IN, B, ROT, 6, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     return launch_cfg<IN, B, ROT, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
 }
 
