@@ -308,6 +308,40 @@ def test_output_guard_band(cr):
     assert (b[:pad] == -7).all() and (b[pad + M * N:] == -7).all()
 
 
+def test_two_streams_concurrent(cr):
+    """The library keeps no per-call state: forwards on two streams with
+    separate workspaces, issued back to back so they can overlap, give the
+    same bits as the same calls run one after the other.  The MLP pair is
+    included: both streams rewrite the shared GELU table with the same values
+    while the other may be reading it."""
+    announce("two streams")
+    w = wl.scaled("mlp_16384", M=700, K=1024, N=512, ffn=2048)
+    Wu, Wd = w.weight("w"), w.weight("w2")
+    pu = cr.convrot_linear_prepare_weights(to_dev(Wu), 128)
+    pd = cr.convrot_linear_prepare_weights(to_dev(Wd), 128)
+    xa = to_dev_bf16(w.activations())
+    xb = to_dev_bf16(wl.scaled("mlp_16384", M=700, K=1024, N=512, ffn=2048,
+                               seed=9).activations())
+    ref_a = bf16_bits(cr.convrot_mlp_forward(xa, pu, pd))
+    ref_b = bf16_bits(cr.convrot_mlp_forward(xb, pu, pd))
+    lin_a = host(cr.convrot_linear_forward(xa, pu, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            ya = cr.convrot_mlp_forward(xa, pu, pd, stream=sa)
+            la = cr.convrot_linear_forward(xa, pu, out_dtype=torch.float32, stream=sa)
+        with torch.cuda.stream(sb):
+            yb = cr.convrot_mlp_forward(xb, pu, pd, stream=sb)
+        outs.append((ya, la, yb))
+    torch.cuda.synchronize()
+    for ya, la, yb in outs:
+        assert np.array_equal(bf16_bits(ya), ref_a)
+        assert np.array_equal(host(la), lin_a)
+        assert np.array_equal(bf16_bits(yb), ref_b)
+
+
 # ----------------------------------------------------------- low-rank ----
 
 def test_lowrank_small_full(cr):
