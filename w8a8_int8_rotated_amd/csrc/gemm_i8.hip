@@ -29,11 +29,11 @@
 // direct-to-LDS buffer load (buffer_load_dwordx4 ... lds: each lane fetches
 // 16 bytes and the wave's 1 KiB lands contiguously in LDS), so no registers
 // stage the tiles and no LDS write instructions are issued.  In the K-tiled
-// layout one copy instruction moves one 16-row tile, a contiguous 1 KiB.  The copies of
-// each K-tile are split over the two halves of a step and spread between the
-// MFMAs, which keeps the texture-address queue from filling.  Every wait on a
-// copy is explicit: s_waitcnt vmcnt(n) for this wave's copies, then a barrier
-// for the other waves'.
+// layout one copy instruction moves one 16-row tile, a contiguous 1 KiB.  The
+// copies of each K-tile are split over the two halves of a step and spread
+// between the MFMAs, which keeps the texture-address queue from filling.
+// Every wait on a copy is explicit: s_waitcnt vmcnt(n) for this wave's
+// copies, then a barrier for the other waves'.
 //
 // LDS rows are 64 bytes; chunk c (16 B) of tile row r sits at slot
 // c ^ f(r), f(r) = (r >> 2) & 3, as in the global layout.  The fragment
@@ -46,6 +46,15 @@
 // Workgroups are renumbered so each of the 8 XCDs walks a contiguous range of
 // tiles, grouped 4 tile-rows high, for L2 reuse of both operands (4 rows
 // fetch 30% fewer L2 lines than 8 at K = 5376, measured with TCC_EA0_RDREQ).
+//
+// Also in this file, on the same K loop:
+//  - 256 (n) x 128 (m) tiles (TJ = 2), launched for the last tile-rows when
+//    a round of 256 x 256 tiles would leave CUs idle (launch_t);
+//  - the bf16 x bf16 product of the low-rank comparison variant
+//    (OutKind::BF16_MM: v_mfma_f32_32x32x16_bf16, row-major operands);
+//  - the low-rank factor 1 with the rotation and requantisation of its
+//    output in the epilogue (lowrank_f1_kernel);
+//  - the bf16 GELU table of the MLP's up projection.
 #include "common.hpp"
 
 #include <algorithm>

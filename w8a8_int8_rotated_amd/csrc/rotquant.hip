@@ -2,7 +2,8 @@
 //
 // What it computes (per row x of length K, block b):
 //   v = blockdiag(H_b) . x  in fp32, butterfly strides h = 1, 2, ..., b/2 in
-//       ascending order (Sylvester H_b, natural order, unnormalised);
+//       ascending order (Sylvester H_b, natural order, unnormalised), or the
+//       regular H_4 Kronecker blocks (rotate_regular, b = 64 or 256);
 //   amax = max |v|;  q = rint(v * (127/amax)) in [-127, 127];
 //   s = (amax/127) * fp32(1/sqrt(b));  a zero row gives q = 0, s = 0.
 // The rotation and the row-wise quantise are the fused prologue of a ConvRot
@@ -11,7 +12,8 @@
 // lehuy.net article's ("Cach nen hoat dong", second bullet).
 //
 // Data layout in registers.  A wave covers 512 consecutive elements of a row
-// per "step": 64 lanes x 8 elements.  A block of b elements is spread over
+// per "step": 64 lanes x 8 elements (the pair kernel: 256 elements of each of
+// two rows, one per half-wave).  A block of b elements is spread over
 // L = b/8 lanes, and lane i of the block holds the 8-element chunk pi(i) of it,
 // where pi is the GF(2)-linear map with pi(1)=1, pi(2)=2, pi(4)=7, pi(8)=12,
 // pi(16)=16.  With that assignment the partner of every cross-lane butterfly
@@ -34,7 +36,8 @@
 //
 // Quantise: t = v * inv rounds once (fp32), then t + 1.5*2^23 rounds to an
 // integer with ties to even (|t| <= 127.00001 << 2^22), and the code is the low
-// byte of that float's bits.
+// byte of that float's bits.  Codes go out in the library's K-tiled layout
+// (common.hpp): 8 bytes per lane per step into the row's 16-row block.
 #include "common.hpp"
 
 #include <algorithm>
