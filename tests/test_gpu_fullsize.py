@@ -9,7 +9,8 @@ import torch
 
 import oracle
 from w8a8_int8_rotated_amd import workloads as wl
-from gpu_util import (announce, assert_output_parity, bf16_bits, host, sample_rows, tile,
+from gpu_util import (announce, assert_output_parity, bf16_bits, dev, host, padded_rows,
+                      sample_rows, tile,
                       to_dev, to_dev_bf16, untile)
 
 pytestmark = pytest.mark.gpu
@@ -99,3 +100,41 @@ def test_qk_38656_small_k(cr):
     assert assert_output_parity(yr, y_ref, "bf16", "qk_38656 sampled rows") == 0
     acc = cr.convrot_gemm_i32(to_dev(tile(qx_ref[rows[:8]])), 8, pw)
     assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref[rows[:8]], qw))
+
+
+def test_max_rows_32bit_offsets(cr):
+    """The most rows the entry points accept at K = 5376: the padded code
+    matrix is just under 2^31 bytes (M = 399449, ragged in its last 16-row
+    block; M + 16 would pass 2^31 and is rejected).  N = 256, bf16 out.
+    Codes and row scales of the sampled rows (the last 20 rows included) and
+    their outputs against the oracle, so every 32-bit offset near the limit
+    is exercised."""
+    K, N, b = 5376, 256, 128
+    M = 399449
+    assert padded_rows(M) * K < 2**31 <= padded_rows(M + 16) * K
+    announce(f"largest row count M={M} K={K} N={N} b={b}")
+    # seeded N(0,1) activations drawn on the device in chunks (4.3 GB of
+    # bf16), 1% of channels x30; the oracle gets the same bytes back
+    gen = torch.Generator(device=dev()).manual_seed(0)
+    X = torch.empty((M, K), dtype=torch.bfloat16, device=dev())
+    for r0 in range(0, M, 65536):
+        r1 = min(M, r0 + 65536)
+        X[r0:r1] = torch.randn((r1 - r0, K), generator=gen, device=dev()).to(torch.bfloat16)
+    hot = np.random.default_rng(1).choice(K, size=54, replace=False)
+    X[:, torch.from_numpy(hot).to(dev())] *= 30
+    W = np.random.default_rng(2).normal(0.0, 0.02, (N, K)).astype(np.float32)
+    pw, qw, sw = _prep(cr, W, b)
+    y = cr.convrot_linear_forward(X, pw)
+    qx, sx = cr.convrot_rotate_quantize(X, b)
+    torch.cuda.synchronize()
+    rows = np.union1d(sample_rows(M, 64), np.arange(M - 20, M))
+    rows_d = torch.from_numpy(rows).to(dev())
+    x_rows = bf16_bits(X[rows_d])
+    qx_ref, sx_ref = oracle.rotate_quantize(x_rows, b, "bf16")
+    assert np.array_equal(host(sx[rows_d]), sx_ref), "row scales"
+    blocks = host(qx.view(-1, 16 * K)[torch.from_numpy(rows // 16).to(dev())])
+    got = np.stack([untile(blk, 16, K)[r % 16] for blk, r in zip(blocks, rows)])
+    assert np.array_equal(got, qx_ref), "codes of the sampled rows"
+    y_ref = oracle.linear_forward(x_rows, qw, sw, b, out="bf16")
+    assert assert_output_parity(bf16_bits(y[rows_d]), y_ref, "bf16",
+                                f"M={M} sampled rows") == 0
