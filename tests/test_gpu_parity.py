@@ -484,6 +484,36 @@ def test_gelu_exhaustive(cr):
     assert not diff.any(), [hex(int(x)) for x in u[diff][:8]]
 
 
+def test_gelu_epilogue_every_pattern(cr):
+    """Every bf16 pattern of u -- zero, denormals, the range the epilogue
+    looks up in LDS, huge values, inf and NaN -- through the up projection's
+    GELU epilogue.  Imported weight codes are one-hot at k = 0 and the
+    activation codes are 1 there, so acc = 1 and u = bf16((1 * s_x) * s_w);
+    s_w holds every pattern (as fp32) in a seeded column order, so slabs mix
+    patterns inside and outside the LDS range.  Rows scale them by 1, 0,
+    2^-100, 2^100 and seeded factors; M = 300 gives whole and partial tiles.
+    Expected: the oracle's dequant, then its GELU map (NaN: both NaN)."""
+    announce("gelu epilogue, every bf16 pattern")
+    M, K, N, b = 300, 128, 65536, 128
+    rng = np.random.default_rng(0)
+    sw = (rng.permutation(65536).astype(np.uint32) << 16).view(np.float32)
+    sx = (2.0 ** rng.integers(-12, 13, M) * rng.uniform(0.5, 1.0, M)).astype(np.float32)
+    sx[:4] = [1.0, 0.0, 2.0 ** -100, 2.0 ** 100]
+    qw = np.zeros((N, K), np.int8)
+    qw[:, 0] = 1
+    qx = np.zeros((M, K), np.int8)
+    qx[:, 0] = 1
+    pw = cr.convrot_linear_prepare_weights(to_dev(qw), b, src_scale=to_dev(sw))
+    g = bf16_bits(cr.convrot_gemm_dequant(to_dev(tile(qx)), to_dev(sx), pw, gelu=True))
+    u_ref = oracle.dequant(oracle.gemm_i32(qx, qw), sx, sw, out="bf16")
+    g_ref = oracle.gelu_bf16(u_ref)
+    nan = lambda a: ((a & 0x7f80) == 0x7f80) & ((a & 0x007f) != 0)
+    diff = (g != g_ref) & ~(nan(g) & nan(g_ref))
+    print(f"[parity] gelu epilogue: {int(diff.sum())} of {g.size} outputs differ", flush=True)
+    assert not diff.any(), [(hex(int(u)), hex(int(a)), hex(int(e)))
+                            for u, a, e in zip(u_ref[diff][:6], g[diff][:6], g_ref[diff][:6])]
+
+
 def test_mlp_small(cr):
     """MLP pair with GELU: u, g and the output bit-exact against the oracle."""
     announce("mlp small")

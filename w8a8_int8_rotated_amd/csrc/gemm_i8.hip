@@ -184,6 +184,36 @@ __device__ __forceinline__ uint32_t gelu_pair(uint32_t u2)
     return (uint32_t)g_gelu_bf16[u2 & 0xffffu] | ((uint32_t)g_gelu_bf16[u2 >> 16] << 16);
 }
 
+// The slice of that table the GEMM epilogue reads from LDS: for each sign the
+// patterns with |u| in [2^-31, 2^9), i.e. biased exponents 96..135 (40 x 128
+// entries, 10 KiB per sign).  Gathers from LDS cost a fraction of gathers
+// through the texture path; a 32-row slab in which any |u| falls outside the
+// slice (zero, tiny, huge, inf, NaN) is patched from the full table.
+constexpr int kGeluLo = 96 * 128;      // first |u| pattern of the slice
+constexpr int kGeluSpan = 40 * 128;    // patterns per sign
+__shared__ uint16_t g_gelu_lds[2 * kGeluSpan];
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Offsets of both halves' |u| from the slice start (wrapping below it): a
+// half is inside the slice iff its offset is < kGeluSpan.
+__device__ __forceinline__ u16x2 gelu_slice_off(uint32_t u2)
+{
+    return (__builtin_bit_cast(u16x2, u2) & (u16x2)(0x7fff)) - (u16x2)(kGeluLo);
+}
+
+// Both halves from the LDS slice (an index clamped into it when outside);
+// mx collects the largest offset seen, so that mx < kGeluSpan in both halves
+// means every lookup was inside the slice.
+__device__ __forceinline__ uint32_t gelu_pair_lds(uint32_t u2, u16x2 &mx)
+{
+    const u16x2 d = gelu_slice_off(u2);
+    mx = __builtin_elementwise_max(mx, d);
+    const u16x2 idx = (__builtin_bit_cast(u16x2, u2) >> (u16x2)(15)) * (u16x2)(kGeluSpan) +
+                      __builtin_elementwise_min(d, (u16x2)(kGeluSpan - 1));
+    return (uint32_t)g_gelu_lds[idx.x] | ((uint32_t)g_gelu_lds[idx.y] << 16);
+}
+
 // Dequantise and store a wave's 128 (n) x 32 TJ (m) block.  FULL: the tile
 // lies inside [M, N], so no per-lane bounds checks are needed.
 //
@@ -209,7 +239,8 @@ __device__ __forceinline__ v16i acc_frag(const v16i &a)
 }
 
 // GELU epilogue, one 32-row slab j of a wave's block: dequantise, round to
-// bf16 and look up bf16(GELU(u)) for its 4 x 32 columns ...
+// bf16 and look up bf16(GELU(u)) for its 4 x 32 columns in the LDS slice; if
+// any lane met a |u| outside it, recompute those pairs from the full table ...
 template <int OUT, bool HAS_BIAS, int TJ, int J>
 __device__ __forceinline__ void gelu_lookup(const v16i (&acc)[4][TJ],
                                             const float (&sscale)[3][kTile], int wm, int wn,
@@ -217,6 +248,17 @@ __device__ __forceinline__ void gelu_lookup(const v16i (&acc)[4][TJ],
 {
     const int ml = wm * 32 * TJ + 32 * J + l32;
     const float sxm = sscale[0][ml];
+    // packed bf16 u of columns 4q .. 4q + 3 of fragment i (two dwords)
+    auto u_pair = [&](const v16i &av, int i, int q, int half) {
+        const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
+        const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
+        const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
+        return half == 0 ? cvt_pk_bf16(dequant1<OUT, HAS_BIAS>(av[4 * q + 0], sxm, swv.x, bv.x),
+                                       dequant1<OUT, HAS_BIAS>(av[4 * q + 1], sxm, swv.y, bv.y))
+                         : cvt_pk_bf16(dequant1<OUT, HAS_BIAS>(av[4 * q + 2], sxm, swv.z, bv.z),
+                                       dequant1<OUT, HAS_BIAS>(av[4 * q + 3], sxm, swv.w, bv.w));
+    };
+    u16x2 mx = (u16x2)(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const v16i av = acc_frag(acc[i][J]);
@@ -224,17 +266,28 @@ __device__ __forceinline__ void gelu_lookup(const v16i (&acc)[4][TJ],
         for (int p = 0; p < 2; ++p)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int q = 2 * p + h;
-                const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
-                const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
-                const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
-                gv[i][p][h][0] = gelu_pair(cvt_pk_bf16(
-                    dequant1<OUT, HAS_BIAS>(av[4 * q + 0], sxm, swv.x, bv.x),
-                    dequant1<OUT, HAS_BIAS>(av[4 * q + 1], sxm, swv.y, bv.y)));
-                gv[i][p][h][1] = gelu_pair(cvt_pk_bf16(
-                    dequant1<OUT, HAS_BIAS>(av[4 * q + 2], sxm, swv.z, bv.z),
-                    dequant1<OUT, HAS_BIAS>(av[4 * q + 3], sxm, swv.w, bv.w)));
+                gv[i][p][h][0] = gelu_pair_lds(u_pair(av, i, 2 * p + h, 0), mx);
+                gv[i][p][h][1] = gelu_pair_lds(u_pair(av, i, 2 * p + h, 1), mx);
             }
+    }
+    const bool outside = mx.x >= kGeluSpan || mx.y >= kGeluSpan;
+    if (__builtin_amdgcn_ballot_w64(outside)) {
+        // rare: only the pairs with a half outside the slice gather from the
+        // full table (the others keep their LDS results)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v16i av = acc_frag(acc[i][J]);
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        const uint32_t u2 = u_pair(av, i, 2 * p + h, d);
+                        const u16x2 o = gelu_slice_off(u2);
+                        if (o.x >= kGeluSpan || o.y >= kGeluSpan) gv[i][p][h][d] = gelu_pair(u2);
+                    }
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -652,6 +705,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 
     int m0, n0;
     if (!tile_at(0, m0, n0)) return;
+    if constexpr (OUT == int(OutKind::GELU_BF16)) {
+        // the LDS slice of the GELU table (written by the launch before this
+        // one on the same stream)
+        for (int i = threadIdx.x; i < 2 * kGeluSpan; i += kThreads) {
+            const int neg = i >= kGeluSpan;
+            g_gelu_lds[i] = g_gelu_bf16[(neg << 15) | (i - neg * kGeluSpan + kGeluLo)];
+        }
+        __syncthreads();
+    }
 
     const int l32 = lane & 31, g = lane >> 5;
     const int foff0 = ((0 + g) ^ swz(l32)) << 4;
