@@ -54,7 +54,8 @@
 //    (OutKind::BF16_MM: v_mfma_f32_32x32x16_bf16, row-major operands);
 //  - the low-rank factor 1 with the rotation and requantisation of its
 //    output in the epilogue (lowrank_f1_kernel);
-//  - the bf16 GELU table of the MLP's up projection.
+//  - the bf16 GELU table of the MLP's up projection, whose epilogue reads the
+//    slice with |u| in [2^-31, 2^9) from LDS (20 KiB beside the stages).
 #include "common.hpp"
 
 #include <algorithm>
