@@ -46,6 +46,10 @@ namespace convrot {
 namespace {
 
 constexpr int kStep = 512;      // elements per wave step
+// cache policy of every input load: nt (streaming), since each input byte
+// is read once; measured 8% faster on the M=38656, K=5376 activations read
+// right after a GEMM, 2% on the MLP's g
+constexpr int kStreamLoad = 2;
 constexpr int kTiledStep = 16 * kStep;   // bytes a step spans in a K-tiled row block
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 
@@ -233,14 +237,14 @@ template <int IN>
 __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t row, int e, float (&v)[8])
 {
     if constexpr (IN == int(InType::BF16)) {
-        const v4i d = __builtin_amdgcn_raw_buffer_load_b128(row, e * 2, 0, 0);
+        const v4i d = __builtin_amdgcn_raw_buffer_load_b128(row, e * 2, 0, kStreamLoad);
         v[0] = bf16_lo(d[0]); v[1] = bf16_hi(d[0]);
         v[2] = bf16_lo(d[1]); v[3] = bf16_hi(d[1]);
         v[4] = bf16_lo(d[2]); v[5] = bf16_hi(d[2]);
         v[6] = bf16_lo(d[3]); v[7] = bf16_hi(d[3]);
     } else {
-        const v4i a = __builtin_amdgcn_raw_buffer_load_b128(row, e * 4, 0, 0);
-        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(row, e * 4 + 16, 0, 0);
+        const v4i a = __builtin_amdgcn_raw_buffer_load_b128(row, e * 4, 0, kStreamLoad);
+        const v4i c = __builtin_amdgcn_raw_buffer_load_b128(row, e * 4 + 16, 0, kStreamLoad);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             v[j] = __int_as_float(a[j]);
@@ -442,11 +446,11 @@ __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
             const int e = (part + WPR * t) * kStep + lane_off;
-            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, 0);
+            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, kStreamLoad);
 #pragma unroll
             for (int j = 0; j < 4; ++j) raw[t][j] = a[j];
             if constexpr (DW == 8) {
-                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, 0);
+                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, kStreamLoad);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) raw[t][4 + j] = c[j];
             }
@@ -593,11 +597,11 @@ __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
             const int e = (part + WPR * t) * HS + lane_off;
-            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, 0);
+            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, kStreamLoad);
 #pragma unroll
             for (int j = 0; j < 4; ++j) raw[t][j] = a[j];
             if constexpr (DW == 8) {
-                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, 0);
+                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, kStreamLoad);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) raw[t][4 + j] = c[j];
             }
