@@ -16,8 +16,10 @@ projections, per step time); ``roofline`` for the dominant kernel (its
 algorithmic ops or bytes per launch over its average launch time, timed with
 HIP events recorded on the stream the kernel runs on); ``kernels`` with every
 kernel of the step; ``roofline_rotquant`` for the first rotate+quantise pass;
-and ``cpu_baseline``, the CPU oracle timed on a bounded sample of the same
-rows, which also checks the benchmarked outputs on those rows.
+``cpu_baseline``, the CPU oracle timed on a bounded sample of the same rows,
+which also checks the benchmarked outputs on those rows; and ``ceilings``,
+the INT8 MFMA rate and the streaming HBM rate measured with the library's
+probes, against which ``frac_of_measured_ceiling`` is given.
 
     python bench.py [--steps 20] [--warmup 5] [--workload qkv_38656]
 """
@@ -56,6 +58,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the measured MFMA and HBM ceilings")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run a plain device copy of this size first (counter calibration)")
     return p.parse_args()
@@ -82,9 +86,10 @@ def recorded_traffic(kernel, workload):
 class Stage:
     """One kernel launch of the step, with its algorithmic cost."""
 
-    def __init__(self, name, kernel, fn, ops, nbytes):
+    def __init__(self, name, kernel, fn, ops, nbytes, src=None):
         self.name, self.kernel, self.fn = name, kernel, fn
         self.ops, self.bytes = float(ops), float(nbytes)
+        self.src = src                    # the tensor a rotquant stage reads
         self.bound = "mfma" if self.ops / self.bytes > RIDGE else "hbm"
         self.ms = None
 
@@ -150,7 +155,7 @@ def setup(w, cr, torch, np, dev):
         stages = [
             Stage("rotquant (FWHT + absmax + INT8 codes)", "rotquant",
                   lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
-                  0.0, rq_bytes(M, K)),
+                  0.0, rq_bytes(M, K), src=X),
             Stage("gemm_i8 (INT8 MFMA + dequant epilogue)", "gemm_i8",
                   lambda: cr.convrot_gemm_dequant(qx, sx, pw, bias=bias_d, out=Y, stream=stream),
                   *gemm_cost(M, N, K, ob, bias is not None)),
@@ -176,7 +181,7 @@ def setup(w, cr, torch, np, dev):
         stages = [
             Stage("rotquant X", "rotquant",
                   lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
-                  0.0, rq_bytes(M, K)),
+                  0.0, rq_bytes(M, K), src=X),
         ]
         if b in (64, 128) and r <= 512:
             # the library's fused factor 1: H is rotated and requantised in
@@ -220,7 +225,7 @@ def setup(w, cr, torch, np, dev):
         stages = [
             Stage("rotquant X", "rotquant",
                   lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
-                  0.0, rq_bytes(M, K)),
+                  0.0, rq_bytes(M, K), src=X),
             Stage("gemm_i8 up + GELU (K -> F)", "gemm_i8",
                   lambda: cr.convrot_gemm_dequant(qx, sx, pu, out=G, gelu=True, stream=stream),
                   *gemm_cost(M, F, K)),
@@ -345,6 +350,14 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_ceilings:
+        ceil = ceilings(cr, torch, dev, stream, stages, first_rq)
+        result["ceilings"] = ceil
+        for r, st in ((result["roofline"], dominant), (result["roofline_rotquant"], first_rq)):
+            c = ceil["mfma_i8_changing_operands" if st.bound == "mfma"
+                     else "hbm_stream_rotquant_shape"]["value"]
+            r["frac_of_measured_ceiling"] = round(r["achieved"] / c, 4)
+
     if w.kind == "lowrank":
         result["comparison"] = bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream,
                                                        ms_per_step)
@@ -353,6 +366,57 @@ def main():
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, w, host, Y)
 
     print(json.dumps(result), flush=True)
+
+
+def ceilings(cr, torch, dev, stream, stages, first_rq):
+    """Ceilings measured with the library's probes, beside the spec peaks:
+    the INT8 MFMA rate on operands that change every round (the clock under a
+    sustained INT8 load is power-limited), and a streaming kernel with the
+    first rotquant's traffic (its input's 16-byte items in, 8 bytes out per
+    item, no arithmetic), each run right after the step's last kernel, as
+    rotquant runs inside the step."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    seed = torch.randint(-2**31, 2**31 - 1, (1024,), dtype=torch.int32, device=dev,
+                         generator=torch.Generator(device=dev).manual_seed(0))
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rates = []
+    for _ in range(3):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        ops = cr.convrot_probe_mfma_i8(20000, seed, sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    mfma = max(rates)
+
+    src = first_rq.src
+    n16 = src.numel() * src.element_size() // 16
+    dst = torch.empty(n16 * 8, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(5):
+        stages[-1].fn()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        cr.convrot_probe_stream(src, dst, 0, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    gbs = 24.0 * n16 / (ms * 1e-3) / 1e9
+    log(f"ceilings: INT8 MFMA {mfma:.0f} TOPS on changing operands; "
+        f"streaming {gbs:.0f} GB/s with the rotquant traffic shape")
+    return {
+        "mfma_i8_changing_operands": {
+            "value": round(mfma, 1), "unit": "TOPS",
+            "frac_of_spec": round(mfma / PEAK_INT8_TOPS, 4),
+            "probe": "v_mfma_i32_32x32x32_i8 rounds, one workgroup per CU, operands remixed "
+                     "every round; best of 3"},
+        "hbm_stream_rotquant_shape": {
+            "value": round(gbs, 1), "unit": "GB/s",
+            "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": 24.0 * n16,
+            "probe": "16 B non-temporal load, 8 B store per item, grid-stride; each run right "
+                     "after the step's last kernel; median of 5"},
+    }
 
 
 def bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream, int8_ms):

@@ -303,6 +303,31 @@ CONVROT_API int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int
  * to bf16 (nearest even).  u and g are device pointers; n >= 0. */
 CONVROT_API int convrot_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g, void *stream);
 
+/* ------------------------------------------------------------------ */
+/* measurement probes: ceilings measured on the device, printed by the */
+/* benchmark beside the spec peaks.  They compute nothing of the      */
+/* method.                                                            */
+/* ------------------------------------------------------------------ */
+
+/* INT8 matrix-core rate on operands that change every round: one 256-thread
+ * workgroup per compute unit; each wave runs `iters` rounds of 4 x 4
+ * v_mfma_i32_32x32x32_i8 (16 x 65536 INT8 operations per round) on fragments
+ * seeded from `seed` (4 KiB, device) and remixed after every round.  `sink`
+ * (16 bytes, device) is written only if the accumulators fold to one
+ * improbable value; it keeps the work from being dropped.  *ops (host)
+ * receives the INT8 operations of the launch.  1 <= iters <= 2^24;
+ * device pointers 16-byte aligned. */
+CONVROT_API int convrot_probe_mfma_i8(int64_t iters, const void *seed, void *sink,
+                                      int64_t *ops, void *stream);
+
+/* Streaming probe with the rotate+quantise traffic shape and no arithmetic:
+ * for each 16-byte item i < n16 of src, mode 0 writes 8 bytes to dst + 8 i
+ * (the xor of input words 0 and 1, then of words 2 and 3), mode 1 copies the
+ * 16 bytes to dst + 16 i.  Device pointers, 16-byte aligned, not
+ * overlapping. */
+CONVROT_API int convrot_probe_stream(const void *src, void *dst, int64_t n16, int mode,
+                                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

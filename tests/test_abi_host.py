@@ -236,8 +236,28 @@ def test_lowrank_bf16_validation(cr):
 def _flag(d, flags):
     d.flags = flags
     return d
+
+
+def test_gelu_and_probe_validation(cr):
+    lib = cr.library()
     assert lib.convrot_gelu_bf16(None, 0, None, None) == cr.OK
     assert lib.convrot_gelu_bf16(None, 4, FAKE, None) == cr.EINVAL
+    assert lib.convrot_gelu_bf16(FAKE, -1, FAKE, None) == cr.EINVAL
+    ops = ctypes.c_int64(0)
+    mfma = lambda it=10, seed=FAKE, sink=FAKE, o=ctypes.byref(ops): lib.convrot_probe_mfma_i8(
+        it, seed, sink, o, None)
+    assert mfma(it=0) == cr.EINVAL
+    assert mfma(it=(1 << 24) + 1) == cr.EINVAL
+    assert mfma(seed=None) == cr.EINVAL
+    assert mfma(o=None) == cr.EINVAL
+    assert mfma(sink=FAKE_ODD) == cr.EALIGN
+    stream = lambda src=FAKE, dst=FAKE, n=64, mode=0: lib.convrot_probe_stream(src, dst, n, mode,
+                                                                               None)
+    assert stream(n=0, src=None, dst=None) == cr.OK
+    assert stream(n=-1) == cr.EINVAL
+    assert stream(mode=2) == cr.EINVAL
+    assert stream(dst=None) == cr.EINVAL
+    assert stream(src=FAKE_ODD) == cr.EALIGN
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -532,3 +532,22 @@ def test_mlp_small(cr):
     ub = bf16_bits(cr.convrot_gemm_dequant(qx, sx, pu))
     assert np.array_equal(ub, u_ref)
     assert assert_output_parity(bf16_bits(y), y_ref, "bf16", "mlp small") == 0
+
+
+def test_measurement_probes(cr):
+    """The streaming probe writes what its header states (a copy, or two xors
+    per 16-byte item) and the MFMA probe runs and reports its work."""
+    announce("measurement probes")
+    src = torch.randint(-2**31, 2**31 - 1, (4 * 40000 + 4,), dtype=torch.int32, device="cuda")
+    a = host(src).reshape(-1, 4)
+    dst = torch.zeros(src.numel() // 2, dtype=torch.int32, device="cuda")
+    cr.convrot_probe_stream(src, dst, 0)
+    assert np.array_equal(host(dst).reshape(-1, 2), np.stack([a[:, 0] ^ a[:, 1], a[:, 2] ^ a[:, 3]], 1))
+    dst16 = torch.zeros_like(src)
+    cr.convrot_probe_stream(src, dst16, 1)
+    assert torch.equal(dst16, src)
+    seed = torch.randint(-2**31, 2**31 - 1, (1024,), dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ops = cr.convrot_probe_mfma_i8(8, seed, sink)
+    torch.cuda.synchronize()
+    assert ops == torch.cuda.get_device_properties(0).multi_processor_count * 4 * 8 * 16 * 65536

@@ -73,6 +73,9 @@ _SIGNATURES = {
         _c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
                  ctypes.c_size_t, _c_p]),
     "convrot_gelu_bf16": (_c_int, [_c_p, _c_i64, _c_p, _c_p]),
+    "convrot_probe_mfma_i8": (_c_int, [_c_i64, _c_p, _c_p, ctypes.POINTER(ctypes.c_int64),
+                                       _c_p]),
+    "convrot_probe_stream": (_c_int, [_c_p, _c_p, _c_i64, _c_int, _c_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -411,3 +414,29 @@ def convrot_gelu_bf16(u: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     _check("convrot_gelu_bf16", lib.convrot_gelu_bf16(_ptr(u), u.numel(), _ptr(out),
                                                       _stream(stream)))
     return out
+
+
+def convrot_probe_mfma_i8(iters: int, seed: torch.Tensor, sink: torch.Tensor,
+                          stream=None) -> int:
+    """Launch the INT8 MFMA rate probe; returns its INT8 operation count.
+    seed: 4 KiB on the device (the operands it starts from); sink: 16 bytes."""
+    lib = library()
+    if seed.numel() * seed.element_size() < 4096 or sink.numel() * sink.element_size() < 16:
+        raise ValueError("seed needs 4 KiB and sink 16 bytes")
+    ops = ctypes.c_int64(0)
+    _check("convrot_probe_mfma_i8", lib.convrot_probe_mfma_i8(
+        iters, _ptr(seed), _ptr(sink), ctypes.byref(ops), _stream(stream)))
+    return ops.value
+
+
+def convrot_probe_stream(src: torch.Tensor, dst: torch.Tensor, mode: int, stream=None):
+    """Streaming probe over src's 16-byte items: mode 0 writes 8 bytes per
+    item into dst, mode 1 copies all 16."""
+    lib = library()
+    nbytes = src.numel() * src.element_size()
+    n16 = nbytes // 16
+    if nbytes % 16 or dst.numel() * dst.element_size() < n16 * (8 if mode == 0 else 16):
+        raise ValueError("src must be whole 16-byte items and dst large enough")
+    _check("convrot_probe_stream", lib.convrot_probe_stream(_ptr(src), _ptr(dst), n16, mode,
+                                                            _stream(stream)))
+    return dst

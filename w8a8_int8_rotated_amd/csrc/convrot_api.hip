@@ -481,4 +481,26 @@ int convrot_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g, void *stream)
     return hip_status(convrot::launch_gelu_bf16(u, g, n, static_cast<hipStream_t>(stream)));
 }
 
+int convrot_probe_mfma_i8(int64_t iters, const void *seed, void *sink, int64_t *ops,
+                          void *stream)
+{
+    if (iters < 1 || iters > (int64_t(1) << 24) || !seed || !sink || !ops)
+        return CONVROT_EINVAL;
+    if (!aligned16(seed) || !aligned16(sink)) return CONVROT_EALIGN;
+    *ops = convrot::probe_mfma_i8_ops(iters);
+    return hip_status(convrot::launch_probe_mfma_i8(iters, static_cast<const int *>(seed),
+                                                    static_cast<int *>(sink),
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+int convrot_probe_stream(const void *src, void *dst, int64_t n16, int mode, void *stream)
+{
+    if (n16 < 0 || (mode != 0 && mode != 1)) return CONVROT_EINVAL;
+    if (n16 == 0) return CONVROT_OK;
+    if (!src || !dst) return CONVROT_EINVAL;
+    if (!aligned16(src) || !aligned16(dst)) return CONVROT_EALIGN;
+    return hip_status(convrot::launch_probe_stream(src, dst, n16, mode == 0,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 } // extern "C"
