@@ -551,3 +551,58 @@ def test_measurement_probes(cr):
     ops = cr.convrot_probe_mfma_i8(8, seed, sink)
     torch.cuda.synchronize()
     assert ops == torch.cuda.get_device_properties(0).multi_processor_count * 4 * 8 * 16 * 65536
+
+
+def test_graph_capture_replays(cr):
+    """The linear, low-rank and MLP forwards record into one HIP graph
+    (torch.cuda.graph): a call allocates, synchronises and clears nothing.
+    Three replays, each on new inputs copied into the captured buffers and
+    followed by eager calls and a synchronisation, give the eager bits."""
+    announce("graph capture: linear, low-rank and MLP forwards")
+    rng = np.random.default_rng(5)
+    lin = wl.scaled("linear_4096", M=700, K=1024, N=768)
+    lr = wl.scaled("lowrank_38656", M=520, K=1024, N=784, rank=256)
+    mlp = wl.scaled("mlp_16384", M=300, K=1024, N=512, ffn=2048)
+    prep = lambda W, b: cr.convrot_linear_prepare_weights(to_dev(W), b)
+    pl = prep(lin.weight(), lin.block)
+    bias = to_dev(lin.bias())
+    pa, pb = prep(lr.weight("w"), lr.block), prep(lr.weight("w2"), lr.block)
+    pu, pd = prep(mlp.weight("w"), mlp.block), prep(mlp.weight("w2"), mlp.block)
+    bf = torch.bfloat16
+    u8 = lambda n: torch.empty(n, dtype=torch.uint8, device="cuda")
+    Xl, Xr, Xm = (to_dev_bf16(w.activations()) for w in (lin, lr, mlp))
+    Yl = torch.empty((lin.M, lin.N), dtype=bf, device="cuda")
+    Yr = torch.empty((lr.M, lr.N), dtype=bf, device="cuda")
+    Ym = torch.empty((mlp.M, mlp.N), dtype=bf, device="cuda")
+    wsl = u8(cr.convrot_linear_workspace_bytes(lin.M, lin.K, lin.N, lin.block))
+    wsr = u8(cr.lowrank_convrot_workspace_bytes(lr.M, lr.K, lr.rank, lr.N, lr.block))
+    wsm = u8(cr.convrot_mlp_workspace_bytes(mlp.M, mlp.K, mlp.ffn, mlp.N, mlp.block))
+
+    def calls():
+        cr.convrot_linear_forward(Xl, pl, bias=bias, out=Yl, workspace=wsl)
+        cr.lowrank_convrot_forward(Xr, pa, pb, out=Yr, workspace=wsr)
+        cr.convrot_mlp_forward(Xm, pu, pd, out=Ym, workspace=wsm)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        for X, w in ((Xl, lin), (Xr, lr), (Xm, mlp)):
+            x = rng.normal(0.0, 1.0 + rep, (w.M, w.K)).astype(np.float32)
+            X.copy_(to_dev_bf16(wl.f32_to_bf16_bits(x)))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [bf16_bits(Y) for Y in (Yl, Yr, Ym)]
+        want = [bf16_bits(cr.convrot_linear_forward(Xl, pl, bias=bias)),
+                bf16_bits(cr.lowrank_convrot_forward(Xr, pa, pb)),
+                bf16_bits(cr.convrot_mlp_forward(Xm, pu, pd))]
+        torch.cuda.synchronize()
+        for name, a, b in zip(("linear", "low-rank", "MLP"), got, want):
+            assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager call"
+    print("[parity] graph replays: 3 x 3 forwards equal to eager", flush=True)

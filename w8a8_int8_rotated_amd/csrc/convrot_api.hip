@@ -4,25 +4,30 @@
 #include "convrot.h"
 #include "common.hpp"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 #include <cstdio>
+#include <cstdlib>
 
 namespace convrot {
 
 int device_cu_count()
 {
-    // one entry per device ordinal; a race only repeats the same query
-    static int cached[64] = {};
+    // one entry per device ordinal; threads racing on a first query store
+    // the same value
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
         n = 256;
-    if (dev < 64) cached[dev] = n;
+    if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
