@@ -606,3 +606,44 @@ def test_graph_capture_replays(cr):
         for name, a, b in zip(("linear", "low-rank", "MLP"), got, want):
             assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager call"
     print("[parity] graph replays: 3 x 3 forwards equal to eager", flush=True)
+
+
+def _sweep_cases(n, seed=2024):
+    """Seeded random linear configurations: M, K, N, block, rotation kind,
+    output type, bias, activation distribution."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rot = "regular" if rng.random() < 0.3 else "sylvester"
+        b = int(rng.choice([64, 256] if rot == "regular" else [64, 128, 256]))
+        K = int(rng.integers(1, 97)) * 128          # up to 12288: every rotquant kernel
+        if K % b:
+            K = (K // b + 1) * b
+        N = int(rng.integers(1, 97)) * 16
+        M = max(1, min(int(rng.integers(1, 1500)), int(1.5e10 / (K * N))))
+        cases.append(dict(M=M, K=K, N=N,
+                          b=b, rot=rot, out=str(rng.choice(["bf16", "f32"])),
+                          bias=bool(rng.random() < 0.5),
+                          dist=str(rng.choice(["normal", "student_t4"])), seed=1000 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(24), ids=lambda c: "M{M}_K{K}_N{N}_b{b}_{rot}_{out}".format(**c))
+def test_linear_random_sweep(cr, case):
+    """Random shapes, blocks, rotation kinds, output types and bias through
+    prepare + forward: weight codes, then outputs, against the oracle."""
+    c = case
+    announce(f"sweep {c}")
+    w = wl.Workload("sweep", "linear", M=c["M"], K=c["K"], N=c["N"], block=c["b"], out=c["out"],
+                    x_dist=c["dist"], outlier_frac=0.01, outlier_gain=20,
+                    bias_std=0.05 if c["bias"] else None, seed=c["seed"])
+    x, W, bias = w.activations(), w.weight(), w.bias()
+    pw = cr.convrot_linear_prepare_weights(to_dev(W), c["b"], rotation=c["rot"])
+    qw, sw = oracle.prepare_weights(W, c["b"], rot=c["rot"])
+    assert np.array_equal(untile(pw.codes, *qw.shape), qw) and np.array_equal(host(pw.scale), sw)
+    y = cr.convrot_linear_forward(to_dev_bf16(x), pw,
+                                  bias=None if bias is None else to_dev(bias),
+                                  out_dtype=torch.float32 if c["out"] == "f32" else torch.bfloat16)
+    y_ref = oracle.linear_forward(x, qw, sw, c["b"], bias=bias, out=c["out"], rot=c["rot"])
+    yh = host(y) if c["out"] == "f32" else bf16_bits(y)
+    assert assert_output_parity(yh, y_ref, c["out"], "sweep") == 0
