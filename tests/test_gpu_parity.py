@@ -647,3 +647,52 @@ def test_linear_random_sweep(cr, case):
     y_ref = oracle.linear_forward(x, qw, sw, c["b"], bias=bias, out=c["out"], rot=c["rot"])
     yh = host(y) if c["out"] == "f32" else bf16_bits(y)
     assert assert_output_parity(yh, y_ref, c["out"], "sweep") == 0
+
+
+def _chain_cases(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rot = "regular" if rng.random() < 0.3 else "sylvester"
+        b = int(rng.choice([64, 256] if rot == "regular" else [64, 128, 256]))
+        step = max(b, 128)
+        c = dict(kind=kind, M=int(rng.integers(1, 700)), K=int(rng.integers(1, 25)) * step,
+                 N=int(rng.integers(1, 65)) * 16, b=b, rot=rot,
+                 out=str(rng.choice(["bf16", "f32"])), bias=bool(rng.random() < 0.5),
+                 seed=2000 + 17 * i + (kind == "mlp"))
+        # low-rank: r a multiple of 128 and of b (the fused factor 1 for
+        # b <= 128 and r <= 512); MLP: the hidden width
+        c["r"] = int(rng.integers(1, 7)) * step
+        cases.append(c)
+    return cases
+
+
+@pytest.mark.parametrize("case", _chain_cases("lowrank", 8, 77) + _chain_cases("mlp", 8, 78),
+                         ids=lambda c: "{kind}_M{M}_K{K}_r{r}_N{N}_b{b}_{rot}_{out}".format(**c))
+def test_chain_random_sweep(cr, case):
+    """Seeded random low-rank chains (rank r) and MLP pairs (hidden width r):
+    every block and rotation kind, both outputs, bias on and off, against
+    the oracle (the MLP's down projection gets the bias)."""
+    c = case
+    announce(f"chain sweep {c}")
+    rng = np.random.default_rng(c["seed"])
+    x = wl.f32_to_bf16_bits(rng.standard_t(4, (c["M"], c["K"])).astype(np.float32))
+    W1 = rng.normal(0, 0.02, (c["r"], c["K"])).astype(np.float32)
+    W2 = rng.normal(0, 0.02, (c["N"], c["r"])).astype(np.float32)
+    bias = rng.normal(0, 0.05, c["N"]).astype(np.float32) if c["bias"] else None
+    p1 = cr.convrot_linear_prepare_weights(to_dev(W1), c["b"], rotation=c["rot"])
+    p2 = cr.convrot_linear_prepare_weights(to_dev(W2), c["b"], rotation=c["rot"])
+    q1, s1 = oracle.prepare_weights(W1, c["b"], rot=c["rot"])
+    q2, s2 = oracle.prepare_weights(W2, c["b"], rot=c["rot"])
+    od = torch.float32 if c["out"] == "f32" else torch.bfloat16
+    bd = None if bias is None else to_dev(bias)
+    if c["kind"] == "lowrank":
+        y = cr.lowrank_convrot_forward(to_dev_bf16(x), p1, p2, bias=bd, out_dtype=od)
+        y_ref = oracle.lowrank_forward(x, q1, s1, q2, s2, c["b"], bias=bias, out=c["out"],
+                                       rot=c["rot"])
+    else:
+        y = cr.convrot_mlp_forward(to_dev_bf16(x), p1, p2, bias_down=bd, out_dtype=od)
+        y_ref = oracle.mlp_forward(x, q1, s1, q2, s2, c["b"], bias_down=bias, out=c["out"],
+                                   rot=c["rot"])
+    yh = host(y) if c["out"] == "f32" else bf16_bits(y)
+    assert assert_output_parity(yh, y_ref, c["out"], f"{c['kind']} sweep") == 0
