@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of the step captured in a HIP graph")
+    p.add_argument("--evict-mib", type=int, default=0,
+                   help="write this many MiB of scratch before each timed step (cold caches)")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured MFMA and HBM ceilings")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -150,7 +154,7 @@ def setup(w, cr, torch, np, dev):
         sx = torch.empty(M, dtype=torch.float32, device=dev)
 
         def step():
-            cr.convrot_linear_forward(X, pw, bias=bias_d, out=Y, workspace=ws, stream=stream)
+            cr.convrot_linear_forward(X, pw, bias=bias_d, out=Y, workspace=ws)
 
         stages = [
             Stage("rotquant (FWHT + absmax + INT8 codes)", "rotquant",
@@ -176,7 +180,7 @@ def setup(w, cr, torch, np, dev):
         sh = torch.empty(M, dtype=torch.float32, device=dev)
 
         def step():
-            cr.lowrank_convrot_forward(X, pa, pb, out=Y, workspace=ws, stream=stream)
+            cr.lowrank_convrot_forward(X, pa, pb, out=Y, workspace=ws)
 
         stages = [
             Stage("rotquant X", "rotquant",
@@ -220,7 +224,7 @@ def setup(w, cr, torch, np, dev):
         sg = torch.empty(M, dtype=torch.float32, device=dev)
 
         def step():
-            cr.convrot_mlp_forward(X, pu, pd, out=Y, workspace=ws, stream=stream)
+            cr.convrot_mlp_forward(X, pu, pd, out=Y, workspace=ws)
 
         stages = [
             Stage("rotquant X", "rotquant",
@@ -245,7 +249,7 @@ def setup(w, cr, torch, np, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1 "
                                    "(the forward shards along tokens with no exchange, "
                                    "see the design notes)"}))
         sys.exit(2)
@@ -280,19 +284,54 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # the step recorded once into a HIP graph and replayed: one launch per
+        # step instead of one per kernel (the calls allocate, synchronise and
+        # clear nothing, so they record as they run)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        step = graph.replay
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` forward calls ----
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # ---- timed region: exactly `steps` forward calls, an event after each ----
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    scratch = (torch.empty(args.evict_mib << 20, dtype=torch.uint8, device=dev)
+               if args.evict_mib else None)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    if scratch is None:
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    else:
+        # cold caches: a scratch write evicts the last-level cache before
+        # each step, outside that step's events
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.fill_(i & 0xff)
+            evs[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        per_step = [evs[i].elapsed_time(ends[i]) for i in range(args.steps)]
     wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = sum(per_step) / args.steps
+    srt = sorted(per_step)
+    step_stats = {"median": round(srt[len(srt) // 2], 5), "min": round(srt[0], 5),
+                  "p90": round(srt[min(len(srt) - 1, int(0.9 * len(srt)))], 5),
+                  "cold_caches": scratch is not None}
     tops = ops / (ms_per_step * 1e-3) / 1e12
     log(f"forward: {ms_per_step:.4f} ms/step, {tops:.1f} TOPS (wall {wall:.3f}s)")
 
@@ -344,6 +383,8 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
+        "step_ms": step_stats,
+        "launch": "hipGraph replay" if args.graph else "eager",
         "roofline": dominant.roofline(w.name),
         "roofline_rotquant": first_rq.roofline(w.name),
         "kernels": [s.roofline(w.name) for s in stages],
@@ -354,9 +395,11 @@ def main():
         ceil = ceilings(cr, torch, dev, stream, stages, first_rq)
         result["ceilings"] = ceil
         for r, st in ((result["roofline"], dominant), (result["roofline_rotquant"], first_rq)):
-            c = ceil["mfma_i8_changing_operands" if st.bound == "mfma"
-                     else "hbm_stream_rotquant_shape"]["value"]
-            r["frac_of_measured_ceiling"] = round(r["achieved"] / c, 4)
+            key = ("mfma_i8_changing_operands" if st.bound == "mfma" else
+                   "hbm_stream_rotquant_shape" if st.kernel == "rotquant" else
+                   "hbm_write_stream")        # a GEMM bound by its output stores
+            r["measured_ceiling"] = key
+            r["frac_of_measured_ceiling"] = round(r["achieved"] / ceil[key]["value"], 4)
 
     if w.kind == "lowrank":
         result["comparison"] = bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream,
@@ -403,8 +446,20 @@ def ceilings(cr, torch, dev, stream, stages, first_rq):
         times.append(e0.elapsed_time(e1))
     ms = sorted(times)[len(times) // 2]
     gbs = 24.0 * n16 / (ms * 1e-3) / 1e9
+    # writes only, 1 GiB (the traffic of a GEMM whose output dominates)
+    wdst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    times = []
+    for _ in range(5):
+        stages[-1].fn()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        cr.convrot_probe_stream(None, wdst, 2, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    wgbs = float(1 << 30) / (sorted(times)[len(times) // 2] * 1e-3) / 1e9
     log(f"ceilings: INT8 MFMA {mfma:.0f} TOPS on changing operands; "
-        f"streaming {gbs:.0f} GB/s with the rotquant traffic shape")
+        f"streaming {gbs:.0f} GB/s with the rotquant traffic shape, {wgbs:.0f} GB/s writes only")
     return {
         "mfma_i8_changing_operands": {
             "value": round(mfma, 1), "unit": "TOPS",
@@ -415,6 +470,11 @@ def ceilings(cr, torch, dev, stream, stages, first_rq):
             "value": round(gbs, 1), "unit": "GB/s",
             "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": 24.0 * n16,
             "probe": "16 B non-temporal load, 8 B store per item, grid-stride; each run right "
+                     "after the step's last kernel; median of 5"},
+        "hbm_write_stream": {
+            "value": round(wgbs, 1), "unit": "GB/s",
+            "frac_of_spec": round(wgbs / PEAK_HBM_GBS, 4), "bytes_per_launch": float(1 << 30),
+            "probe": "16 B store per item over 1 GiB, grid-stride, nothing read; each run right "
                      "after the step's last kernel; median of 5"},
     }
 

@@ -320,11 +320,12 @@ CONVROT_API int convrot_gelu_bf16(const uint16_t *u, int64_t n, uint16_t *g, voi
 CONVROT_API int convrot_probe_mfma_i8(int64_t iters, const void *seed, void *sink,
                                       int64_t *ops, void *stream);
 
-/* Streaming probe with the rotate+quantise traffic shape and no arithmetic:
- * for each 16-byte item i < n16 of src, mode 0 writes 8 bytes to dst + 8 i
- * (the xor of input words 0 and 1, then of words 2 and 3), mode 1 copies the
- * 16 bytes to dst + 16 i.  Device pointers, 16-byte aligned, not
- * overlapping. */
+/* Streaming probe with no arithmetic, over n16 16-byte items: mode 0 (the
+ * rotate+quantise traffic shape) reads item i of src and writes 8 bytes to
+ * dst + 8 i (the xor of input words 0 and 1, then of words 2 and 3); mode 1
+ * copies the 16 bytes to dst + 16 i; mode 2 reads nothing (src may be NULL)
+ * and writes the low 32 bits of i to all four words of dst + 16 i.  Device
+ * pointers, 16-byte aligned, not overlapping. */
 CONVROT_API int convrot_probe_stream(const void *src, void *dst, int64_t n16, int mode,
                                      void *stream);
 

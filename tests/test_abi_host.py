@@ -255,7 +255,8 @@ def test_gelu_and_probe_validation(cr):
                                                                                None)
     assert stream(n=0, src=None, dst=None) == cr.OK
     assert stream(n=-1) == cr.EINVAL
-    assert stream(mode=2) == cr.EINVAL
+    assert stream(mode=3) == cr.EINVAL
+    assert stream(mode=0, src=None) == cr.EINVAL
     assert stream(dst=None) == cr.EINVAL
     assert stream(src=FAKE_ODD) == cr.EALIGN
 

@@ -546,6 +546,9 @@ def test_measurement_probes(cr):
     dst16 = torch.zeros_like(src)
     cr.convrot_probe_stream(src, dst16, 1)
     assert torch.equal(dst16, src)
+    cr.convrot_probe_stream(None, dst16, 2)
+    idx = np.arange(src.numel() // 4, dtype=np.int64).astype(np.int32)
+    assert np.array_equal(host(dst16).reshape(-1, 4), np.repeat(idx[:, None], 4, 1))
     seed = torch.randint(-2**31, 2**31 - 1, (1024,), dtype=torch.int32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     ops = cr.convrot_probe_mfma_i8(8, seed, sink)

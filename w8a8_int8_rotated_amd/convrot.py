@@ -429,14 +429,18 @@ def convrot_probe_mfma_i8(iters: int, seed: torch.Tensor, sink: torch.Tensor,
     return ops.value
 
 
-def convrot_probe_stream(src: torch.Tensor, dst: torch.Tensor, mode: int, stream=None):
-    """Streaming probe over src's 16-byte items: mode 0 writes 8 bytes per
-    item into dst, mode 1 copies all 16."""
+def convrot_probe_stream(src, dst: torch.Tensor, mode: int, stream=None):
+    """Streaming probe: mode 0 reads src's 16-byte items and writes 8 bytes
+    per item into dst, mode 1 copies them, mode 2 (src None) only writes all
+    of dst's 16-byte items."""
     lib = library()
-    nbytes = src.numel() * src.element_size()
-    n16 = nbytes // 16
-    if nbytes % 16 or dst.numel() * dst.element_size() < n16 * (8 if mode == 0 else 16):
-        raise ValueError("src must be whole 16-byte items and dst large enough")
-    _check("convrot_probe_stream", lib.convrot_probe_stream(_ptr(src), _ptr(dst), n16, mode,
-                                                            _stream(stream)))
+    if mode == 2:
+        n16 = dst.numel() * dst.element_size() // 16
+    else:
+        nbytes = src.numel() * src.element_size()
+        n16 = nbytes // 16
+        if nbytes % 16 or dst.numel() * dst.element_size() < n16 * (8 if mode == 0 else 16):
+            raise ValueError("src must be whole 16-byte items and dst large enough")
+    _check("convrot_probe_stream", lib.convrot_probe_stream(
+        None if src is None else _ptr(src), _ptr(dst), n16, mode, _stream(stream)))
     return dst

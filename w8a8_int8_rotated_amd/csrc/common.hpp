@@ -97,10 +97,11 @@ hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
 
 // Measurement probes (probes.hip): INT8 MFMA rounds on changing operands, one
 // workgroup per CU (probe_mfma_i8_ops: the INT8 operations of one launch),
-// and a streaming copy of n16 16-byte items (narrow: 8 bytes out per item).
+// and a streaming pass over n16 16-byte items (mode 0: 8 bytes out per item,
+// 1: a copy, 2: writes only).
 int64_t probe_mfma_i8_ops(int64_t iters);
 hipError_t launch_probe_mfma_i8(int64_t iters, const int *seed, int *sink, hipStream_t stream);
-hipError_t launch_probe_stream(const void *src, void *dst, int64_t n16, bool narrow,
+hipError_t launch_probe_stream(const void *src, void *dst, int64_t n16, int mode,
                                hipStream_t stream);
 
 } // namespace convrot

@@ -500,11 +500,11 @@ int convrot_probe_mfma_i8(int64_t iters, const void *seed, void *sink, int64_t *
 
 int convrot_probe_stream(const void *src, void *dst, int64_t n16, int mode, void *stream)
 {
-    if (n16 < 0 || (mode != 0 && mode != 1)) return CONVROT_EINVAL;
+    if (n16 < 0 || mode < 0 || mode > 2) return CONVROT_EINVAL;
     if (n16 == 0) return CONVROT_OK;
-    if (!src || !dst) return CONVROT_EINVAL;
-    if (!aligned16(src) || !aligned16(dst)) return CONVROT_EALIGN;
-    return hip_status(convrot::launch_probe_stream(src, dst, n16, mode == 0,
+    if ((!src && mode != 2) || !dst) return CONVROT_EINVAL;
+    if ((src && !aligned16(src)) || !aligned16(dst)) return CONVROT_EALIGN;
+    return hip_status(convrot::launch_probe_stream(src, dst, n16, mode,
                                                    static_cast<hipStream_t>(stream)));
 }
 

@@ -7,8 +7,9 @@
 //    than constant ones, so this rate, not 5.0 POP/s, is what a GEMM can
 //    approach on this part.
 //  - stream_probe: a streaming kernel with the rotate+quantise traffic shape
-//    (16 bytes read, 8 written per item; or a plain 16-byte copy) and no
-//    arithmetic, i.e. what HBM delivers to that access pattern.
+//    (16 bytes read, 8 written per item), a plain 16-byte copy, or writes
+//    only (the traffic of a GEMM whose output dominates), with no arithmetic:
+//    what HBM delivers to that access pattern.
 #include "common.hpp"
 
 #include <algorithm>
@@ -71,15 +72,21 @@ __global__ __launch_bounds__(kProbeThreads, 1) void mfma_i8_probe(int64_t iters,
 }
 
 // Grid-stride streaming: item i reads 16 bytes of src (non-temporal) and
-// writes 8 (NARROW, two xors of the input words) or all 16 bytes to dst.
-template <bool NARROW>
+// writes 8 (MODE 0: two xors of the input words) or all 16 bytes (MODE 1) to
+// dst; MODE 2 reads nothing and writes the item index to all 16 bytes.
+template <int MODE>
 __global__ __launch_bounds__(kProbeThreads) void stream_probe(const v4i *__restrict__ src,
                                                               void *__restrict__ dst, int64_t n16)
 {
     const int64_t stride = (int64_t)gridDim.x * kProbeThreads;
     for (int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x; i < n16; i += stride) {
+        if constexpr (MODE == 2) {
+            const int lo = (int)i;
+            static_cast<v4i *>(dst)[i] = (v4i){lo, lo, lo, lo};
+            continue;
+        }
         const v4i d = __builtin_nontemporal_load(&src[i]);
-        if constexpr (NARROW) {
+        if constexpr (MODE == 0) {
             v2i o;
             o[0] = d[0] ^ d[1];
             o[1] = d[2] ^ d[3];
@@ -104,19 +111,23 @@ hipError_t launch_probe_mfma_i8(int64_t iters, const int *seed, int *sink, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_probe_stream(const void *src, void *dst, int64_t n16, bool narrow,
+hipError_t launch_probe_stream(const void *src, void *dst, int64_t n16, int mode,
                                hipStream_t stream)
 {
     if (n16 == 0) return hipSuccess;
     // 64 workgroups per CU, each thread walking items a grid apart
     const int64_t blocks = std::min<int64_t>((int64_t)device_cu_count() * 64,
                                              (n16 + kProbeThreads - 1) / kProbeThreads);
-    if (narrow)
-        hipLaunchKernelGGL(stream_probe<true>, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
-                           stream, static_cast<const v4i *>(src), dst, n16);
+    const auto s = static_cast<const v4i *>(src);
+    if (mode == 0)
+        hipLaunchKernelGGL(stream_probe<0>, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
+                           stream, s, dst, n16);
+    else if (mode == 1)
+        hipLaunchKernelGGL(stream_probe<1>, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
+                           stream, s, dst, n16);
     else
-        hipLaunchKernelGGL(stream_probe<false>, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
-                           stream, static_cast<const v4i *>(src), dst, n16);
+        hipLaunchKernelGGL(stream_probe<2>, dim3((unsigned)blocks), dim3(kProbeThreads), 0,
+                           stream, s, dst, n16);
     return hipGetLastError();
 }
 
