@@ -23,6 +23,7 @@ import argparse
 import collections
 import csv
 import hashlib
+import json
 import sys
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -33,17 +34,45 @@ def _short(name: str) -> str:
     return name.split("(")[0]
 
 
+def _medians(trace_csv):
+    """Median dispatch duration (ns) per kernel name, from the kernel trace."""
+    d = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        d[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: sorted(v)[len(v) // 2] for k, v in d.items()}
+
+
+def _bench_line(log):
+    """The JSON line bench.py printed in the profiled run."""
+    for line in reversed(open(log, errors="replace").read().splitlines()):
+        if line.startswith('{"metric"'):
+            return json.loads(line)
+    return None
+
+
 def stats(args):
     rows = list(csv.DictReader(open(args.csv)))
+    med = _medians(args.trace) if args.trace else {}
     out = [f"# Kernel durations -- {args.workload}", "",
            "Command (run from /tmp, repository at $R):", "", "```", args.command, "```", "",
-           "| kernel | calls | average (us) | min (us) | max (us) | share |",
-           "|---|---:|---:|---:|---:|---:|"]
+           "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
+        m = med.get(r["Name"])
         out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{'' if m is None else f'{m / 1e3:.1f}'} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                    f"{float(r['Percentage']):.1f}% |")
     out.append("")
+    bl = _bench_line(args.bench_log) if args.bench_log else None
+    if bl:
+        out += ["The averages include the warm-up dispatches; the medians are the steady "
+                "state.  The same run's bench.py line timed each stage with HIP events "
+                "between the stages (one stage can be several kernels, e.g. a GEMM and "
+                "its tail launch):", ""]
+        out += [f"- {k['kernel']}: {k['avg_launch_ms'] * 1e3:.1f} us per call"
+                for k in bl["kernels"]]
+        out.append("")
     text = "\n".join(out)
     _emit(text, args.output)
 
@@ -168,6 +197,8 @@ def main():
     s.add_argument("csv")
     s.add_argument("--command", required=True)
     s.add_argument("--workload", required=True)
+    s.add_argument("--trace", help="run_kernel_trace.csv of the same run (medians)")
+    s.add_argument("--bench-log", help="the profiled run's output (its bench.py JSON line)")
     s.add_argument("-o", "--output")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
