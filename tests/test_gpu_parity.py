@@ -484,6 +484,21 @@ def test_gelu_exhaustive(cr):
     assert not diff.any(), [hex(int(x)) for x in u[diff][:8]]
 
 
+def test_gelu_hook_alignment_and_tail(cr):
+    """The elementwise GELU hook on every bf16 pattern in a seeded order:
+    16-byte-aligned buffers (8 values per thread from the LDS slice) with a
+    ragged tail, and buffers offset by one element (one value per thread)."""
+    announce("gelu hook: aligned, ragged tail, misaligned")
+    u = np.random.default_rng(3).permutation(65536).astype(np.uint16)
+    ud = to_dev_bf16(u)
+    nan = lambda a: ((a & 0x7f80) == 0x7f80) & ((a & 0x007f) != 0)
+    for lo, hi in ((0, 65536), (0, 65533), (1, 65536), (5, 60007)):
+        g = bf16_bits(cr.convrot_gelu_bf16(ud[lo:hi]))
+        g_ref = oracle.gelu_bf16(u[lo:hi])
+        diff = (g != g_ref) & ~(nan(g) & nan(g_ref))
+        assert not diff.any(), (lo, hi, int(diff.sum()))
+
+
 def test_gelu_epilogue_every_pattern(cr):
     """Every bf16 pattern of u -- zero, denormals, the range the epilogue
     looks up in LDS, huge values, inf and NaN -- through the up projection's

@@ -215,6 +215,38 @@ __device__ __forceinline__ uint32_t gelu_pair_lds(uint32_t u2, u16x2 &mx)
     return (uint32_t)g_gelu_lds[idx.x] | ((uint32_t)g_gelu_lds[idx.y] << 16);
 }
 
+// g = bf16(GELU(u)) for 8 consecutive values per thread (one 16-byte load
+// and store), from the LDS slice of the table; a thread holding a value
+// outside the slice redoes its 8 values from the full table.  Grid-stride
+// over n8 groups; each workgroup fills its LDS slice once.
+__global__ __launch_bounds__(256) void gelu_apply8_kernel(const uint4 *__restrict__ u,
+                                                          uint4 *__restrict__ g, int64_t n8)
+{
+    for (int i = threadIdx.x; i < 2 * kGeluSpan; i += 256) {
+        const int neg = i >= kGeluSpan;
+        g_gelu_lds[i] = g_gelu_bf16[(neg << 15) | (i - neg * kGeluSpan + kGeluLo)];
+    }
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(u) + i);
+        u16x2 mx = (u16x2)(0);
+        uint4 o;
+        o.x = gelu_pair_lds(x[0], mx);
+        o.y = gelu_pair_lds(x[1], mx);
+        o.z = gelu_pair_lds(x[2], mx);
+        o.w = gelu_pair_lds(x[3], mx);
+        if (mx.x >= kGeluSpan || mx.y >= kGeluSpan) {
+            o.x = gelu_pair(x[0]);
+            o.y = gelu_pair(x[1]);
+            o.z = gelu_pair(x[2]);
+            o.w = gelu_pair(x[3]);
+        }
+        g[i] = o;
+    }
+}
+
 // Dequantise and store a wave's 128 (n) x 32 TJ (m) block.  FULL: the tile
 // lies inside [M, N], so no per-lane bounds checks are needed.
 //
@@ -1183,8 +1215,19 @@ hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream
 {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
-    hipLaunchKernelGGL(gelu_apply_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                       u, g, n);
+    // 16-byte aligned buffers: 8 values per thread from the LDS slice, the
+    // last n % 8 one per thread; otherwise one per thread throughout
+    const bool vec = ((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(g)) & 15) == 0;
+    const int64_t n8 = vec ? n / 8 : 0;
+    if (n8 > 0) {
+        const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, (int64_t)device_cu_count() * 4);
+        hipLaunchKernelGGL(gelu_apply8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const uint4 *>(u), reinterpret_cast<uint4 *>(g), n8);
+    }
+    const int64_t rest = n - 8 * n8;
+    if (rest > 0)
+        hipLaunchKernelGGL(gelu_apply_kernel, dim3((unsigned)((rest + 255) / 256)), dim3(256), 0,
+                           stream, u + 8 * n8, g + 8 * n8, rest);
     return hipGetLastError();
 }
 
