@@ -83,7 +83,8 @@ int hip_status(hipError_t e)
 int check_linear_shape(int64_t N, int64_t K, int block)
 {
     if (N <= 0 || K <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
-    if (K % 128 != 0 || N % 16 != 0 || K > kMaxK || N * K >= kI32Bound)
+    // N is bounded before the product, so it cannot overflow
+    if (K % 128 != 0 || N % 16 != 0 || K > kMaxK || N >= kI32Bound || N * K >= kI32Bound)
         return CONVROT_EUNSUPPORTED;
     return CONVROT_OK;
 }
@@ -105,7 +106,8 @@ int check_weights(const convrot_weights *W)
 int check_rows(int64_t M, int64_t K)
 {
     if (M < 0) return CONVROT_EINVAL;
-    if (convrot::padded_rows(M) * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    // K <= 65536 here; M is bounded before padding and product
+    if (M >= kI32Bound || convrot::padded_rows(M) * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
     return CONVROT_OK;
 }
 
@@ -177,14 +179,16 @@ size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block, int w_dt
 
 size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block)
 {
-    if (M < 0 || check_linear_shape(N, K, block) != CONVROT_OK) return 0;
+    if (check_linear_shape(N, K, block) != CONVROT_OK || check_rows(M, K) != CONVROT_OK)
+        return 0;
     return codes_bytes(M, K) + scales_bytes(M);
 }
 
 size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r, int64_t N, int block)
 {
-    if (M < 0 || check_linear_shape(r, K, block) != CONVROT_OK ||
-        check_linear_shape(N, r, block) != CONVROT_OK)
+    if (check_linear_shape(r, K, block) != CONVROT_OK ||
+        check_linear_shape(N, r, block) != CONVROT_OK || check_rows(M, K) != CONVROT_OK ||
+        check_rows(M, r) != CONVROT_OK)
         return 0;
     return codes_bytes(M, K) + scales_bytes(M) + round_up((size_t)M * (size_t)r * 2u, kAlign) +
            codes_bytes(M, r) + scales_bytes(M);
@@ -192,8 +196,9 @@ size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r, int64_t 
 
 size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N, int block)
 {
-    if (M < 0 || check_linear_shape(F, K, block) != CONVROT_OK ||
-        check_linear_shape(N, F, block) != CONVROT_OK)
+    if (check_linear_shape(F, K, block) != CONVROT_OK ||
+        check_linear_shape(N, F, block) != CONVROT_OK || check_rows(M, K) != CONVROT_OK ||
+        check_rows(M, F) != CONVROT_OK)
         return 0;
     return codes_bytes(M, K) + scales_bytes(M) + round_up((size_t)M * (size_t)F * 2u, kAlign) +
            codes_bytes(M, F) + scales_bytes(M);
@@ -375,7 +380,7 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
 
 size_t lowrank_bf16_workspace_bytes(int64_t M, int64_t r)
 {
-    if (M < 0 || r <= 0) return 0;
+    if (M < 0 || r <= 0 || r > kMaxK || M >= kI32Bound || M * 2 * r >= kI32Bound) return 0;
     return round_up((size_t)M * (size_t)r * 2u, kAlign);
 }
 
@@ -386,8 +391,8 @@ int lowrank_bf16_forward(const void *X, int64_t M, int64_t K, const void *A, int
     if (M < 0 || K <= 0 || r <= 0 || N <= 0) return CONVROT_EINVAL;
     if (K % 64 != 0 || r % 64 != 0 || N % 16 != 0 || K > kMaxK || r > kMaxK)
         return CONVROT_EUNSUPPORTED;
-    if (M * 2 * K >= kI32Bound || M * 2 * r >= kI32Bound || N * 2 * K >= kI32Bound ||
-        N * 2 * r >= kI32Bound)
+    if (M >= kI32Bound || N >= kI32Bound || M * 2 * K >= kI32Bound || M * 2 * r >= kI32Bound ||
+        N * 2 * K >= kI32Bound || N * 2 * r >= kI32Bound)
         return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!X || !A || !B || !Y) return CONVROT_EINVAL;
@@ -414,7 +419,7 @@ int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, in
     if ((flags & ~CONVROT_ROT_REGULAR) != 0) return CONVROT_EUNSUPPORTED;
     if (!valid_rotation(flags, block)) return CONVROT_EINVAL;
     if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
-    if (K > kMaxK || convrot::padded_rows(M) * K >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    if (K > kMaxK || check_rows(M, K) != CONVROT_OK) return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!X || !q || !s_out) return CONVROT_EINVAL;
     if (!aligned16(X) || !aligned16(q) || !aligned16(s_out)) return CONVROT_EALIGN;
