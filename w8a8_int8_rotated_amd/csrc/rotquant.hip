@@ -487,9 +487,10 @@ __global__ __launch_bounds__(NW * 64) void rotquant_stream_kernel(
                 for (int j = 0; j < 8; ++j) v[t][j] = __int_as_float(raw[t][j]);
             }
         }
-        // next group (or this one again on the last pass: its loads are
-        // harmless and keep the sequence uniform)
-        issue(gi + gridDim.x < ngroups ? gi + gridDim.x : gi);
+        // next group; on the last pass a group past the end, whose rows are
+        // out of range: its loads read an empty buffer (zeros, no memory
+        // traffic) and keep the sequence of memory operations uniform
+        issue(gi + gridDim.x);
 
         float m = 0.0f;
 #pragma unroll
@@ -638,9 +639,10 @@ __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
                 for (int j = 0; j < 8; ++j) v[t][j] = __int_as_float(raw[t][j]);
             }
         }
-        // next group (or this one again on the last pass: its loads are
-        // harmless and keep the sequence uniform)
-        issue(gi + gridDim.x < ngroups ? gi + gridDim.x : gi);
+        // next group; on the last pass a group past the end, whose rows are
+        // out of range: its loads read an empty buffer (zeros, no memory
+        // traffic) and keep the sequence of memory operations uniform
+        issue(gi + gridDim.x);
 
         float m = 0.0f;
 #pragma unroll
