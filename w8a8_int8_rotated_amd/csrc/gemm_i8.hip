@@ -466,6 +466,17 @@ __device__ __forceinline__ TileSrc tile_src(const int8_t *qw, const int8_t *qx, 
     return t;
 }
 
+// The copy source after a workgroup's last tile: empty ranges, so the copies
+// the pipeline issues ahead for a next tile read zeros without memory
+// traffic (their LDS stages are never read).
+__device__ __forceinline__ TileSrc empty_src(const int8_t *qw, const int8_t *qx)
+{
+    TileSrc t;
+    t.w = __builtin_amdgcn_make_buffer_rsrc((void *)qw, (short)0, 0, kRsrcWord3);
+    t.x = __builtin_amdgcn_make_buffer_rsrc((void *)qx, (short)0, 0, kRsrcWord3);
+    return t;
+}
+
 // Copy j of wave w moves rows [(n w + j) 16, +16) of an operand tile of 64 n
 // rows (n = 4 for the 256-row weight tile, TJ for the activation tile): the
 // 1 KiB tile of that row block, lane i its i-th 16 bytes.
@@ -770,7 +781,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     TileSrc cur = tile_src<MM>(qw, qx, m0, n0, M, N, K);
     int nm0 = m0, nn0 = n0;
     bool more = tile_at(1, nm0, nn0);
-    TileSrc nxt = more ? tile_src<MM>(qw, qx, nm0, nn0, M, N, K) : cur;
+    TileSrc nxt = more ? tile_src<MM>(qw, qx, nm0, nn0, M, N, K) : empty_src(qw, qx);
 
     for (int it = 0;; ++it) {
         v16i acc[4][TJ];
@@ -795,8 +806,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         wait_lds_reads();
         block_barrier();
         // stage S-1 is read by no one now: the next tile's K-tile S-1 goes
-        // out ahead of this tile's stores (the last tile re-reads its own,
-        // which no one consumes)
+        // out ahead of this tile's stores (after the last tile: from the empty
+        // source, no traffic)
         {
             int8_t *const wl = pick<S, S - 1>(sw0, sw1, sw2, sw3);
             int8_t *const xl = pick<S, S - 1>(sx0, sx1, sx2, sx3);
@@ -819,7 +830,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         cur = nxt;
         load_scales(m0, n0, sc_x, sc_w, sc_b);
         more = tile_at(it + 2, nm0, nn0);
-        if (more) nxt = tile_src<MM>(qw, qx, nm0, nn0, M, N, K);
+        nxt = more ? tile_src<MM>(qw, qx, nm0, nn0, M, N, K) : empty_src(qw, qx);
         // sscale is rewritten only after the next K loop's barriers
     }
     // No copy may still be writing LDS when the workgroup ends.
@@ -1062,7 +1073,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowrank_f1_kernel(
     TileSrc cur = src_of(t);
     int tn = t + gridDim.x;
     bool more = tn < tiles;
-    TileSrc nxt = more ? src_of(tn) : cur;
+    TileSrc nxt = more ? src_of(tn) : empty_src(qa, qx);
 
     for (int it = 0;; ++it) {
         v16i acc[4][TJ];
@@ -1096,7 +1107,7 @@ __global__ __launch_bounds__(kThreads, 1) void lowrank_f1_kernel(
         load_scales(t);
         tn = t + gridDim.x;
         more = tn < tiles;
-        if (more) nxt = src_of(tn);
+        nxt = more ? src_of(tn) : empty_src(qa, qx);
     }
     wait_vmcnt<0>();
 }
