@@ -714,3 +714,26 @@ def test_chain_random_sweep(cr, case):
                                    rot=c["rot"])
     yh = host(y) if c["out"] == "f32" else bf16_bits(y)
     assert assert_output_parity(yh, y_ref, c["out"], f"{c['kind']} sweep") == 0
+
+
+def test_nonfinite_rows_stay_local(cr):
+    """Non-finite inputs give unspecified values but stay in their own rows:
+    rows holding NaN or inf change nothing else, through the linear forward
+    and the MLP pair (whose GELU sees the NaN and inf patterns)."""
+    announce("non-finite rows: linear and MLP")
+    w = wl.scaled("mlp_16384", M=96, K=1024, N=512, ffn=1024)
+    x, Wu, Wd = w.activations(), w.weight("w"), w.weight("w2")
+    bad = {5: 0x7fc0, 17: 0x7f80, 40: 0xff80}            # NaN, +inf, -inf
+    xb = x.copy()
+    for r, pat in bad.items():
+        xb[r, 3] = pat
+    good = np.array([r for r in range(w.M) if r not in bad])
+    pu, qu, su = _prepare_pair(cr, Wu, w.block)
+    pd, qd, sd = _prepare_pair(cr, Wd, w.block)
+    y = bf16_bits(cr.convrot_linear_forward(to_dev_bf16(xb), pu))
+    y_ref = oracle.linear_forward(x[good], qu, su, w.block, out="bf16")
+    assert np.array_equal(y[good], y_ref)
+    ym = bf16_bits(cr.convrot_mlp_forward(to_dev_bf16(xb), pu, pd))
+    ym_ref = oracle.mlp_forward(x[good], qu, su, qd, sd, w.block, out="bf16")
+    assert np.array_equal(ym[good], ym_ref)
+    torch.cuda.synchronize()
