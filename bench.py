@@ -382,6 +382,9 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": cfg,
+        "inputs_sha256": {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()[:16]
+                          for k, v in host.items() if v is not None},
+        "env": environment(torch),
         "pct_int8_peak": round(100.0 * tops / PEAK_INT8_TOPS, 2),
         "step_ms": step_stats,
         "launch": "hipGraph replay" if args.graph else "eager",
@@ -409,6 +412,23 @@ def main():
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, w, host, Y)
 
     print(json.dumps(result), flush=True)
+
+
+def environment(torch):
+    """The device and host the numbers were taken on."""
+    import platform
+    props = torch.cuda.get_device_properties(0)
+    cpu = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       cpu)
+    except OSError:
+        pass
+    return {"gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", ""),
+            "compute_units": props.multi_processor_count,
+            "hbm_gib": round(props.total_memory / 2**30, 1), "hip": torch.version.hip,
+            "torch": torch.__version__, "host_cpu": cpu, "host_threads": os.cpu_count()}
 
 
 def ceilings(cr, torch, dev, stream, stages, first_rq):
