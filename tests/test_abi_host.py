@@ -268,3 +268,25 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(convrot, "_lib", None)
     with pytest.raises(ImportError):
         convrot.library()
+
+
+def test_call_log(cr):
+    """CONVROT_LOG=1 makes the main entry points print their name, shape and
+    status to stderr (checked on calls that fail validation, so nothing is
+    launched)."""
+    import subprocess
+    import sys
+    code = ("import ctypes; from w8a8_int8_rotated_amd import convrot as cr; "
+            "lib = cr.library(); "
+            "print(lib.convrot_linear_forward(None, 4, None, None, None, 1, None, 0, None)); "
+            "print(lib.lowrank_convrot_forward(None, -1, None, None, None, None, 1, None, 0, None))")
+    env = dict(os.environ, CONVROT_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "[convrot] convrot_linear_forward M=4 N=0 K=0 -> invalid argument" in r.stderr
+    assert "[convrot] lowrank_convrot_forward M=-1" in r.stderr
+    env["CONVROT_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=ROOT, timeout=120)
+    assert "[convrot]" not in r.stderr

@@ -140,6 +140,15 @@ size_t codes_bytes(int64_t M, int64_t K)
 }
 size_t scales_bytes(int64_t M) { return round_up((size_t)M * 4u, kAlign); }
 
+// With CONVROT_LOG=1 the main entry points also print their name, shape and
+// status to stderr.
+void log_call(const char *name, int64_t M, int64_t N, int64_t K, int rc)
+{
+    if (log_enabled())
+        std::fprintf(stderr, "[convrot] %s M=%lld N=%lld K=%lld -> %s\n", name, (long long)M,
+                     (long long)N, (long long)K, convrot_status_string(rc));
+}
+
 } // namespace
 
 extern "C" {
@@ -204,7 +213,7 @@ size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N, i
            codes_bytes(M, F) + scales_bytes(M);
 }
 
-int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
+static int prepare_weights_impl(const void *W, int w_dtype, int layout,
                                    const float *src_scale, int64_t N, int64_t K, int block,
                                    convrot_weights *out, void *ws, size_t ws_bytes, void *stream)
 {
@@ -255,7 +264,17 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
     return CONVROT_OK;
 }
 
-int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
+int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
+                                   const float *src_scale, int64_t N, int64_t K, int block,
+                                   convrot_weights *out, void *ws, size_t ws_bytes, void *stream)
+{
+    const int rc = prepare_weights_impl(W, w_dtype, layout, src_scale, N, K, block, out, ws,
+                                        ws_bytes, stream);
+    log_call("convrot_linear_prepare_weights", 0, N, K, rc);
+    return rc;
+}
+
+static int linear_forward_impl(const void *X, int64_t M, const convrot_weights *W,
                            const float *bias, void *Y, int y_dtype, void *ws, size_t ws_bytes,
                            void *stream)
 {
@@ -285,7 +304,16 @@ int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
     return hip_status(e);
 }
 
-int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
+int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
+                           const float *bias, void *Y, int y_dtype, void *ws, size_t ws_bytes,
+                           void *stream)
+{
+    const int rc = linear_forward_impl(X, M, W, bias, Y, y_dtype, ws, ws_bytes, stream);
+    log_call("convrot_linear_forward", M, W ? W->N : 0, W ? W->K : 0, rc);
+    return rc;
+}
+
+static int lowrank_forward_impl(const void *X, int64_t M, const convrot_weights *A,
                             const convrot_weights *B, const float *bias, void *Y, int y_dtype,
                             void *ws, size_t ws_bytes, void *stream)
 {
@@ -334,7 +362,16 @@ int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
     return hip_status(e);
 }
 
-int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
+int lowrank_convrot_forward(const void *X, int64_t M, const convrot_weights *A,
+                            const convrot_weights *B, const float *bias, void *Y, int y_dtype,
+                            void *ws, size_t ws_bytes, void *stream)
+{
+    const int rc = lowrank_forward_impl(X, M, A, B, bias, Y, y_dtype, ws, ws_bytes, stream);
+    log_call("lowrank_convrot_forward", M, B ? B->N : 0, A ? A->K : 0, rc);
+    return rc;
+}
+
+static int mlp_forward_impl(const void *X, int64_t M, const convrot_weights *W_up,
                         const float *bias_up, const convrot_weights *W_down,
                         const float *bias_down, void *Y, int y_dtype, void *ws, size_t ws_bytes,
                         void *stream)
@@ -376,6 +413,17 @@ int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
         e = convrot::launch_gemm_i8(qg, W_down->codes, sg, W_down->scale, bias_down, Y,
                                     out_kind(y_dtype), M, W_down->N, F, s);
     return hip_status(e);
+}
+
+int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
+                        const float *bias_up, const convrot_weights *W_down,
+                        const float *bias_down, void *Y, int y_dtype, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    const int rc = mlp_forward_impl(X, M, W_up, bias_up, W_down, bias_down, Y, y_dtype, ws,
+                                    ws_bytes, stream);
+    log_call("convrot_mlp_forward", M, W_down ? W_down->N : 0, W_up ? W_up->K : 0, rc);
+    return rc;
 }
 
 size_t lowrank_bf16_workspace_bytes(int64_t M, int64_t r)
