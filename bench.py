@@ -433,8 +433,9 @@ def environment(torch):
 
 def ceilings(cr, torch, dev, stream, stages, first_rq):
     """Ceilings measured with the library's probes, beside the spec peaks:
-    the INT8 MFMA rate on operands that change every round (the clock under a
-    sustained INT8 load is power-limited), and a streaming kernel with the
+    the sustained INT8 MFMA rate on operands that change every round, with
+    no memory traffic (the clock under a sustained INT8 load is
+    power-limited), and a streaming kernel with the
     first rotquant's traffic (its input's 16-byte items in, 8 bytes out per
     item, no arithmetic), each run right after the step's last kernel, as
     rotquant runs inside the step."""
@@ -442,15 +443,21 @@ def ceilings(cr, torch, dev, stream, stages, first_rq):
     seed = torch.randint(-2**31, 2**31 - 1, (1024,), dtype=torch.int32, device=dev,
                          generator=torch.Generator(device=dev).manual_seed(0))
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    # The clock takes tens of milliseconds to settle after a change of load:
+    # a few-millisecond launch right after the step measures the ramp, not the
+    # rate the power limit holds.  One untimed launch of about 0.1 s first,
+    # then the median of three more.
+    iters = 400_000
+    cr.convrot_probe_mfma_i8(iters, seed, sink, stream=stream)
     rates = []
     for _ in range(3):
         e0, e1 = ev(), ev()
         e0.record(stream)
-        ops = cr.convrot_probe_mfma_i8(20000, seed, sink, stream=stream)
+        ops = cr.convrot_probe_mfma_i8(iters, seed, sink, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         rates.append(ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
-    mfma = max(rates)
+    mfma = sorted(rates)[1]
 
     src = first_rq.src
     n16 = src.numel() * src.element_size() // 16
@@ -485,7 +492,8 @@ def ceilings(cr, torch, dev, stream, stages, first_rq):
             "value": round(mfma, 1), "unit": "TOPS",
             "frac_of_spec": round(mfma / PEAK_INT8_TOPS, 4),
             "probe": "v_mfma_i32_32x32x32_i8 rounds, one workgroup per CU, operands remixed "
-                     "every round; best of 3"},
+                     "every round; sustained: median of 3 launches of about 0.1 s after an "
+                     "untimed one"},
         "hbm_stream_rotquant_shape": {
             "value": round(gbs, 1), "unit": "GB/s",
             "frac_of_spec": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": 24.0 * n16,
