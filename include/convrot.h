@@ -262,7 +262,12 @@ CONVROT_API int lowrank_bf16_forward(const void *X, int64_t M, int64_t K, const 
 
 /* Rotate and quantise rows: X [M, K] row-major (x_dtype F32 or BF16) -> q
  * K-tiled int8 codes (Mp x K bytes; the padding rows are left as they were)
- * and s [M] F32.  flags: 0 or CONVROT_ROT_REGULAR (the rotation kind). */
+ * and s [M] F32.  flags: 0 or CONVROT_ROT_REGULAR (the rotation kind), plus
+ * optionally CONVROT_FLAG_GELU (defined below): the rows are then
+ * bf16(GELU(X)) of bf16 X, as convrot_mlp_forward quantises its intermediate
+ * when 6144 < K <= 24576 (the up projection writes X = u with the plain
+ * epilogue and the GELU is applied as the rows are loaded).  With the flag,
+ * F32 input or K outside that range returns EUNSUPPORTED. */
 CONVROT_API int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K,
                             int block, uint32_t flags, int8_t *q, float *s,
                             void *stream);

@@ -159,8 +159,16 @@ def test_lowrank_and_mlp_validation(cr):
 
 def test_hook_validation(cr):
     lib = cr.library()
-    assert lib.convrot_rotate_quantize(FAKE, cr.BF16, 4, 512, 128, 1, FAKE, FAKE, None) \
-        == cr.EUNSUPPORTED                                     # flags
+    rq = lambda x_dtype, K, flags, M=4: lib.convrot_rotate_quantize(
+        FAKE, x_dtype, M, K, 128, flags, FAKE, FAKE, None)
+    assert rq(cr.BF16, 512, 2) == cr.EUNSUPPORTED                  # unknown flag bit
+    # GELU on load: bf16 rows with 6144 < K <= 24576 only
+    assert rq(cr.BF16, 512, cr.FLAG_GELU) == cr.EUNSUPPORTED
+    assert rq(cr.BF16, 6144, cr.FLAG_GELU) == cr.EUNSUPPORTED
+    assert rq(cr.BF16, 24576 + 128, cr.FLAG_GELU) == cr.EUNSUPPORTED
+    assert rq(cr.F32, 8192, cr.FLAG_GELU) == cr.EUNSUPPORTED
+    assert rq(cr.BF16, 6144 + 128, cr.FLAG_GELU, M=0) == cr.OK
+    assert rq(cr.BF16, 24576, cr.FLAG_GELU, M=0) == cr.OK
     assert lib.convrot_rotate_quantize(FAKE, cr.BF16, 4, 500, 128, 0, FAKE, FAKE, None) \
         == cr.EINVAL
     assert lib.convrot_rotate_quantize(FAKE, cr.I8, 4, 512, 128, 0, FAKE, FAKE, None) \

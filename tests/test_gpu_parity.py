@@ -549,6 +549,60 @@ def test_mlp_small(cr):
     assert assert_output_parity(bf16_bits(y), y_ref, "bf16", "mlp small") == 0
 
 
+@pytest.mark.parametrize("M,K,b,rot", [(35, 6272, 128, "sylvester"), (18, 24576, 256, "sylvester"),
+                                       (9, 12288, 64, "regular"), (21, 21504, 128, "sylvester")])
+def test_rotquant_gelu_on_load_bitexact(cr, M, K, b, rot):
+    """The rotate+quantise hook with CONVROT_FLAG_GELU: codes and scales of
+    bf16(GELU(u)) bit-exact against the oracle's rotquant of its GELU, on rows
+    of scaled normals, a zero row and rows of random bf16 patterns (every
+    exponent up to 2^100, denormals included, both signs)."""
+    announce(f"rotquant gelu-on-load M={M} K={K} b={b} {rot}")
+    rng = np.random.default_rng(K + M)
+    u = oracle.f32_to_bf16((rng.standard_normal((M, K)) * 3).astype(np.float32))
+    u[1] = 0
+    pat = rng.integers(0, 1 << 16, (3, K), dtype=np.uint32).astype(np.uint16)
+    # exponents up to 2^100: the rotation's sums stay finite (denormals included)
+    small = ((pat >> 7) & 0xff) <= 127 + 100
+    u[2:5] = np.where(small, pat, u[2:5])
+    g_ref = oracle.gelu_bf16(u)
+    q_ref, s_ref = oracle.rotate_quantize(g_ref, b, "bf16", rot=rot)
+    X = torch.from_numpy(u.view(np.int16)).to("cuda").view(torch.bfloat16)
+    q, sc = cr.convrot_rotate_quantize(X, b, rotation=rot, gelu=True)
+    assert np.array_equal(untile(q, M, K), q_ref)
+    assert np.array_equal(host(sc), s_ref)
+
+
+@pytest.mark.parametrize("M,F,b,rot,with_bias", [
+    (37, 6272, 128, "sylvester", False),   # just above the streaming kernel's rows
+    (70, 24576, 256, "sylvester", True),   # the longest rows of the pair kernel
+    (16, 12288, 64, "sylvester", False),   # 8-wave rows (at most 48 steps of 256)
+    (33, 8192, 64, "regular", True),
+    (5, 21504, 256, "regular", False),
+])
+def test_mlp_gelu_on_load(cr, M, F, b, rot, with_bias):
+    """MLPs whose intermediate rows (6144 < F <= 24576) go to the two-rows-
+    per-wave rotquant kernel: the up projection writes u with the plain
+    epilogue and rotquant applies GELU as it loads.  The output must be
+    bit-exact against the oracle (so every code and scale of g is, too: one
+    code off changes its row's sums)."""
+    announce(f"mlp gelu-on-load M={M} F={F} b={b} {rot} bias={with_bias}")
+    w = wl.scaled("mlp_16384", M=M, K=256, N=160, ffn=F, block=b, seed=F + M)
+    x, Wu, Wd = w.activations(), w.weight("w"), w.weight("w2")
+    rng = np.random.default_rng(F)
+    bu = (rng.standard_normal(F) * 0.5).astype(np.float32) if with_bias else None
+    bd = (rng.standard_normal(160) * 0.5).astype(np.float32) if with_bias else None
+    pu = cr.convrot_linear_prepare_weights(to_dev(Wu), b, rotation=rot)
+    pd = cr.convrot_linear_prepare_weights(to_dev(Wd), b, rotation=rot)
+    qu, su = oracle.prepare_weights(Wu, b, rot=rot)
+    qd, sd = oracle.prepare_weights(Wd, b, rot=rot)
+    y = cr.convrot_mlp_forward(to_dev_bf16(x), pu, pd,
+                               bias_up=to_dev(bu) if with_bias else None,
+                               bias_down=to_dev(bd) if with_bias else None)
+    y_ref = oracle.mlp_forward(x, qu, su, qd, sd, b, bias_up=bu, bias_down=bd, out="bf16",
+                               rot=rot)
+    assert assert_output_parity(bf16_bits(y), y_ref, "bf16", "mlp gelu-on-load") == 0
+
+
 def test_measurement_probes(cr):
     """The streaming probe writes what its header states (a copy, or two xors
     per 16-byte item) and the MFMA probe runs and reports its work."""

@@ -347,15 +347,18 @@ def _codes(q, M: int, K: int, device):
 
 
 def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=None,
-                            rotation: str = "sylvester"):
-    """Rotate + quantise the rows of X: (q, s), q the K-tiled codes (Mp, K)."""
+                            rotation: str = "sylvester", gelu: bool = False):
+    """Rotate + quantise the rows of X: (q, s), q the K-tiled codes (Mp, K).
+    gelu: quantise bf16(GELU(X)) instead (bf16 X, 6144 < K <= 24576), as the
+    MLP path does with its intermediate."""
     lib = library()
     M, K = X.shape
     q = _codes(q, M, K, X.device)
     if s is None:
         s = torch.empty(M, dtype=torch.float32, device=X.device)
+    flags = ROTATIONS[rotation] | (FLAG_GELU if gelu else 0)
     rc = lib.convrot_rotate_quantize(_ptr(X), _dtype_tag(X.dtype), M, K, block,
-                                     ROTATIONS[rotation], _ptr(q), _ptr(s), _stream(stream))
+                                     flags, _ptr(q), _ptr(s), _stream(stream))
     _check("convrot_rotate_quantize", rc)
     return q, s
 

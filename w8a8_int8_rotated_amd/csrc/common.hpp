@@ -67,6 +67,15 @@ hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
                            int64_t ld, int block, bool regular, float inv_sqrt_b, int8_t *q,
                            float *s, hipStream_t stream);
 
+// Rotate and quantise bf16(GELU(u)) for bf16 rows u: the MLP's down-projection
+// input, read as the up projection's plain output.  gelu_table holds
+// bf16(GELU(x)) for every bf16 pattern x (launch_gelu_table).  Only for rows
+// that the two-rows-per-wave kernel serves: rotquant_fuses_gelu(K).
+bool rotquant_fuses_gelu(int64_t K);
+hipError_t launch_rotquant_gelu(const void *src, int64_t M, int64_t K, int64_t ld, int block,
+                                bool regular, float inv_sqrt_b, const uint16_t *gelu_table,
+                                int8_t *q, float *s, hipStream_t stream);
+
 // Factor 1 of the low-rank chain with the requantisation fused in:
 // (qh, sh) = rotate+quantise(bf16(((float)(qx . qa^T) * sx) * sa)) along the R
 // outputs, for R % 128 == 0, R <= 512 and block 64 or 128 (lowrank_f1_fusable).
@@ -77,6 +86,9 @@ hipError_t launch_lowrank_f1(const int8_t *qx, const int8_t *qa, const float *sx
 
 // g[i] = bf16(GELU(u[i])) for bf16 u, as the MLP's up projection applies it.
 hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream);
+// Fill the 65,536-entry bf16 GELU table (stream-ordered) and return its device
+// address on the current device.
+hipError_t launch_gelu_table(const uint16_t **table, hipStream_t stream);
 
 // INT8 codes [R, C] into the K-tiled layout (R % 16 == 0, C % 64 == 0); the
 // source is row-major [R, C] (ld = C) or, with transposed, [C, R].

@@ -401,14 +401,28 @@ static int mlp_forward_impl(const void *X, int64_t M, const convrot_weights *W_u
     float *sg = static_cast<float *>(c.take((size_t)M * 4u));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const float isb = inv_sqrt_block(W_up->block);
+    // GELU goes where it costs least: for the long rows that the two-rows-
+    // per-wave rotquant kernel serves, into that kernel's loads (the up
+    // projection writes u with the plain epilogue and g is never stored);
+    // otherwise into the up projection's epilogue.  Both give bf16(GELU(u)).
+    const bool gelu_on_load = convrot::rotquant_fuses_gelu(F);
     hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W_up->K, W_up->K,
                                             W_up->block, is_regular(W_up), isb, qx, sx, s);
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qx, W_up->codes, sx, W_up->scale, bias_up, g,
-                                    convrot::OutKind::GELU_BF16, M, F, W_up->K, s);
-    if (e == hipSuccess)
+                                    gelu_on_load ? convrot::OutKind::BF16
+                                                 : convrot::OutKind::GELU_BF16,
+                                    M, F, W_up->K, s);
+    if (e == hipSuccess && gelu_on_load) {
+        const uint16_t *table = nullptr;
+        e = convrot::launch_gelu_table(&table, s);
+        if (e == hipSuccess)
+            e = convrot::launch_rotquant_gelu(g, M, F, F, W_down->block, is_regular(W_down), isb,
+                                              table, qg, sg, s);
+    } else if (e == hipSuccess) {
         e = convrot::launch_rotquant(g, convrot::InType::BF16, M, F, F, W_down->block,
                                      is_regular(W_down), isb, qg, sg, s);
+    }
     if (e == hipSuccess)
         e = convrot::launch_gemm_i8(qg, W_down->codes, sg, W_down->scale, bias_down, Y,
                                     out_kind(y_dtype), M, W_down->N, F, s);
@@ -464,17 +478,29 @@ int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, in
                             uint32_t flags, int8_t *q, float *s_out, void *stream)
 {
     if (M < 0 || K <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
-    if ((flags & ~CONVROT_ROT_REGULAR) != 0) return CONVROT_EUNSUPPORTED;
-    if (!valid_rotation(flags, block)) return CONVROT_EINVAL;
+    if ((flags & ~(CONVROT_ROT_REGULAR | CONVROT_FLAG_GELU)) != 0) return CONVROT_EUNSUPPORTED;
+    const uint32_t rot = flags & CONVROT_ROT_REGULAR;
+    const bool gelu = (flags & CONVROT_FLAG_GELU) != 0;
+    if (!valid_rotation(rot, block)) return CONVROT_EINVAL;
     if (x_dtype != CONVROT_F32 && x_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
+    if (gelu && (x_dtype != CONVROT_BF16 || !convrot::rotquant_fuses_gelu(K)))
+        return CONVROT_EUNSUPPORTED;
     if (K > kMaxK || check_rows(M, K) != CONVROT_OK) return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!X || !q || !s_out) return CONVROT_EINVAL;
     if (!aligned16(X) || !aligned16(q) || !aligned16(s_out)) return CONVROT_EALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gelu) {
+        const uint16_t *table = nullptr;
+        hipError_t e = convrot::launch_gelu_table(&table, s);
+        if (e == hipSuccess)
+            e = convrot::launch_rotquant_gelu(X, M, K, K, block, rot != 0, inv_sqrt_block(block),
+                                              table, q, s_out, s);
+        return hip_status(e);
+    }
     const convrot::InType in = x_dtype == CONVROT_F32 ? convrot::InType::F32 : convrot::InType::BF16;
-    return hip_status(convrot::launch_rotquant(X, in, M, K, K, block, flags != 0,
-                                               inv_sqrt_block(block), q,
-                                               s_out, static_cast<hipStream_t>(stream)));
+    return hip_status(convrot::launch_rotquant(X, in, M, K, K, block, rot != 0,
+                                               inv_sqrt_block(block), q, s_out, s));
 }
 
 int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W, int32_t *acc,

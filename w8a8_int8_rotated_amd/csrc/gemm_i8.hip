@@ -59,6 +59,7 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <utility>
 
 namespace convrot {
@@ -161,7 +162,7 @@ __device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float b
 // instead of evaluating erf per element.  Every launch that reads the table is
 // preceded on its own stream by a launch that (re)writes it with the same
 // values, so a reader never sees a partial table.
-__device__ uint16_t g_gelu_bf16[65536];
+__device__ __align__(16) uint16_t g_gelu_bf16[65536];
 
 __global__ __launch_bounds__(256) void gelu_table_kernel()
 {
@@ -1220,6 +1221,29 @@ hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
                   : launch_t<int(OutKind::BF16_MM), false>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gelu_table(const uint16_t **table, hipStream_t stream)
+{
+    // the table's device address, per device ordinal (each device holds its
+    // own copy of the module's globals); racing first queries store the same
+    static std::atomic<const uint16_t *> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint16_t *p = dev >= 0 && dev < 64 ? cached[dev].load(std::memory_order_relaxed) : nullptr;
+    if (!p) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_gelu_bf16));
+        if (e != hipSuccess) return e;
+        p = static_cast<const uint16_t *>(a);
+        // readers copy it in 16-byte pieces
+        if (reinterpret_cast<uintptr_t>(p) & 15) return hipErrorInvalidValue;
+        if (dev >= 0 && dev < 64) cached[dev].store(p, std::memory_order_relaxed);
+    }
+    hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
+    *table = p;
+    return hipGetLastError();
 }
 
 hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream)

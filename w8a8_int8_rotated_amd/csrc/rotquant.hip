@@ -551,11 +551,23 @@ hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
 // persistent workgroup per CU walks pair groups, and each wave loads the raw
 // input of its next group before rotating the current one, so memory and the
 // rotation overlap inside the wave as well as across waves.
-template <int IN, int B, int ROT, int SPR, int WPR, int NW>
+// GELU (bf16 input only): each loaded value u is replaced by bf16(GELU(u))
+// from the 65,536-entry table gtab (one entry per bf16 pattern) before the
+// rotation, so the MLP's intermediate is read once, as u, and g is never
+// written.  The table is copied into LDS (128 KiB) when the workgroup starts.
+template <int IN, int B, int ROT, int SPR, int WPR, int NW, bool GELU = false>
 __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
     const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
-    int8_t *__restrict__ q, float *__restrict__ s)
+    int8_t *__restrict__ q, float *__restrict__ s, const uint16_t *__restrict__ gtab)
 {
+    static_assert(!GELU || IN == int(InType::BF16), "GELU applies to bf16 input");
+    __shared__ uint16_t tab[GELU ? 65536 : 2];
+    if constexpr (GELU) {
+        const uint4 *gt = reinterpret_cast<const uint4 *>(gtab);
+        uint4 *lt = reinterpret_cast<uint4 *>(tab);
+        for (int i = threadIdx.x; i < 65536 / 8; i += NW * 64) lt[i] = gt[i];
+        __syncthreads();
+    }
     static_assert(NW % WPR == 0 && WPR > 1, "");
     static_assert(B <= 256, "a block lies inside a half-wave");
     constexpr int HS = 256;                   // elements per row per step
@@ -631,8 +643,11 @@ __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
             if constexpr (DW == 4) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    v[t][2 * j] = bf16_lo((uint32_t)raw[t][j]);
-                    v[t][2 * j + 1] = bf16_hi((uint32_t)raw[t][j]);
+                    uint32_t u = (uint32_t)raw[t][j];
+                    if constexpr (GELU)
+                        u = (uint32_t)tab[u & 0xffffu] | ((uint32_t)tab[u >> 16] << 16);
+                    v[t][2 * j] = bf16_lo(u);
+                    v[t][2 * j + 1] = bf16_hi(u);
                 }
             } else {
 #pragma unroll
@@ -685,15 +700,17 @@ __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
     }
 }
 
-template <int IN, int B, int ROT, int SPR, int WPR, int NW>
+template <int IN, int B, int ROT, int SPR, int WPR, int NW, bool GELU = false>
 hipError_t launch_pair(const void *src, int64_t M, int64_t K, int64_t ld,
-                         float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
+                         float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream,
+                         const uint16_t *gtab = nullptr)
 {
     constexpr int rows_per_wg = 2 * (NW / WPR);
     const int64_t groups = (M + rows_per_wg - 1) / rows_per_wg;
     const int64_t grid = std::min<int64_t>(groups, device_cu_count());
-    hipLaunchKernelGGL((rotquant_pair_kernel<IN, B, ROT, SPR, WPR, NW>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, stream, src, M, (int)K, ld, inv_sqrt_b, q, s);
+    hipLaunchKernelGGL((rotquant_pair_kernel<IN, B, ROT, SPR, WPR, NW, GELU>),
+                       dim3((unsigned)grid), dim3(NW * 64), 0, stream, src, M, (int)K, ld,
+                       inv_sqrt_b, q, s, gtab);
     return hipGetLastError();
 }
 
@@ -737,6 +754,18 @@ hipError_t launch_in(const void *src, int64_t M, int64_t K, int64_t ld, int bloc
     case 256: return launch_b<IN, 256, 0>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+// The pair kernel's range, with GELU on load (bf16 rows, 6144 < K <= 24576).
+template <int B, int ROT>
+hipError_t launch_gelu_b(const void *src, int64_t M, int64_t K, int64_t ld, float inv_sqrt_b,
+                         int8_t *q, float *s, const uint16_t *gtab, hipStream_t stream)
+{
+    constexpr int BF = int(InType::BF16);
+    const int64_t hsteps = (K + 255) / 256;
+    if (hsteps <= 48)
+        return launch_pair<BF, B, ROT, 6, 8, 16, true>(src, M, K, ld, inv_sqrt_b, q, s, stream, gtab);
+    return launch_pair<BF, B, ROT, 6, 16, 16, true>(src, M, K, ld, inv_sqrt_b, q, s, stream, gtab);
 }
 
 // ---------------------------------------------------------- tile codes ----
@@ -803,6 +832,32 @@ hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
         return launch_in<int(InType::BF16)>(src, M, K, ld, block, regular, inv_sqrt_b, q, s,
                                             stream);
     return launch_in<int(InType::F32)>(src, M, K, ld, block, regular, inv_sqrt_b, q, s, stream);
+}
+
+bool rotquant_fuses_gelu(int64_t K)
+{
+    return K > 12 * kStep && K <= 96 * 256;
+}
+
+hipError_t launch_rotquant_gelu(const void *src, int64_t M, int64_t K, int64_t ld, int block,
+                                bool regular, float inv_sqrt_b, const uint16_t *gelu_table,
+                                int8_t *q, float *s, hipStream_t stream)
+{
+    if (!rotquant_fuses_gelu(K) || !gelu_table) return hipErrorInvalidValue;
+    if (M == 0) return hipSuccess;
+    if (regular) {
+        switch (block) {
+        case 64: return launch_gelu_b<64, 1>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
+        case 256: return launch_gelu_b<256, 1>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (block) {
+    case 64: return launch_gelu_b<64, 0>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
+    case 128: return launch_gelu_b<128, 0>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
+    case 256: return launch_gelu_b<256, 0>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_tile_codes(const int8_t *src, bool transposed, int8_t *dst, int64_t R,
