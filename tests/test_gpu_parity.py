@@ -635,25 +635,30 @@ def test_graph_capture_replays(cr):
     lin = wl.scaled("linear_4096", M=700, K=1024, N=768)
     lr = wl.scaled("lowrank_38656", M=520, K=1024, N=784, rank=256)
     mlp = wl.scaled("mlp_16384", M=300, K=1024, N=512, ffn=2048)
+    mlp2 = wl.scaled("mlp_16384", M=96, K=256, N=160, ffn=6400)   # GELU on load
     prep = lambda W, b: cr.convrot_linear_prepare_weights(to_dev(W), b)
     pl = prep(lin.weight(), lin.block)
     bias = to_dev(lin.bias())
     pa, pb = prep(lr.weight("w"), lr.block), prep(lr.weight("w2"), lr.block)
     pu, pd = prep(mlp.weight("w"), mlp.block), prep(mlp.weight("w2"), mlp.block)
+    pu2, pd2 = prep(mlp2.weight("w"), mlp2.block), prep(mlp2.weight("w2"), mlp2.block)
     bf = torch.bfloat16
     u8 = lambda n: torch.empty(n, dtype=torch.uint8, device="cuda")
-    Xl, Xr, Xm = (to_dev_bf16(w.activations()) for w in (lin, lr, mlp))
+    Xl, Xr, Xm, Xm2 = (to_dev_bf16(w.activations()) for w in (lin, lr, mlp, mlp2))
     Yl = torch.empty((lin.M, lin.N), dtype=bf, device="cuda")
     Yr = torch.empty((lr.M, lr.N), dtype=bf, device="cuda")
     Ym = torch.empty((mlp.M, mlp.N), dtype=bf, device="cuda")
+    Ym2 = torch.empty((mlp2.M, mlp2.N), dtype=bf, device="cuda")
     wsl = u8(cr.convrot_linear_workspace_bytes(lin.M, lin.K, lin.N, lin.block))
     wsr = u8(cr.lowrank_convrot_workspace_bytes(lr.M, lr.K, lr.rank, lr.N, lr.block))
     wsm = u8(cr.convrot_mlp_workspace_bytes(mlp.M, mlp.K, mlp.ffn, mlp.N, mlp.block))
+    wsm2 = u8(cr.convrot_mlp_workspace_bytes(mlp2.M, mlp2.K, mlp2.ffn, mlp2.N, mlp2.block))
 
     def calls():
         cr.convrot_linear_forward(Xl, pl, bias=bias, out=Yl, workspace=wsl)
         cr.lowrank_convrot_forward(Xr, pa, pb, out=Yr, workspace=wsr)
         cr.convrot_mlp_forward(Xm, pu, pd, out=Ym, workspace=wsm)
+        cr.convrot_mlp_forward(Xm2, pu2, pd2, out=Ym2, workspace=wsm2)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -665,19 +670,65 @@ def test_graph_capture_replays(cr):
     with torch.cuda.graph(graph):
         calls()
     for rep in range(3):
-        for X, w in ((Xl, lin), (Xr, lr), (Xm, mlp)):
+        for X, w in ((Xl, lin), (Xr, lr), (Xm, mlp), (Xm2, mlp2)):
             x = rng.normal(0.0, 1.0 + rep, (w.M, w.K)).astype(np.float32)
             X.copy_(to_dev_bf16(wl.f32_to_bf16_bits(x)))
         graph.replay()
         torch.cuda.synchronize()
-        got = [bf16_bits(Y) for Y in (Yl, Yr, Ym)]
+        got = [bf16_bits(Y) for Y in (Yl, Yr, Ym, Ym2)]
         want = [bf16_bits(cr.convrot_linear_forward(Xl, pl, bias=bias)),
                 bf16_bits(cr.lowrank_convrot_forward(Xr, pa, pb)),
-                bf16_bits(cr.convrot_mlp_forward(Xm, pu, pd))]
+                bf16_bits(cr.convrot_mlp_forward(Xm, pu, pd)),
+                bf16_bits(cr.convrot_mlp_forward(Xm2, pu2, pd2))]
         torch.cuda.synchronize()
-        for name, a, b in zip(("linear", "low-rank", "MLP"), got, want):
+        for name, a, b in zip(("linear", "low-rank", "MLP", "MLP, GELU on load"), got, want):
             assert np.array_equal(a, b), f"replay {rep}: {name} differs from the eager call"
-    print("[parity] graph replays: 3 x 3 forwards equal to eager", flush=True)
+    print("[parity] graph replays: 3 x 4 forwards equal to eager", flush=True)
+
+
+_CAPTURE_FIRST = r'''
+import numpy as np, torch
+from w8a8_int8_rotated_amd import convrot as cr
+from w8a8_int8_rotated_amd import workloads as wl
+m = wl.scaled("mlp_16384", M=64, K=256, N=160, ffn=6400)
+# weights prepared through other entry points; the MLP path's GELU table is
+# first looked up inside the capture below
+pu = cr.convrot_linear_prepare_weights(torch.from_numpy(m.weight("w")).cuda(), m.block)
+pd = cr.convrot_linear_prepare_weights(torch.from_numpy(m.weight("w2")).cuda(), m.block)
+X = torch.from_numpy(m.activations().view(np.int16)).cuda().view(torch.bfloat16)
+Y = torch.empty((m.M, m.N), dtype=torch.bfloat16, device="cuda")
+ws = torch.empty(cr.convrot_mlp_workspace_bytes(m.M, m.K, m.ffn, m.N, m.block),
+                 dtype=torch.uint8, device="cuda")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    cr.convrot_mlp_forward(X, pu, pd, out=Y, workspace=ws)
+for _ in range(2):
+    Y.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    want = cr.convrot_mlp_forward(X, pu, pd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), want.view(torch.int16)), "replay differs"
+print("capture-first ok", flush=True)
+'''
+
+
+def test_graph_capture_first_call_gelu_on_load(tmp_path):
+    """A fresh process whose first MLP call with GELU on load is recorded
+    into a graph (the table's device address is first looked up during the
+    capture): the replays equal eager calls."""
+    import os
+    import subprocess
+    import sys
+    announce("graph capture: first GELU-on-load MLP call inside the capture")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "capture_first.py"
+    script.write_text(_CAPTURE_FIRST)
+    r = subprocess.run([sys.executable, str(script)], capture_output=True, text=True,
+                       timeout=110, cwd=root, env=dict(os.environ, PYTHONPATH=root))
+    print(r.stdout.strip(), r.stderr.strip()[-2000:], flush=True)
+    assert r.returncode == 0 and "capture-first ok" in r.stdout
 
 
 def _sweep_cases(n, seed=2024):
