@@ -167,7 +167,7 @@ CONVROT_API size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t 
 CONVROT_API size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r,
                                        int64_t N, int block);
 
-/* Workspace for convrot_mlp_forward (codes of X, bf16 activation g [M, F],
+/* Workspace for convrot_mlp_forward (codes of X, the bf16 intermediate u or g [M, F],
  * codes of g, row scales). */
 CONVROT_API size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
                                    int block);
@@ -228,8 +228,11 @@ CONVROT_API int lowrank_convrot_forward(const void *X, int64_t M, const convrot_
 
 /* MLP pair: u = bf16(linear(X; W_up) + bias_up); g = bf16(GELU(u)) with the
  * erf form of GELU (see convrot_gelu_bf16); Y = linear(g; W_down) + bias_down.
- * Requires W_up->N == W_down->K (= F) and the same block and rotation kind.  GELU is applied in the epilogue of the
- * up projection, so u is never written. */
+ * Requires W_up->N == W_down->K (= F) and the same block and rotation kind.
+ * Where GELU runs depends on F only, never the result: for 6144 < F <= 24576
+ * the up projection writes u and the rotate+quantise pass of the down
+ * projection applies GELU as it loads u (g is never written); otherwise the
+ * up projection's epilogue applies it and writes g (u is never written). */
 CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weights *W_up,
                         const float *bias_up, const convrot_weights *W_down,
                         const float *bias_down, void *Y, int y_dtype, void *ws,
