@@ -311,8 +311,9 @@ def test_output_guard_band(cr):
 def test_two_streams_concurrent(cr):
     """The library keeps no per-call state: forwards on two streams with
     separate workspaces, issued back to back so they can overlap, give the
-    same bits as the same calls run one after the other.  The MLP pair is
-    included: both streams rewrite the shared GELU table with the same values
+    same bits as the same calls run one after the other.  MLP pairs of both
+    kinds are included (GELU in the up projection's epilogue, and GELU on
+    load): both streams rewrite the shared GELU table with the same values
     while the other may be reading it."""
     announce("two streams")
     w = wl.scaled("mlp_16384", M=700, K=1024, N=512, ffn=2048)
@@ -325,21 +326,35 @@ def test_two_streams_concurrent(cr):
     ref_a = bf16_bits(cr.convrot_mlp_forward(xa, pu, pd))
     ref_b = bf16_bits(cr.convrot_mlp_forward(xb, pu, pd))
     lin_a = host(cr.convrot_linear_forward(xa, pu, out_dtype=torch.float32))
+    # an MLP whose rotquant applies GELU on load (F = 6400): both streams
+    # refill the table while the other's rotquant copies it into LDS
+    w2 = wl.scaled("mlp_16384", M=300, K=256, N=160, ffn=6400)
+    pu2 = cr.convrot_linear_prepare_weights(to_dev(w2.weight("w")), 128)
+    pd2 = cr.convrot_linear_prepare_weights(to_dev(w2.weight("w2")), 128)
+    xa2 = to_dev_bf16(w2.activations())
+    xb2 = to_dev_bf16(wl.scaled("mlp_16384", M=300, K=256, N=160, ffn=6400,
+                                seed=11).activations())
+    ref_a2 = bf16_bits(cr.convrot_mlp_forward(xa2, pu2, pd2))
+    ref_b2 = bf16_bits(cr.convrot_mlp_forward(xb2, pu2, pd2))
     torch.cuda.synchronize()
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for _ in range(3):
         with torch.cuda.stream(sa):
             ya = cr.convrot_mlp_forward(xa, pu, pd, stream=sa)
+            ya2 = cr.convrot_mlp_forward(xa2, pu2, pd2, stream=sa)
             la = cr.convrot_linear_forward(xa, pu, out_dtype=torch.float32, stream=sa)
         with torch.cuda.stream(sb):
+            yb2 = cr.convrot_mlp_forward(xb2, pu2, pd2, stream=sb)
             yb = cr.convrot_mlp_forward(xb, pu, pd, stream=sb)
-        outs.append((ya, la, yb))
+        outs.append((ya, la, yb, ya2, yb2))
     torch.cuda.synchronize()
-    for ya, la, yb in outs:
+    for ya, la, yb, ya2, yb2 in outs:
         assert np.array_equal(bf16_bits(ya), ref_a)
         assert np.array_equal(host(la), lin_a)
         assert np.array_equal(bf16_bits(yb), ref_b)
+        assert np.array_equal(bf16_bits(ya2), ref_a2)
+        assert np.array_equal(bf16_bits(yb2), ref_b2)
 
 
 # ----------------------------------------------------------- low-rank ----
