@@ -138,3 +138,29 @@ def test_max_rows_32bit_offsets(cr):
     y_ref = oracle.linear_forward(x_rows, qw, sw, b, out="bf16")
     assert assert_output_parity(bf16_bits(y[rows_d]), y_ref, "bf16",
                                 f"M={M} sampled rows") == 0
+
+
+def test_max_rows_gelu_on_load(cr):
+    """The MLP entry point at the most rows it accepts for F = 24576, the
+    longest intermediate rows that rotquant applies GELU to as it loads them:
+    the padded codes of g are just under 2^31 bytes (M = 87369, ragged in the
+    last 16-row block), u is 4.3 GB.  Sampled outputs (the last 20 rows
+    included) against the oracle."""
+    K, F, N, b = 256, 24576, 160, 128
+    M = 87369
+    assert padded_rows(M) * F < 2**31 <= padded_rows(M + 16) * F
+    announce(f"largest row count, GELU on load: M={M} K={K} F={F} N={N} b={b}")
+    gen = torch.Generator(device=dev()).manual_seed(3)
+    X = (torch.randn((M, K), generator=gen, device=dev()) * 2).to(torch.bfloat16)
+    rng = np.random.default_rng(4)
+    Wu = rng.normal(0.0, 0.06, (F, K)).astype(np.float32)
+    Wd = rng.normal(0.0, 0.02, (N, F)).astype(np.float32)
+    pu, qu, su = _prep(cr, Wu, b)
+    pd, qd, sd = _prep(cr, Wd, b)
+    y = cr.convrot_mlp_forward(X, pu, pd)
+    torch.cuda.synchronize()
+    rows = np.union1d(sample_rows(M, 48), np.arange(M - 20, M))
+    rows_d = torch.from_numpy(rows).to(dev())
+    y_ref = oracle.mlp_forward(bf16_bits(X[rows_d]), qu, su, qd, sd, b, out="bf16")
+    assert assert_output_parity(bf16_bits(y[rows_d]), y_ref, "bf16",
+                                f"MLP M={M} F={F} sampled rows") == 0
