@@ -45,6 +45,18 @@ MUTANTS = [
      ["test_regular_columns", "test_regular_hadamard_properties"]),
     ("regular_digit_skip", "for (int h = 1; h < b; h *= 4)", "for (int h = 4; h < b; h *= 4)",
      ["test_regular_columns", "test_regular_hadamard_properties"]),
+    # every exact-arithmetic pin of the Hadamard passes with the strides
+    # reversed; only the hand-worked fp32 association catches it
+    ("descending_strides", "for (int h = 1; h < b; h *= 2)", "for (int h = b / 2; h >= 1; h /= 2)",
+     ["test_golden_fwht_stage_order"]),
+    ("lowrank_bias_on_factor1", "qa, sa, r, NULL, OR_BF16, h);", "qa, sa, r, bias, OR_BF16, h);",
+     ["test_lowrank_is_two_chained_linears_with_bias"]),
+    ("lowrank_bias_dropped", "qb, sb, N, bias, out_dtype, out);", "qb, sb, N, NULL, out_dtype, out);",
+     ["test_lowrank_is_two_chained_linears_with_bias"]),
+    ("mlp_dropped_bias_up", "qu, su, F, bias_up, OR_BF16, u);", "qu, su, F, NULL, OR_BF16, u);",
+     ["test_mlp_is_two_biased_linears_around_gelu"]),
+    ("mlp_dropped_bias_down", "qd, sd, N, bias_down,", "qd, sd, N, NULL,",
+     ["test_mlp_is_two_biased_linears_around_gelu"]),
 ]
 
 CALL = {
@@ -62,6 +74,11 @@ CALL = {
     "test_gelu_bf16_and_mlp_chain": lambda: pins.test_gelu_bf16_and_mlp_chain(),
     "test_regular_columns": lambda: pins.test_regular_columns(64),
     "test_regular_hadamard_properties": lambda: pins.test_regular_hadamard_properties(64),
+    "test_golden_fwht_stage_order": lambda: pins.test_golden_fwht_stage_order(),
+    "test_lowrank_is_two_chained_linears_with_bias":
+        lambda: pins.test_lowrank_is_two_chained_linears_with_bias(),
+    "test_mlp_is_two_biased_linears_around_gelu":
+        lambda: pins.test_mlp_is_two_biased_linears_around_gelu(),
 }
 
 

@@ -184,6 +184,28 @@ def test_golden_hand_example_b4():
     assert np.allclose(y, g["Wx_float"], atol=0.03)
 
 
+def _hexf(xs):
+    return np.array([float.fromhex(x) for x in xs], np.float32)
+
+
+def test_golden_fwht_stage_order():
+    """The butterfly association (reading: strides ascending, each stage
+    rounded once in fp32) against the hand-worked vectors of
+    tests/golden/fwht_order.json: with one input at 1 and others at 2^-24 the
+    rounding of 1 + 2^-24 (a tie, to even) depends on which stage runs first,
+    and only the ascending order gives the recorded bits."""
+    g = json.load(open(os.path.join(GOLDEN, "fwht_order.json")))
+    for case in g["cases"]:
+        b = case["block"]
+        v = _hexf(case["v"])[None, :]
+        got = oracle.fwht(v, b)[0]
+        want = _hexf(case["ascending"])
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (b, got, want)
+        for other in ("descending", "order_1_4_2"):
+            if other in case:
+                assert not np.array_equal(got, _hexf(case[other]))
+
+
 # ------------------------------------------------------------- quantiser ----
 
 def _rand_rows(rng, rows, K, scale=1.0):
@@ -454,6 +476,27 @@ def test_lowrank_vs_dense_fp64():
     assert np.all(np.abs(y.astype(np.float64) - y_ref) <= bound_y + prop + 1e-6)
 
 
+def test_lowrank_is_two_chained_linears_with_bias():
+    """O8 as the composition the workload names: h = bf16(linear(X; A)) with
+    no bias, then linear(h; B) with the bias, bit for bit (the bias belongs
+    to the second factor only; both outputs checked)."""
+    b = 128
+    w = wl.scaled("lowrank_38656", M=12, K=256, N=192, rank=128)
+    x = w.activations()
+    qa, sa = oracle.prepare_weights(w.weight("w"), b)
+    qb, sb = oracle.prepare_weights(w.weight("w2"), b)
+    bias = np.random.default_rng(41).normal(0, 0.5, 192).astype(np.float32)
+    h_ref = oracle.linear_forward(x, qa, sa, b, bias=None, out="bf16")
+    for out in ("f32", "bf16"):
+        y, h = oracle.lowrank_forward(x, qa, sa, qb, sb, b, bias=bias, out=out, return_h=True)
+        assert np.array_equal(h, h_ref)
+        y_ref = oracle.linear_forward(h_ref, qb, sb, b, bias=bias, out=out)
+        assert np.array_equal(y, y_ref)
+        # the bias is really there: without it every output moves
+        y_nb = oracle.linear_forward(h_ref, qb, sb, b, bias=None, out=out)
+        assert not np.array_equal(y, y_nb)
+
+
 def test_lowrank_rejects_bad_rank():
     q = np.zeros((100, 128), np.int8)
     s = np.ones(100, np.float32)
@@ -511,3 +554,26 @@ def test_gelu_bf16_and_mlp_chain():
     # the down projection of the oracle equals a linear on g
     y2 = oracle.linear_forward(g, qd, sd, b, out="f32")
     assert np.array_equal(y, y2)
+
+
+def test_mlp_is_two_biased_linears_around_gelu():
+    """O9 as a composition: u = bf16(linear(X; W_up) + bias_up), g =
+    bf16(GELU(u)), y = linear(g; W_down) + bias_down, bit for bit, each bias
+    on its own projection."""
+    b = 128
+    w = wl.scaled("mlp_16384", M=9, K=256, N=128, ffn=256)
+    x = w.activations()
+    qu, su = oracle.prepare_weights(w.weight("w"), b)
+    qd, sd = oracle.prepare_weights(w.weight("w2"), b)
+    rng = np.random.default_rng(43)
+    bu = rng.normal(0, 0.5, 256).astype(np.float32)
+    bd = rng.normal(0, 0.5, 128).astype(np.float32)
+    y, u, g = oracle.mlp_forward(x, qu, su, qd, sd, b, bias_up=bu, bias_down=bd, out="f32",
+                                 return_intermediates=True)
+    u_ref = oracle.linear_forward(x, qu, su, b, bias=bu, out="bf16")
+    assert np.array_equal(u, u_ref)
+    assert not np.array_equal(u, oracle.linear_forward(x, qu, su, b, out="bf16"))
+    assert np.array_equal(g, oracle.gelu_bf16(u_ref))
+    y_ref = oracle.linear_forward(g, qd, sd, b, bias=bd, out="f32")
+    assert np.array_equal(y, y_ref)
+    assert not np.array_equal(y, oracle.linear_forward(g, qd, sd, b, out="f32"))
