@@ -134,6 +134,65 @@ def _torch_dtype(tag: int) -> torch.dtype:
     return {F32: torch.float32, BF16: torch.bfloat16}[tag]
 
 
+def _on_device(device, **tensors):
+    """Every tensor the library will dereference is a GPU tensor on `device`
+    (any GPU when None).  Called after the shape and dtype checks, so a
+    host-side caller sees those errors first."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda" or (device is not None and t.device != device):
+            raise ValueError(f"{name} must be a GPU tensor on {device or 'the GPU'}, "
+                             f"got {t.device}")
+
+
+def _need(t, name: str, dtypes, shape):
+    """Check a tensor argument before its pointer reaches the library: its
+    dtype, exact shape and contiguity (the device is checked by _on_device)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name: str, dtypes, shape):
+    return None if t is None else _need(t, name, dtypes, shape)
+
+
+def _weights(W, name: str):
+    if not isinstance(W, PreparedWeights):
+        raise ValueError(f"{name} must be PreparedWeights from convrot_linear_prepare_weights")
+    return W.codes.device
+
+
+def _rows(X, name: str, K: int):
+    """bf16 activations [M, K]; returns M."""
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor [M, {K}]")
+    _need(X, name, torch.bfloat16, (X.shape[0], K))
+    return X.shape[0]
+
+
+def _output(out, M: int, N: int, dtypes):
+    return None if out is None else _need(out, "out", dtypes, (M, N))
+
+
+def _check_workspace(nbytes: int, workspace):
+    if workspace is None or nbytes == 0:
+        return
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 \
+            or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+
+
 def _workspace(nbytes: int, device, workspace):
     if nbytes == 0:
         return None
@@ -200,13 +259,23 @@ def convrot_linear_prepare_weights(W: torch.Tensor, block: int, layout: int = OU
     """Rotate + quantise + pack a weight (``[N, K]`` or ``[K, N]`` per layout)
     with the rotation kind ``'sylvester'`` or ``'regular'``."""
     lib = library()
-    if W.dim() != 2:
-        raise ValueError("W must be 2-D")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor")
+    if layout not in (OUT_MAJOR, IN_MAJOR):
+        raise ValueError("layout must be OUT_MAJOR or IN_MAJOR")
     if layout == OUT_MAJOR:
         N, K = W.shape
     else:
         K, N = W.shape
+    if W.dtype not in (torch.float32, torch.bfloat16, torch.int8):
+        raise ValueError(f"W must be float32, bfloat16 or int8 codes, got {W.dtype}")
+    if (W.dtype == torch.int8) != (src_scale is not None):
+        raise ValueError("src_scale is required for int8 codes and only for them")
+    _opt(src_scale, "src_scale", torch.float32, (N,))
+    if rotation not in ROTATIONS:
+        raise ValueError(f"rotation must be one of {sorted(ROTATIONS)}")
     W = W.contiguous()
+    _on_device(W.device, W=W, src_scale=src_scale)
     tag = _dtype_tag(W.dtype)
     nbytes = lib.convrot_weights_packed_bytes(N, K, block)
     if nbytes == 0:
@@ -261,11 +330,16 @@ def convrot_linear_forward(X: torch.Tensor, W: PreparedWeights, bias=None,
                            out_dtype: torch.dtype = torch.bfloat16, out=None,
                            workspace=None, stream=None) -> torch.Tensor:
     lib = library()
-    M = X.shape[0]
-    if out is None:
-        out = torch.empty((M, W.N), dtype=out_dtype, device=X.device)
+    dev = _weights(W, "W")
+    M = _rows(X, "X", W.K)
+    _opt(bias, "bias", torch.float32, (W.N,))
+    _output(out, M, W.N, (torch.bfloat16, torch.float32))
     wsb = lib.convrot_linear_workspace_bytes(M, W.K, W.N, W.block)
-    ws = _workspace(wsb, X.device, workspace)
+    _check_workspace(wsb, workspace)
+    _on_device(dev, X=X, bias=bias, out=out, workspace=workspace)
+    if out is None:
+        out = torch.empty((M, W.N), dtype=out_dtype, device=dev)
+    ws = _workspace(wsb, dev, workspace)
     rc = lib.convrot_linear_forward(_ptr(X), M, W.ref(), _ptr(bias), _ptr(out),
                                     _dtype_tag(out.dtype), _ptr(ws),
                                     ws.numel() if ws is not None else 0, _stream(stream))
@@ -277,11 +351,18 @@ def lowrank_convrot_forward(X: torch.Tensor, A: PreparedWeights, B: PreparedWeig
                             bias=None, out_dtype: torch.dtype = torch.bfloat16, out=None,
                             workspace=None, stream=None) -> torch.Tensor:
     lib = library()
-    M = X.shape[0]
-    if out is None:
-        out = torch.empty((M, B.N), dtype=out_dtype, device=X.device)
+    dev = _weights(A, "A")
+    if _weights(B, "B") != dev:
+        raise ValueError("A and B must be on the same device")
+    M = _rows(X, "X", A.K)
+    _opt(bias, "bias", torch.float32, (B.N,))
+    _output(out, M, B.N, (torch.bfloat16, torch.float32))
     wsb = lib.lowrank_convrot_workspace_bytes(M, A.K, A.N, B.N, A.block)
-    ws = _workspace(wsb, X.device, workspace)
+    _check_workspace(wsb, workspace)
+    _on_device(dev, X=X, bias=bias, out=out, workspace=workspace)
+    if out is None:
+        out = torch.empty((M, B.N), dtype=out_dtype, device=dev)
+    ws = _workspace(wsb, dev, workspace)
     rc = lib.lowrank_convrot_forward(_ptr(X), M, A.ref(), B.ref(), _ptr(bias), _ptr(out),
                                      _dtype_tag(out.dtype), _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream))
@@ -293,11 +374,19 @@ def convrot_mlp_forward(X: torch.Tensor, W_up: PreparedWeights, W_down: Prepared
                         bias_up=None, bias_down=None, out_dtype: torch.dtype = torch.bfloat16,
                         out=None, workspace=None, stream=None) -> torch.Tensor:
     lib = library()
-    M = X.shape[0]
-    if out is None:
-        out = torch.empty((M, W_down.N), dtype=out_dtype, device=X.device)
+    dev = _weights(W_up, "W_up")
+    if _weights(W_down, "W_down") != dev:
+        raise ValueError("W_up and W_down must be on the same device")
+    M = _rows(X, "X", W_up.K)
+    _opt(bias_up, "bias_up", torch.float32, (W_up.N,))
+    _opt(bias_down, "bias_down", torch.float32, (W_down.N,))
+    _output(out, M, W_down.N, (torch.bfloat16, torch.float32))
     wsb = lib.convrot_mlp_workspace_bytes(M, W_up.K, W_up.N, W_down.N, W_up.block)
-    ws = _workspace(wsb, X.device, workspace)
+    _check_workspace(wsb, workspace)
+    _on_device(dev, X=X, bias_up=bias_up, bias_down=bias_down, out=out, workspace=workspace)
+    if out is None:
+        out = torch.empty((M, W_down.N), dtype=out_dtype, device=dev)
+    ws = _workspace(wsb, dev, workspace)
     rc = lib.convrot_mlp_forward(_ptr(X), M, W_up.ref(), _ptr(bias_up), W_down.ref(),
                                  _ptr(bias_down), _ptr(out), _dtype_tag(out.dtype), _ptr(ws),
                                  ws.numel() if ws is not None else 0, _stream(stream))
@@ -310,17 +399,23 @@ def lowrank_bf16_forward(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bias
     """Comparison variant: bf16(bf16(X . A^T) . B^T + bias), bf16 factors
     A [r, K] and B [N, r], no rotation or quantisation."""
     lib = library()
-    for t in (X, A, B):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("X, A and B must be contiguous bf16")
+    for t, name in ((X, "X"), (A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
     M, K = X.shape
     r, N = A.shape[0], B.shape[0]
-    if A.shape[1] != K or B.shape[1] != r:
-        raise ValueError("A must be [r, K] and B [N, r]")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    dev = A.device
+    _need(X, "X", torch.bfloat16, (M, K))
+    _need(A, "A", torch.bfloat16, (r, K))
+    _need(B, "B", torch.bfloat16, (N, r))
+    _opt(bias, "bias", torch.float32, (N,))
+    _output(out, M, N, torch.bfloat16)
     wsb = lib.lowrank_bf16_workspace_bytes(M, r)
-    ws = _workspace(wsb, X.device, workspace)
+    _check_workspace(wsb, workspace)
+    _on_device(dev, X=X, A=A, B=B, bias=bias, out=out, workspace=workspace)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = _workspace(wsb, dev, workspace)
     rc = lib.lowrank_bf16_forward(_ptr(X), M, K, _ptr(A), r, _ptr(B), N, _ptr(bias), _ptr(out),
                                   _ptr(ws), ws.numel() if ws is not None else 0,
                                   _stream(stream))
@@ -336,12 +431,14 @@ def padded_rows(M: int) -> int:
 
 
 def _codes(q, M: int, K: int, device):
-    """A K-tiled code buffer for M rows of K codes: allocated as (Mp, K) int8,
-    or a caller tensor checked to hold Mp * K bytes."""
+    """A K-tiled code buffer for M rows of K codes: allocated as (Mp, K) int8
+    on `device` when q is None, or a caller tensor checked to hold Mp * K
+    bytes (its device is checked by the caller)."""
     Mp = padded_rows(M)
     if q is None:
         return torch.empty((Mp, K), dtype=torch.int8, device=device)
-    if q.dtype != torch.int8 or not q.is_contiguous() or q.numel() < Mp * K:
+    if not isinstance(q, torch.Tensor) or q.dtype != torch.int8 or not q.is_contiguous() \
+            or q.numel() < Mp * K:
         raise ValueError(f"K-tiled codes need a contiguous int8 tensor of {Mp * K} elements")
     return q
 
@@ -352,8 +449,17 @@ def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=
     gelu: quantise bf16(GELU(X)) instead (bf16 X, 6144 < K <= 24576), as the
     MLP path does with its intermediate."""
     lib = library()
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor [M, K]")
     M, K = X.shape
-    q = _codes(q, M, K, X.device)
+    _need(X, "X", (torch.bfloat16, torch.float32), (M, K))
+    q = _codes(q, M, K, X.device) if q is not None else None
+    _opt(s, "s", torch.float32, (M,))
+    if rotation not in ROTATIONS:
+        raise ValueError(f"rotation must be one of {sorted(ROTATIONS)}")
+    _on_device(X.device, X=X, q=q, s=s)
+    if q is None:
+        q = _codes(None, M, K, X.device)
     if s is None:
         s = torch.empty(M, dtype=torch.float32, device=X.device)
     flags = ROTATIONS[rotation] | (FLAG_GELU if gelu else 0)
@@ -366,9 +472,12 @@ def convrot_rotate_quantize(X: torch.Tensor, block: int, q=None, s=None, stream=
 def convrot_gemm_i32(q_x: torch.Tensor, M: int, W: PreparedWeights, out=None, stream=None):
     """acc [M, N] int32 from K-tiled codes q_x of M rows."""
     lib = library()
-    _codes(q_x, M, W.K, None)
+    dev = _weights(W, "W")
+    _codes(q_x, M, W.K, dev)
+    _output(out, M, W.N, torch.int32)
+    _on_device(dev, q_x=q_x, out=out)
     if out is None:
-        out = torch.empty((M, W.N), dtype=torch.int32, device=q_x.device)
+        out = torch.empty((M, W.N), dtype=torch.int32, device=dev)
     rc = lib.convrot_gemm_i32(_ptr(q_x), M, W.ref(), _ptr(out), _stream(stream))
     _check("convrot_gemm_i32", rc)
     return out
@@ -379,10 +488,17 @@ def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeight
                          stream=None):
     """Y [M, N] from K-tiled codes q_x and row scales s_x [M]."""
     lib = library()
+    dev = _weights(W, "W")
+    if not isinstance(s_x, torch.Tensor) or s_x.dim() != 1:
+        raise ValueError("s_x must be a 1-D tensor [M]")
     M = s_x.shape[0]
-    _codes(q_x, M, W.K, None)
+    _need(s_x, "s_x", torch.float32, (M,))
+    _codes(q_x, M, W.K, dev)
+    _opt(bias, "bias", torch.float32, (W.N,))
+    _output(out, M, W.N, (torch.bfloat16, torch.float32))
+    _on_device(dev, q_x=q_x, s_x=s_x, bias=bias, out=out)
     if out is None:
-        out = torch.empty((M, W.N), dtype=out_dtype, device=q_x.device)
+        out = torch.empty((M, W.N), dtype=out_dtype, device=dev)
     rc = lib.convrot_gemm_dequant(_ptr(q_x), _ptr(s_x), M, W.ref(), _ptr(bias), _ptr(out),
                                   _dtype_tag(out.dtype), FLAG_GELU if gelu else 0,
                                   _stream(stream))
@@ -395,11 +511,19 @@ def convrot_lowrank_factor1(q_x: torch.Tensor, s_x: torch.Tensor, A: PreparedWei
     """Factor 1 of the low-rank chain with its output rotated and requantised:
     returns (q_h, s_h), q_h the K-tiled codes (Mp, r), s_h [M] f32."""
     lib = library()
+    dev = _weights(A, "A")
+    if not isinstance(s_x, torch.Tensor) or s_x.dim() != 1:
+        raise ValueError("s_x must be a 1-D tensor [M]")
     M = s_x.shape[0]
-    _codes(q_x, M, A.K, None)
-    q_h = _codes(q_h, M, A.N, q_x.device)
+    _need(s_x, "s_x", torch.float32, (M,))
+    _codes(q_x, M, A.K, dev)
+    if q_h is not None:
+        _codes(q_h, M, A.N, dev)
+    _opt(s_h, "s_h", torch.float32, (M,))
+    _on_device(dev, q_x=q_x, s_x=s_x, q_h=q_h, s_h=s_h)
+    q_h = _codes(q_h, M, A.N, dev)
     if s_h is None:
-        s_h = torch.empty(M, dtype=torch.float32, device=q_x.device)
+        s_h = torch.empty(M, dtype=torch.float32, device=dev)
     rc = lib.convrot_lowrank_factor1(_ptr(q_x), _ptr(s_x), M, A.ref(), _ptr(q_h), _ptr(s_h),
                                      _stream(stream))
     _check("convrot_lowrank_factor1", rc)
@@ -409,9 +533,11 @@ def convrot_lowrank_factor1(q_x: torch.Tensor, s_x: torch.Tensor, A: PreparedWei
 def convrot_gelu_bf16(u: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     """bf16(GELU(u)) elementwise, as the MLP's up projection applies it."""
     lib = library()
-    if u.dtype != torch.bfloat16:
-        raise ValueError("u must be bf16")
+    if not isinstance(u, torch.Tensor) or u.dtype != torch.bfloat16:
+        raise ValueError("u must be a bf16 tensor")
     u = u.contiguous()
+    _opt(out, "out", torch.bfloat16, tuple(u.shape))
+    _on_device(u.device, u=u, out=out)
     if out is None:
         out = torch.empty_like(u)
     _check("convrot_gelu_bf16", lib.convrot_gelu_bf16(_ptr(u), u.numel(), _ptr(out),
