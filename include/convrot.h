@@ -35,10 +35,18 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates nothing and keeps no state between calls.  It is re-entrant:
- *     calls on different streams may overlap if they use separate workspaces.
+ *     allocates nothing and keeps no per-call state.  It is re-entrant: calls
+ *     on different streams may overlap if they use separate workspaces.  Its
+ *     one piece of device state is a read-only 65,536-entry bf16 GELU table
+ *     (one copy per device, in the library's code object), written once per
+ *     device by the first call of a GELU path (convrot_mlp_forward,
+ *     CONVROT_FLAG_GELU, convrot_gelu_bf16).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *     Calls are asynchronous on that stream; the host never synchronises.
+ *     Calls are asynchronous on that stream.  The host waits only once per
+ *     device: the first GELU-path call that is not being recorded into a graph
+ *     waits for its table fill, so that launches on any stream may read the
+ *     table from then on.  A GELU-path call recorded into a graph before that
+ *     records the fill too (each replay rewrites the same values).
  *   - Float matrices (X, Y, weights, intermediates in bf16) are row-major and
  *     dense; bf16 tensors hold raw bfloat16 bits.  INT8 code matrices (the
  *     test hooks' q_x and q_h, prepared weight codes) use the K-tiled layout

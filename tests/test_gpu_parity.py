@@ -746,6 +746,51 @@ def test_graph_capture_first_call_gelu_on_load(tmp_path):
     assert r.returncode == 0 and "capture-first ok" in r.stdout
 
 
+_GELU_ONCE = r'''
+import numpy as np, torch
+from w8a8_int8_rotated_amd import convrot as cr
+from w8a8_int8_rotated_amd import workloads as wl
+m = wl.scaled("mlp_16384", M=64, K=256, N=160, ffn=6400)      # GELU on load
+m2 = wl.scaled("mlp_16384", M=48, K=256, N=128, ffn=512)      # GELU in the up epilogue
+prep = lambda W, b: cr.convrot_linear_prepare_weights(torch.from_numpy(W).cuda(), b)
+pu, pd = prep(m.weight("w"), m.block), prep(m.weight("w2"), m.block)
+pu2, pd2 = prep(m2.weight("w"), m2.block), prep(m2.weight("w2"), m2.block)
+X = torch.from_numpy(m.activations().view(np.int16)).cuda().view(torch.bfloat16)
+X2 = torch.from_numpy(m2.activations().view(np.int16)).cuda().view(torch.bfloat16)
+side = torch.cuda.Stream()
+outs = []
+for i in range(3):
+    outs.append(cr.convrot_mlp_forward(X, pu, pd))
+    with torch.cuda.stream(side):
+        outs.append(cr.convrot_mlp_forward(X2, pu2, pd2))
+    cr.convrot_gelu_bf16(X2)
+torch.cuda.synchronize()
+for a, b in zip(outs[0::2], outs[2::2]):
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+print("gelu-once ok", flush=True)
+'''
+
+
+def test_gelu_table_written_once_per_device(cr, tmp_path):
+    """The GELU table is written by the first GELU-path call and by no later
+    one: a fresh process making nine GELU-path calls on two streams (both MLP
+    forms and the elementwise hook) logs exactly one table write, and its
+    repeated forwards agree bit for bit."""
+    import os
+    import subprocess
+    import sys
+    announce("GELU table written once per device")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = tmp_path / "gelu_once.py"
+    script.write_text(_GELU_ONCE)
+    r = subprocess.run([sys.executable, str(script)], capture_output=True, text=True,
+                       timeout=110, cwd=root,
+                       env=dict(os.environ, PYTHONPATH=root, CONVROT_LOG="1"))
+    print(r.stdout.strip(), r.stderr.strip()[-1500:], flush=True)
+    assert r.returncode == 0 and "gelu-once ok" in r.stdout
+    assert r.stderr.count("GELU table written") == 1, r.stderr
+
+
 def _sweep_cases(n, seed=2024):
     """Seeded random linear configurations: M, K, N, block, rotation kind,
     output type, bias, activation distribution."""

@@ -86,8 +86,10 @@ hipError_t launch_lowrank_f1(const int8_t *qx, const int8_t *qa, const float *sx
 
 // g[i] = bf16(GELU(u[i])) for bf16 u, as the MLP's up projection applies it.
 hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream);
-// Fill the 65,536-entry bf16 GELU table (stream-ordered) and return its device
-// address on the current device.
+// The device address of the 65,536-entry bf16 GELU table on the current
+// device, written on `stream` if it has not been yet: the first such call that
+// is not being recorded into a graph waits for the fill once, after which no
+// call launches it again on that device.
 hipError_t launch_gelu_table(const uint16_t **table, hipStream_t stream);
 
 // INT8 codes [R, C] into the K-tiled layout (R % 16 == 0, C % 64 == 0); the

@@ -60,6 +60,8 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
+#include <cstdlib>
 #include <utility>
 
 namespace convrot {
@@ -159,9 +161,12 @@ __device__ __forceinline__ float dequant1(int acc, float sxm, float swn, float b
 // 0.5 z (1 + erf(z / sqrt 2)), evaluated in fp64 on the bf16 value z of the
 // up projection's output, then rounded to fp32 and to bf16 (round to nearest
 // even both times).  The MLP's up projection looks its outputs up here
-// instead of evaluating erf per element.  Every launch that reads the table is
-// preceded on its own stream by a launch that (re)writes it with the same
-// values, so a reader never sees a partial table.
+// instead of evaluating erf per element.  The table is written once per device
+// (launch_gelu_table): the first call of a GELU path that is not being
+// recorded into a graph fills it on its stream and waits for the fill, and
+// every later launch on any stream reads the finished table.  A call recorded
+// into a graph before that records the fill too, and each replay rewrites the
+// table with the same values.
 __device__ __align__(16) uint16_t g_gelu_bf16[65536];
 
 __global__ __launch_bounds__(256) void gelu_table_kernel()
@@ -1169,8 +1174,11 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
                     const float *bias, void *Y, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream)
 {
-    if constexpr (OUT == int(OutKind::GELU_BF16))
-        hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
+    if constexpr (OUT == int(OutKind::GELU_BF16)) {
+        const uint16_t *table = nullptr;
+        const hipError_t e = launch_gelu_table(&table, stream);
+        if (e != hipSuccess) return e;
+    }
     const int cus = device_cu_count();
     const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
     auto rounds = [&](int64_t tiles) { return (double)((tiles + cus - 1) / cus); };
@@ -1225,13 +1233,15 @@ hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
 
 hipError_t launch_gelu_table(const uint16_t **table, hipStream_t stream)
 {
-    // the table's device address, per device ordinal (each device holds its
-    // own copy of the module's globals); racing first queries store the same
+    // per device ordinal (each device holds its own copy of the module's
+    // globals): the table's device address, and whether it has been written
     static std::atomic<const uint16_t *> cached[64];
+    static std::atomic<int> filled[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    const uint16_t *p = dev >= 0 && dev < 64 ? cached[dev].load(std::memory_order_relaxed) : nullptr;
+    const bool known = dev >= 0 && dev < 64;
+    const uint16_t *p = known ? cached[dev].load(std::memory_order_relaxed) : nullptr;
     if (!p) {
         void *a = nullptr;
         e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_gelu_bf16));
@@ -1239,17 +1249,32 @@ hipError_t launch_gelu_table(const uint16_t **table, hipStream_t stream)
         p = static_cast<const uint16_t *>(a);
         // readers copy it in 16-byte pieces
         if (reinterpret_cast<uintptr_t>(p) & 15) return hipErrorInvalidValue;
-        if (dev >= 0 && dev < 64) cached[dev].store(p, std::memory_order_relaxed);
+        if (known) cached[dev].store(p, std::memory_order_relaxed);
     }
-    hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
     *table = p;
-    return hipGetLastError();
+    if (known && filled[dev].load(std::memory_order_acquire)) return hipSuccess;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess || cap != hipStreamCaptureStatusNone || !known) return e;
+    // the one wait of the library: once per device, so that launches on other
+    // streams may read the table without being ordered after this one
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return e;
+    filled[dev].store(1, std::memory_order_release);
+    if (std::getenv("CONVROT_LOG") && std::getenv("CONVROT_LOG")[0] == '1')
+        std::fprintf(stderr, "[convrot] GELU table written on device %d\n", dev);
+    return hipSuccess;
 }
 
 hipError_t launch_gelu_bf16(const uint16_t *u, uint16_t *g, int64_t n, hipStream_t stream)
 {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(gelu_table_kernel, dim3(256), dim3(256), 0, stream);
+    const uint16_t *table = nullptr;
+    const hipError_t e = launch_gelu_table(&table, stream);
+    if (e != hipSuccess) return e;
     // 16-byte aligned buffers: 8 values per thread from the LDS slice, the
     // last n % 8 one per thread; otherwise one per thread throughout
     const bool vec = ((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(g)) & 15) == 0;
