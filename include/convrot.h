@@ -57,7 +57,11 @@
  *   - Non-finite inputs give unspecified (but memory-safe) results.
  *   - Shape limits: K % 128 == 0, N % 16 == 0, K <= 65536, Mp*K < 2^31 with
  *     Mp = M rounded up to a multiple of 16, N*K < 2^31 (EUNSUPPORTED
- *     otherwise).  M == 0 is a no-op returning OK.
+ *     otherwise).  M == 0 is a no-op returning OK.  The contraction consumes
+ *     K in pairs of 64-byte K-tiles, hence K % 128.  A layer whose K is an
+ *     odd multiple of 64 (b = 64) is served exactly by padding K with one
+ *     zero block: zero columns of X and W rotate to zero blocks, change no
+ *     row amax and add nothing to the INT32 sum.
  *
  * K-tiled INT8 layout of a code matrix with M rows of K codes (K % 64 == 0):
  * rows are padded to Mp (a multiple of 16) and the code (m, k) sits at byte
@@ -158,25 +162,34 @@ CONVROT_API int convrot_version(void);
 /* sizing queries (host only, no HIP calls)                            */
 /* ------------------------------------------------------------------ */
 
-/* Bytes of packed codes for an [N, K] weight (0 for invalid shapes). */
+/* Bytes of packed codes for an [N, K] weight (0 for invalid shapes): one
+ * INT8 code per weight, as the INT8 checkpoint stores them (PulpCut input-major
+ * README, "Input-major checkpoint"), in the K-tiled layout above. */
 CONVROT_API size_t convrot_weights_packed_bytes(int64_t N, int64_t K, int block);
 
-/* Workspace for convrot_linear_prepare_weights (0 is a valid answer). */
+/* Workspace for convrot_linear_prepare_weights (0 is a valid answer): the
+ * transposed float weights when an input-major [input, output] source is
+ * rotated (PulpCut input-major README, "Input-major checkpoint"). */
 CONVROT_API size_t convrot_prepare_workspace_bytes(int64_t N, int64_t K, int block,
                                        int w_dtype, int layout);
 
 /* Workspace for convrot_linear_forward: K-tiled INT8 codes (Mp x K bytes) and
  * F32 row scales [M] of the rotated activations, each region 256-byte
- * aligned. */
+ * aligned.  A caller-owned static workspace stands in for per-call
+ * allocation (MiniMax-H3-Rung-Omega README, "Technical Architecture
+ * Overview", Floor 1: one contiguous workspace instead of per-call mallocs). */
 CONVROT_API size_t convrot_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int block);
 
 /* Workspace for lowrank_convrot_forward (codes of X, bf16 intermediate
- * H [M, r], codes of H, and row scales). */
+ * H [M, r], codes of H, and row scales) -- the low-rank linears of the INT8
+ * package (HyperFlow H3 Flash card, "Choose a Weight Format"). */
 CONVROT_API size_t lowrank_convrot_workspace_bytes(int64_t M, int64_t K, int64_t r,
                                        int64_t N, int block);
 
 /* Workspace for convrot_mlp_forward (codes of X, the bf16 intermediate u or g [M, F],
- * codes of g, row scales). */
+ * codes of g, row scales): the MLP whose activation feeds a rotated, rowwise
+ * quantised fc2 (MiniMax-H3-Rung-Omega README, "Technical Architecture
+ * Overview", Floor 1). */
 CONVROT_API size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
                                    int block);
 
@@ -184,7 +197,12 @@ CONVROT_API size_t convrot_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, 
 /* weight preparation (load time)                                      */
 /* ------------------------------------------------------------------ */
 
-/* Rotate, quantise and pack one weight matrix.
+/* Rotate, quantise and pack one weight matrix: the INT8 codes with one F32
+ * scale per output channel, output-major [output, input] or input-major
+ * [input, output] at the source (PulpCut input-major README, "Input-major
+ * checkpoint"), rotated so that dequantising and undoing the rotation gives
+ * the weights back (HyperFlow H3 Flash MLX card, "Where the weights come
+ * from").
  *   W         device; F32 or BF16 float weights, or I8 codes that are already
  *             rotated (import mode).  Layout per `layout`:
  *             CONVROT_OUT_MAJOR -> [N, K], CONVROT_IN_MAJOR -> [K, N].
@@ -207,11 +225,50 @@ CONVROT_API int convrot_linear_prepare_weights(const void *W, int w_dtype, int l
                                    int block, convrot_weights *out, void *ws,
                                    size_t ws_bytes, void *stream);
 
+/* The rank a low-rank pair is stored with (0 for r <= 0, r > 65536 or a bad
+ * block): r rounded up to a multiple of 128, or of 256 when b = 256.  The
+ * checkpoint loader pads low-rank ranks to a multiple of 64 (HyperFlow H3
+ * Flash card, "Standalone Transformer (AutoModel)", pad_lowrank_ranks); 128
+ * is such a multiple and the contraction's K granularity, and 256 lets whole
+ * blocks tile the rank. */
+CONVROT_API int64_t lowrank_convrot_padded_rank(int64_t r, int block);
+
+/* Workspace for lowrank_convrot_prepare_weights: the zero-padded float copies
+ * of both factors when the rank needs padding, else 0. */
+CONVROT_API size_t lowrank_convrot_prepare_workspace_bytes(int64_t r, int64_t K, int64_t N,
+                                                           int block, int w_dtype);
+
+/* Prepare a low-rank pair W ~ B . A (HyperFlow H3 Flash card, "Choose a Weight
+ * Format" and "Standalone Transformer (AutoModel)"):
+ *   A, B      device float weights (w_dtype CONVROT_F32 or CONVROT_BF16), both
+ *             output-major and row-major: A [r, K], B [N, r].
+ *   outA      prepared [rp, K] factor, rp = lowrank_convrot_padded_rank(r, b);
+ *             outA->codes / outA->scale point to caller allocations of
+ *             convrot_weights_packed_bytes(rp, K, b) and 4*rp bytes.
+ *   outB      prepared [N, rp] factor; convrot_weights_packed_bytes(N, rp, b)
+ *             and 4*N bytes.  outA->flags == outB->flags selects the rotation
+ *             kind, as for convrot_linear_prepare_weights.
+ *   ws        device workspace of lowrank_convrot_prepare_workspace_bytes(...)
+ *             (may be NULL when it is 0); it is read in stream order.
+ * The rank is padded with zero rows of A and zero columns of B, which leaves
+ * B . A unchanged; their rotated blocks are zero, so when b divides r the
+ * forward equals the unpadded chain bit for bit.  Errors as for
+ * convrot_linear_prepare_weights (EUNSUPPORTED for other dtypes or for padded
+ * shapes outside the limits). */
+CONVROT_API int lowrank_convrot_prepare_weights(const void *A, const void *B, int w_dtype,
+                                                int64_t r, int64_t K, int64_t N, int block,
+                                                convrot_weights *outA, convrot_weights *outB,
+                                                void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* forward entry points                                                */
 /* ------------------------------------------------------------------ */
 
-/* Y = dequant(Q(R x) . Q(W R^T)^T) (+ bias) for every row x of X.
+/* Y = dequant(Q(R x) . Q(W R^T)^T) (+ bias) for every row x of X: the W8A8
+ * linear behind a block-diagonal Hadamard rotation (lehuy.net article on
+ * HyperFlow H3 Flash, "Cach nen hoat dong", second bullet), the activation
+ * rotated and quantised row-wise first (MiniMax-H3-Rung-Omega README,
+ * "Technical Architecture Overview", Floor 1).
  *   X       device bf16 [M, W->K] activations.
  *   W       prepared weights (host struct).
  *   bias    device F32 [W->N] or NULL.
@@ -223,7 +280,9 @@ CONVROT_API int convrot_linear_forward(const void *X, int64_t M, const convrot_w
                            const float *bias, void *Y, int y_dtype, void *ws,
                            size_t ws_bytes, void *stream);
 
-/* Low-rank ConvRot linear: h = bf16(linear(X; A)) with A [r, K] and no bias,
+/* Low-rank ConvRot linear (HyperFlow H3 Flash card, "Choose a Weight Format":
+ * the INT8 package holds W8A8 linears and low-rank factorised ones; both
+ * factors are W8A8 here): h = bf16(linear(X; A)) with A [r, K] and no bias,
  * then Y = linear(h; B) with B [N, r] and the bias; h is re-rotated along r
  * with the same block and requantised per token.  Requires A->N == B->K (= r),
  * A->block == B->block, the same rotation kind (A->flags == B->flags) and
@@ -234,7 +293,11 @@ CONVROT_API int lowrank_convrot_forward(const void *X, int64_t M, const convrot_
                             void *Y, int y_dtype, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* MLP pair: u = bf16(linear(X; W_up) + bias_up); g = bf16(GELU(u)) with the
+/* MLP pair, its activation applied in front of the rotated, rowwise
+ * quantised down projection (MiniMax-H3-Rung-Omega README, "Technical
+ * Architecture Overview", Floor 1, fuses the activation, ConvRot and the
+ * rowwise INT8 quantise ahead of MLP.fc2):
+ * u = bf16(linear(X; W_up) + bias_up); g = bf16(GELU(u)) with the
  * erf form of GELU (see convrot_gelu_bf16); Y = linear(g; W_down) + bias_down.
  * Requires W_up->N == W_down->K (= F) and the same block and rotation kind.
  * Where GELU runs depends on F only, never the result: for 6144 < F <= 24576
@@ -271,7 +334,10 @@ CONVROT_API int lowrank_bf16_forward(const void *X, int64_t M, int64_t K, const 
 /* tests.  Same validation and error behaviour as the entry points.    */
 /* ------------------------------------------------------------------ */
 
-/* Rotate and quantise rows: X [M, K] row-major (x_dtype F32 or BF16) -> q
+/* Rotate and quantise rows (the rotation and rowwise INT8 quantise of
+ * MiniMax-H3-Rung-Omega README, "Technical Architecture Overview", Floor 1;
+ * for F32 weight rows, the weight preparation of convrot_linear_prepare_weights):
+ * X [M, K] row-major (x_dtype F32 or BF16) -> q
  * K-tiled int8 codes (Mp x K bytes; the padding rows are left as they were)
  * and s [M] F32.  flags: 0 or CONVROT_ROT_REGULAR (the rotation kind), plus
  * optionally CONVROT_FLAG_GELU (defined below): the rows are then
@@ -284,11 +350,14 @@ CONVROT_API int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, i
                             void *stream);
 
 /* Exact INT32 contraction acc[M, N] (row-major) = q_x . codes(W)^T, q_x the
- * K-tiled codes of M rows (Mp x W->K bytes). */
+ * K-tiled codes of M rows (Mp x W->K bytes): the INT8 GEMM of the W8A8 linear
+ * (mmh3turbo README, "Why it is fast, and where it is not"). */
 CONVROT_API int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W,
                      int32_t *acc, void *stream);
 
-/* Contraction plus the dequant epilogue from given codes and row scales:
+/* Contraction plus the dequant epilogue from given codes and row scales,
+ * per token (s_x) and per output channel (s_w, the checkpoint's per-output
+ * F32 scales: PulpCut input-major README, "Input-major checkpoint"):
  * Y = ((float)(q_x . codes(W)^T) * s_x) * s_w (+ bias).  With
  * CONVROT_FLAG_GELU (y_dtype must be BF16) the epilogue writes
  * bf16(GELU(float(bf16(Y)))), the activation the MLP entry point feeds to its
@@ -313,7 +382,9 @@ CONVROT_API int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int
                             const convrot_weights *A, int8_t *q_h, float *s_h,
                             void *stream);
 
-/* g[i] = bf16(GELU(u[i])) for n bf16 values, exactly as the MLP entry point
+/* The activation in front of fc2 (MiniMax-H3-Rung-Omega README, "Technical
+ * Architecture Overview", Floor 1), GELU form:
+ * g[i] = bf16(GELU(u[i])) for n bf16 values, exactly as the MLP entry point
  * and CONVROT_FLAG_GELU apply it: GELU in its erf form, 0.5 z (1 + erf(z /
  * sqrt 2)), evaluated in fp64 on the bf16 value z, rounded to fp32 and then
  * to bf16 (nearest even).  u and g are device pointers; n >= 0. */

@@ -4,7 +4,10 @@
  * one linear forward with bias and fp32 output, and checks the weight codes,
  * the weight scales and every output against the CPU oracle linked beside
  * it, bit for bit.  It also checks that a misaligned pointer is rejected
- * before anything is launched.
+ * before anything is launched.  Then it prepares low-rank pairs whose rank
+ * needs padding (lowrank_convrot_prepare_weights) and runs the low-rank
+ * forward with bias: outputs bit for bit against the oracle's chain on the
+ * unpadded factors when b divides r, on zero-padded factors otherwise.
  *
  * Test infrastructure: tests/test_c_abi.py builds it with gcc and runs it.
  * Exit status 0 = every check passed.
@@ -24,6 +27,10 @@ int oracle_rotate_quantize_rows_rot(const void *src, int dtype, int64_t rows, in
 int oracle_linear_forward(const uint16_t *X, int64_t M, int64_t K, int b, const int8_t *qw,
                           const float *sw, int64_t N, const float *bias, int out_dtype,
                           void *out);
+int oracle_lowrank_forward(const uint16_t *X, int64_t M, int64_t K, int b, const int8_t *qa,
+                           const float *sa, int64_t r, const int8_t *qb, const float *sb,
+                           int64_t N, const float *bias, int out_dtype, void *out,
+                           uint16_t *h_out);
 
 #define HIP_OK(x)                                                                  \
     do {                                                                           \
@@ -63,6 +70,73 @@ static int64_t tiled(int64_t m, int64_t k, int64_t K)
 {
     return ((m / 16) * (K / 64) + k / 64) * 1024 + (m % 16) * 64 +
            (((k / 16) % 4) ^ ((m / 4) % 4)) * 16 + k % 16;
+}
+
+/* One low-rank pair A [r, K], B [N, r] (fp32, seeded), rank r padded by the
+ * library; returns the number of fp32 outputs that differ from the oracle
+ * (or a negative code on a failed call). */
+static int64_t lowrank_case(const uint16_t *X, const void *dX, int64_t M, int64_t K, int64_t r,
+                            int64_t N, int b, uint64_t *seed)
+{
+    const int64_t rp = lowrank_convrot_padded_rank(r, b);
+    /* the oracle's factors: unpadded when b divides r, else zero-padded */
+    const int64_t ro = (r % b == 0) ? r : rp;
+    float *A = calloc((size_t)(ro * K), sizeof(float)), *B = calloc((size_t)(N * ro), sizeof(float));
+    float *A0 = malloc(sizeof(float) * r * K), *B0 = malloc(sizeof(float) * N * r);
+    float *bias = malloc(sizeof(float) * N), *Y = malloc(sizeof(float) * M * N);
+    float *Yref = malloc(sizeof(float) * M * N), *sa = malloc(sizeof(float) * ro);
+    float *sb = malloc(sizeof(float) * N);
+    int8_t *qa = malloc((size_t)(ro * K)), *qb = malloc((size_t)(N * ro));
+    if (!A || !B || !A0 || !B0 || !bias || !Y || !Yref || !sa || !sb || !qa || !qb || rp <= 0)
+        return -4;
+    for (int64_t i = 0; i < r * K; ++i) A0[i] = A[i] = 0.05f * uniform(seed);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < r; ++j) B0[n * r + j] = B[n * ro + j] = 0.05f * uniform(seed);
+    for (int64_t i = 0; i < N; ++i) bias[i] = 0.5f * uniform(seed);
+
+    void *dA, *dB, *dca, *dsa, *dcb, *dsb, *dbias, *dY, *dwp = NULL, *dws;
+    const size_t ca = convrot_weights_packed_bytes(rp, K, b), cb = convrot_weights_packed_bytes(N, rp, b);
+    const size_t wp = lowrank_convrot_prepare_workspace_bytes(r, K, N, b, CONVROT_F32);
+    const size_t wf = lowrank_convrot_workspace_bytes(M, K, rp, N, b);
+    if (!ca || !cb || !wf || (rp != r && !wp)) return -5;
+    if (hipMalloc(&dA, sizeof(float) * r * K) || hipMalloc(&dB, sizeof(float) * N * r) ||
+        hipMalloc(&dca, ca) || hipMalloc(&dsa, 4 * rp) || hipMalloc(&dcb, cb) ||
+        hipMalloc(&dsb, 4 * N) || hipMalloc(&dbias, 4 * N) || hipMalloc(&dY, 4 * M * N) ||
+        (wp && hipMalloc(&dwp, wp)) || hipMalloc(&dws, wf))
+        return -2;
+    if (hipMemcpy(dA, A0, sizeof(float) * r * K, hipMemcpyHostToDevice) ||
+        hipMemcpy(dB, B0, sizeof(float) * N * r, hipMemcpyHostToDevice) ||
+        hipMemcpy(dbias, bias, 4 * N, hipMemcpyHostToDevice))
+        return -2;
+    convrot_weights wa, wb;
+    memset(&wa, 0, sizeof wa);
+    memset(&wb, 0, sizeof wb);
+    wa.codes = (int8_t *)dca; wa.scale = (float *)dsa;
+    wb.codes = (int8_t *)dcb; wb.scale = (float *)dsb;
+    int rc = lowrank_convrot_prepare_weights(dA, dB, CONVROT_F32, r, K, N, b, &wa, &wb, dwp, wp,
+                                             NULL);
+    if (rc == CONVROT_OK && (wa.N != rp || wb.K != rp)) rc = -6;
+    if (rc == CONVROT_OK)
+        rc = lowrank_convrot_forward(dX, M, &wa, &wb, dbias, dY, CONVROT_F32, dws, wf, NULL);
+    if (rc != CONVROT_OK) {
+        fprintf(stderr, "low-rank r=%lld b=%d: %s\n", (long long)r, b, convrot_status_string(rc));
+        return -3;
+    }
+    if (hipDeviceSynchronize() || hipMemcpy(Y, dY, 4 * M * N, hipMemcpyDeviceToHost)) return -2;
+    if (oracle_rotate_quantize_rows_rot(A, 0, ro, K, K, b, 0, qa, sa) != 0 ||
+        oracle_rotate_quantize_rows_rot(B, 0, N, ro, ro, b, 0, qb, sb) != 0 ||
+        oracle_lowrank_forward(X, M, K, b, qa, sa, ro, qb, sb, N, bias, 0, Yref, NULL) != 0)
+        return -6;
+    int64_t bad = 0;
+    for (int64_t i = 0; i < M * N; ++i) bad += memcmp(&Y[i], &Yref[i], 4) != 0;
+    printf("c-abi low-rank M=%lld K=%lld r=%lld (stored %lld) N=%lld b=%d: %lld outputs differ "
+           "from the oracle\n", (long long)M, (long long)K, (long long)r, (long long)rp,
+           (long long)N, b, (long long)bad);
+    hipFree(dA); hipFree(dB); hipFree(dca); hipFree(dsa); hipFree(dcb); hipFree(dsb);
+    hipFree(dbias); hipFree(dY); hipFree(dwp); hipFree(dws);
+    free(A); free(B); free(A0); free(B0); free(bias); free(Y); free(Yref); free(sa); free(sb);
+    free(qa); free(qb);
+    return bad;
 }
 
 int main(void)
@@ -130,6 +204,11 @@ int main(void)
            "differ from the oracle\n",
            (long long)M, (long long)K, (long long)N, b, (long long)bad_codes,
            (long long)bad_scales, (long long)bad_out);
+    /* low-rank pairs: r = 192 at b = 64 (padded to 256, b divides r) and
+     * r = 320 at b = 128 (padded to 384, b does not divide r) */
+    const int64_t lr1 = lowrank_case(X, dX, M, K, 192, 272, 64, &seed);
+    const int64_t lr2 = lowrank_case(X, dX, M, K, 320, 272, 128, &seed);
+    if (lr1 != 0 || lr2 != 0) return lr1 < 0 || lr2 < 0 ? 7 : 1;
     hipFree(dX); hipFree(dW); hipFree(dcodes); hipFree(dscale); hipFree(dbias); hipFree(dY);
     hipFree(dwsp); hipFree(dwsf);
     free(X); free(W); free(bias); free(Y); free(Yref); free(sw); free(sw_ref); free(qw_ref);

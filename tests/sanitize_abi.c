@@ -72,6 +72,9 @@ int main(void)
                 acc += lowrank_convrot_workspace_bytes(dims[i], dims[j], 512, dims[j], blocks[k]);
                 acc += convrot_mlp_workspace_bytes(dims[i], dims[j], 21504, dims[j], blocks[k]);
                 acc += lowrank_bf16_workspace_bytes(dims[i], dims[j]);
+                acc += lowrank_convrot_prepare_workspace_bytes(dims[i], dims[j], dims[j],
+                                                               blocks[k], CONVROT_F32);
+                acc += (size_t)lowrank_convrot_padded_rank(dims[i], blocks[k]);
             }
     EXPECT(convrot_weights_packed_bytes(16, 65536 + 128, 128) == 0, 1);
     EXPECT(convrot_weights_packed_bytes(512, 5376, 128) == (size_t)512 * 5376, 1);
@@ -181,6 +184,41 @@ int main(void)
     EXPECT(lowrank_bf16_forward(FAKE, 8, 500, FAKE, 64, FAKE, 256, NULL, FAKE, FAKE, 1 << 20,
                                 NULL),
            CONVROT_EUNSUPPORTED);
+    /* low-rank preparation: rank padding and validation */
+    EXPECT(lowrank_convrot_padded_rank(192, 64), 256);
+    EXPECT(lowrank_convrot_padded_rank(320, 128), 384);
+    EXPECT(lowrank_convrot_padded_rank(320, 256), 512);
+    EXPECT(lowrank_convrot_padded_rank(512, 128), 512);
+    EXPECT(lowrank_convrot_padded_rank(0, 128), 0);
+    EXPECT(lowrank_convrot_prepare_workspace_bytes(512, 5376, 5376, 128, CONVROT_F32) == 0, 1);
+    EXPECT(lowrank_convrot_prepare_workspace_bytes(192, 512, 272, 64, CONVROT_BF16) ==
+               (size_t)256 * 512 * 2 + (size_t)272 * 256 * 2, 1);
+    EXPECT(lowrank_convrot_prepare_workspace_bytes(192, 512, 272, 64, CONVROT_I8) == 0, 1);
+    convrot_weights pa = desc(0, 0, 0), pb = desc(0, 0, 0);
+    pa.magic = pb.magic = 0;
+    EXPECT(lowrank_convrot_prepare_weights(FAKE, FAKE, CONVROT_I8, 192, 512, 272, 64, &pa, &pb,
+                                           FAKE, 1 << 20, NULL),
+           CONVROT_EUNSUPPORTED);
+    EXPECT(lowrank_convrot_prepare_weights(FAKE, FAKE, CONVROT_F32, 192, 512, 272, 64, &pa, &pb,
+                                           NULL, 0, NULL),
+           CONVROT_EWORKSPACE);
+    EXPECT(lowrank_convrot_prepare_weights(FAKE, FAKE, CONVROT_F32, 192, 500, 272, 64, &pa, &pb,
+                                           FAKE, 1 << 20, NULL),
+           CONVROT_EINVAL);
+    EXPECT(lowrank_convrot_prepare_weights(FAKE_ODD, FAKE, CONVROT_F32, 192, 512, 272, 64, &pa,
+                                           &pb, FAKE, 1 << 20, NULL),
+           CONVROT_EALIGN);
+    EXPECT(lowrank_convrot_prepare_weights(FAKE, FAKE, CONVROT_F32, 192, 512, 270, 64, &pa, &pb,
+                                           FAKE, 1 << 20, NULL),
+           CONVROT_EUNSUPPORTED);
+    EXPECT(lowrank_convrot_prepare_weights(NULL, FAKE, CONVROT_F32, 192, 512, 272, 64, &pa, &pb,
+                                           FAKE, 1 << 20, NULL),
+           CONVROT_EINVAL);
+    pb.flags = CONVROT_ROT_REGULAR;
+    EXPECT(lowrank_convrot_prepare_weights(FAKE, FAKE, CONVROT_F32, 192, 512, 272, 64, &pa, &pb,
+                                           FAKE, 1 << 20, NULL),
+           CONVROT_EINVAL);
+    EXPECT(pa.magic == 0 && pb.magic == 0, 1);
     int64_t ops = 0;
     EXPECT(convrot_probe_mfma_i8(0, FAKE, FAKE, &ops, NULL), CONVROT_EINVAL);
     EXPECT(convrot_probe_stream(FAKE, FAKE, 64, 3, NULL), CONVROT_EINVAL);

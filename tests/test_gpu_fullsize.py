@@ -48,8 +48,19 @@ def test_qkv_38656_fullsize(cr):
     y_ref = oracle.linear_forward(x[rows], qw, sw, w.block, out="bf16")
     yr = bf16_bits(y[torch.from_numpy(rows).cuda()])
     assert assert_output_parity(yr, y_ref, "bf16", "qkv_38656 sampled rows") == 0
-    acc = cr.convrot_gemm_i32(to_dev(tile(qx_ref[rows[:16]])), 16, pw)
-    assert np.array_equal(host(acc), oracle.gemm_i32(qx_ref[rows[:16]], qw))
+    # INT32 accumulators from the full-size launch: one row in every 256-row
+    # tile (at an offset that walks through the tile) plus the sampled rows
+    acc = cr.convrot_gemm_i32(qx, w.M, pw)
+    tiles = (w.M + 255) // 256
+    per_tile = np.minimum(np.arange(tiles) * 256 + (np.arange(tiles) * 37) % 256, w.M - 1)
+    arows = np.unique(np.concatenate([per_tile, rows]))
+    got = host(acc[torch.from_numpy(arows).cuda()])
+    del acc
+    want = oracle.gemm_i32(qx_ref[arows], qw)
+    bad = int(np.count_nonzero(got != want))
+    print(f"[parity] qkv_38656 INT32: {bad} differ on {len(arows)} rows "
+          f"(every one of {tiles} m-tiles)", flush=True)
+    assert bad == 0
 
 
 def test_lowrank_38656_fullsize(cr):

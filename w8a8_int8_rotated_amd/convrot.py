@@ -54,6 +54,10 @@ _SIGNATURES = {
     "convrot_linear_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int]),
     "lowrank_convrot_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
     "convrot_mlp_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int]),
+    "lowrank_convrot_padded_rank": (_c_i64, [_c_i64, _c_int]),
+    "lowrank_convrot_prepare_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_int, _c_int]),
+    "lowrank_convrot_prepare_weights": (
+        _c_int, [_c_p, _c_p, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _W, _W, _c_p, _c_sz, _c_p]),
     "convrot_linear_prepare_weights": (
         _c_int, [_c_p, _c_int, _c_int, _c_p, _c_i64, _c_i64, _c_int, _W, _c_p, _c_sz, _c_p]),
     "convrot_linear_forward": (
@@ -298,29 +302,54 @@ def convrot_linear_prepare_weights(W: torch.Tensor, block: int, layout: int = OU
 
 
 def lowrank_padded_rank(r: int, block: int) -> int:
-    """The rank a low-rank pair is stored with: r rounded up to a multiple of
-    128 (the contraction's K granularity) and of the Hadamard block b."""
-    m = 256 if block == 256 else 128
-    return (r + m - 1) // m * m
+    """The rank a low-rank pair is stored with (lowrank_convrot_padded_rank)."""
+    return library().lowrank_convrot_padded_rank(r, block)
 
 
 def convrot_lowrank_prepare(A: torch.Tensor, B: torch.Tensor, block: int, stream=None,
                             rotation: str = "sylvester"):
-    """Prepare a low-rank pair W ~ B . A, A [r, K] and B [N, r] (output-major),
-    padding the rank with zero rows of A and zero columns of B to
-    lowrank_padded_rank(r, block), as the checkpoint loader pads ranks to a
-    multiple of 64.  The padding leaves the product B . A unchanged; when r is
-    already a multiple of b, the rotated and requantised intermediate of the
-    real rank positions is unchanged too."""
-    if A.dim() != 2 or B.dim() != 2 or B.shape[1] != A.shape[0]:
-        raise ValueError("A must be [r, K] and B [N, r]")
-    r = A.shape[0]
-    rp = lowrank_padded_rank(r, block)
-    if rp != r:
-        A = torch.cat([A, A.new_zeros((rp - r, A.shape[1]))], dim=0)
-        B = torch.cat([B, B.new_zeros((B.shape[0], rp - r))], dim=1)
-    pa = convrot_linear_prepare_weights(A.contiguous(), block, stream=stream, rotation=rotation)
-    pb = convrot_linear_prepare_weights(B.contiguous(), block, stream=stream, rotation=rotation)
+    """Prepare a low-rank pair W ~ B . A, A [r, K] and B [N, r] (output-major,
+    float32 or bfloat16) with lowrank_convrot_prepare_weights, which pads the
+    rank with zero rows of A and zero columns of B to
+    lowrank_padded_rank(r, block).  Returns two PreparedWeights."""
+    lib = library()
+    for t, name in ((A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
+    r, K = A.shape
+    N = B.shape[0]
+    if A.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"A must be float32 or bfloat16, got {A.dtype}")
+    B = B.contiguous()
+    _need(B, "B", A.dtype, (N, r))
+    if rotation not in ROTATIONS:
+        raise ValueError(f"rotation must be one of {sorted(ROTATIONS)}")
+    A = A.contiguous()
+    _on_device(A.device, A=A, B=B)
+    tag = _dtype_tag(A.dtype)
+    rp = lib.lowrank_convrot_padded_rank(r, block)
+    na, nb = lib.convrot_weights_packed_bytes(rp, K, block), lib.convrot_weights_packed_bytes(N, rp, block)
+    if rp == 0 or na == 0 or nb == 0:
+        raise ConvRotError("lowrank_convrot_prepare_weights", EUNSUPPORTED)
+    dev = A.device
+    pws = []
+    descs = []
+    for n, nbytes in ((rp, na), (N, nb)):
+        d = convrot_weights()
+        codes = torch.empty(nbytes, dtype=torch.int8, device=dev)
+        scale = torch.empty(n, dtype=torch.float32, device=dev)
+        d.codes, d.scale, d.flags = codes.data_ptr(), scale.data_ptr(), ROTATIONS[rotation]
+        descs.append(d)
+        pws.append((codes, scale))
+    wsb = lib.lowrank_convrot_prepare_workspace_bytes(r, K, N, block, tag)
+    ws = _workspace(wsb, dev, None)
+    rc = lib.lowrank_convrot_prepare_weights(
+        _ptr(A), _ptr(B), tag, r, K, N, block, ctypes.byref(descs[0]), ctypes.byref(descs[1]),
+        _ptr(ws), wsb, _stream(stream))
+    _check("lowrank_convrot_prepare_weights", rc)
+    pa = PreparedWeights(descs[0], *pws[0])
+    pb = PreparedWeights(descs[1], *pws[1])
+    pa._ws = pb._ws = ws    # keep alive until the stream has consumed it
     return pa, pb
 
 

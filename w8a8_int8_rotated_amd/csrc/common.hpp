@@ -97,6 +97,11 @@ hipError_t launch_gelu_table(const uint16_t **table, hipStream_t stream);
 hipError_t launch_tile_codes(const int8_t *src, bool transposed, int8_t *dst, int64_t R,
                              int64_t C, hipStream_t stream);
 
+// dst [Rd, Cd] (Rd >= R, Cd >= C) = the [R, C] matrix src of 2- or 4-byte
+// elements in its top-left corner, zeros elsewhere.
+hipError_t launch_pad_copy(const void *src, int64_t R, int64_t C, void *dst, int64_t Rd,
+                           int64_t Cd, int elem_bytes, hipStream_t stream);
+
 // Transpose an [R, C] matrix of 1-, 2- or 4-byte elements into [C, R].
 hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
                             int elem_bytes, hipStream_t stream);

@@ -274,6 +274,96 @@ int convrot_linear_prepare_weights(const void *W, int w_dtype, int layout,
     return rc;
 }
 
+// The rank a low-rank pair is stored with: r rounded up to a multiple of 128
+// (a multiple of 64, as the checkpoint loader pads ranks, and the
+// contraction's K granularity), or of 256 for b = 256 so that whole blocks
+// tile the rank.
+static int64_t lowrank_rank(int64_t r, int block)
+{
+    const int64_t m = block == 256 ? 256 : 128;
+    return (r + m - 1) / m * m;
+}
+
+static bool lowrank_prep_args(int64_t r, int64_t K, int64_t N, int block, int w_dtype)
+{
+    // r is bounded before it is rounded up, so the rounding cannot overflow
+    if (r <= 0 || r > kMaxK || !valid_block(block) ||
+        (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16))
+        return false;
+    const int64_t rp = lowrank_rank(r, block);
+    return check_linear_shape(rp, K, block) == CONVROT_OK &&
+           check_linear_shape(N, rp, block) == CONVROT_OK;
+}
+
+int64_t lowrank_convrot_padded_rank(int64_t r, int block)
+{
+    if (r <= 0 || r > kMaxK || !valid_block(block)) return 0;
+    return lowrank_rank(r, block);
+}
+
+size_t lowrank_convrot_prepare_workspace_bytes(int64_t r, int64_t K, int64_t N,
+                                                          int block, int w_dtype)
+{
+    if (!lowrank_prep_args(r, K, N, block, w_dtype)) return 0;
+    const int64_t rp = lowrank_rank(r, block);
+    if (rp == r) return 0;
+    const size_t es = w_dtype == CONVROT_F32 ? 4u : 2u;
+    return round_up((size_t)rp * (size_t)K * es, kAlign) + round_up((size_t)N * (size_t)rp * es, kAlign);
+}
+
+static int lowrank_prepare_impl(const void *A, const void *B, int w_dtype, int64_t r, int64_t K,
+                                int64_t N, int block, convrot_weights *outA,
+                                convrot_weights *outB, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!A || !B || !outA || !outB || !outA->codes || !outA->scale || !outB->codes ||
+        !outB->scale)
+        return CONVROT_EINVAL;
+    if (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
+    if (r <= 0 || K <= 0 || N <= 0 || !valid_block(block) || K % block != 0) return CONVROT_EINVAL;
+    if (outA->flags != outB->flags || !valid_rotation((uint32_t)outA->flags, block))
+        return CONVROT_EINVAL;
+    if (!lowrank_prep_args(r, K, N, block, w_dtype)) return CONVROT_EUNSUPPORTED;
+    if (!aligned16(A) || !aligned16(B) || (ws && !aligned16(ws))) return CONVROT_EALIGN;
+    const int64_t rp = lowrank_rank(r, block);
+    const size_t need = lowrank_convrot_prepare_workspace_bytes(r, K, N, block, w_dtype);
+    if (need > 0 && (!ws || ws_bytes < need)) return CONVROT_EWORKSPACE;
+    const int es = w_dtype == CONVROT_F32 ? 4 : 2;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const void *Ap = A, *Bp = B;
+    if (rp != r) {
+        // A gains zero rows r .. rp-1, B zero columns r .. rp-1: B' A' = B A,
+        // and the zero blocks of A' and the zero columns of B' rotate to zero
+        Carve c(ws);
+        void *a = c.take((size_t)rp * (size_t)K * es);
+        void *b = c.take((size_t)N * (size_t)rp * es);
+        hipError_t e = convrot::launch_pad_copy(A, r, K, a, rp, K, es, s);
+        if (e == hipSuccess) e = convrot::launch_pad_copy(B, N, r, b, N, rp, es, s);
+        const int rc = hip_status(e);
+        if (rc != CONVROT_OK) return rc;
+        Ap = a;
+        Bp = b;
+    }
+    // the float copies are consumed in stream order, so the workspace may be
+    // reused once the stream has passed this call
+    int rc = prepare_weights_impl(Ap, w_dtype, CONVROT_OUT_MAJOR, nullptr, rp, K, block, outA,
+                                  nullptr, 0, stream);
+    if (rc == CONVROT_OK)
+        rc = prepare_weights_impl(Bp, w_dtype, CONVROT_OUT_MAJOR, nullptr, N, rp, block, outB,
+                                  nullptr, 0, stream);
+    return rc;
+}
+
+int lowrank_convrot_prepare_weights(const void *A, const void *B, int w_dtype,
+                                               int64_t r, int64_t K, int64_t N, int block,
+                                               convrot_weights *outA, convrot_weights *outB,
+                                               void *ws, size_t ws_bytes, void *stream)
+{
+    const int rc = lowrank_prepare_impl(A, B, w_dtype, r, K, N, block, outA, outB, ws, ws_bytes,
+                                        stream);
+    log_call("lowrank_convrot_prepare_weights", r, N, K, rc);
+    return rc;
+}
+
 static int linear_forward_impl(const void *X, int64_t M, const convrot_weights *W,
                            const float *bias, void *Y, int y_dtype, void *ws, size_t ws_bytes,
                            void *stream)

@@ -821,6 +821,22 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ sr
     }
 }
 
+// --------------------------------------------------------- padded copy ----
+
+// dst [Rd, Cd] = src [R, C] in its top-left corner, zeros elsewhere
+// (grid-stride over the destination).
+template <typename T>
+__global__ __launch_bounds__(256) void pad_copy_kernel(const T *__restrict__ src, int64_t R,
+                                                       int64_t C, T *__restrict__ dst,
+                                                       int64_t Rd, int64_t Cd)
+{
+    const int64_t n = Rd * Cd, stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const int64_t r = i / Cd, c = i % Cd;
+        dst[i] = (r < R && c < C) ? src[r * C + c] : T(0);
+    }
+}
+
 } // namespace
 
 hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
@@ -887,6 +903,27 @@ hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
     case 4:
         hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, stream,
                            (const float *)src, (float *)dst, R, C);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_copy(const void *src, int64_t R, int64_t C, void *dst, int64_t Rd,
+                           int64_t Cd, int elem_bytes, hipStream_t stream)
+{
+    const int64_t n = Rd * Cd;
+    if (n == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 8 * device_cu_count());
+    switch (elem_bytes) {
+    case 2:
+        hipLaunchKernelGGL(pad_copy_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                           (const uint16_t *)src, R, C, (uint16_t *)dst, Rd, Cd);
+        break;
+    case 4:
+        hipLaunchKernelGGL(pad_copy_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
+                           (const uint32_t *)src, R, C, (uint32_t *)dst, Rd, Cd);
         break;
     default:
         return hipErrorInvalidValue;
