@@ -280,6 +280,24 @@ CONVROT_API int convrot_linear_forward(const void *X, int64_t M, const convrot_w
                            const float *bias, void *Y, int y_dtype, void *ws,
                            size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): convrot_linear_forward
+ * without a workspace argument.  The rotated activations' K-tiled codes and
+ * row scales go to a static device array of the library of
+ * CONVROT_NOALLOC_SCRATCH_BYTES (32 MiB, one copy per device, held until the
+ * process ends) instead of a caller workspace; the call allocates nothing.
+ * Shapes whose convrot_linear_workspace_bytes(M, K, N, b) exceed that size
+ * return CONVROT_EWORKSPACE (use convrot_linear_forward); M = 4096 at
+ * K = 5376 fits.  Every call on a device shares that device's array, so calls
+ * on one device that overlap in time (concurrent streams) race and must be
+ * ordered by the caller.  Nothing in the array needs to start at zero: each
+ * call writes every code and scale it reads.  Otherwise the arguments, the
+ * results (bit for bit) and the errors are those of convrot_linear_forward. */
+#define CONVROT_NOALLOC_SCRATCH_BYTES (32u << 20)
+CONVROT_API int convrot_linear_forward_noalloc(const void *X, int64_t M,
+                                               const convrot_weights *W, const float *bias,
+                                               void *Y, int y_dtype, void *stream);
+
 /* Low-rank ConvRot linear (HyperFlow H3 Flash card, "Choose a Weight Format":
  * the INT8 package holds W8A8 linears and low-rank factorised ones; both
  * factors are W8A8 here): h = bf16(linear(X; A)) with A [r, K] and no bias,

@@ -62,6 +62,8 @@ _SIGNATURES = {
         _c_int, [_c_p, _c_int, _c_int, _c_p, _c_i64, _c_i64, _c_int, _W, _c_p, _c_sz, _c_p]),
     "convrot_linear_forward": (
         _c_int, [_c_p, _c_i64, _W, _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "convrot_linear_forward_noalloc": (
+        _c_int, [_c_p, _c_i64, _W, _c_p, _c_p, _c_int, _c_p]),
     "lowrank_convrot_forward": (
         _c_int, [_c_p, _c_i64, _W, _W, _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
     "convrot_mlp_forward": (
@@ -373,6 +375,26 @@ def convrot_linear_forward(X: torch.Tensor, W: PreparedWeights, bias=None,
                                     _dtype_tag(out.dtype), _ptr(ws),
                                     ws.numel() if ws is not None else 0, _stream(stream))
     _check("convrot_linear_forward", rc)
+    return out
+
+
+def convrot_linear_forward_noalloc(X: torch.Tensor, W: PreparedWeights, bias=None,
+                                   out_dtype: torch.dtype = torch.bfloat16, out=None,
+                                   stream=None) -> torch.Tensor:
+    """convrot_linear_forward with the library's static device scratch as its
+    workspace (the C call allocates nothing; pass `out` to allocate nothing
+    here either).  Calls on one device must not overlap in time."""
+    lib = library()
+    dev = _weights(W, "W")
+    M = _rows(X, "X", W.K)
+    _opt(bias, "bias", torch.float32, (W.N,))
+    _output(out, M, W.N, (torch.bfloat16, torch.float32))
+    _on_device(dev, X=X, bias=bias, out=out)
+    if out is None:
+        out = torch.empty((M, W.N), dtype=out_dtype, device=dev)
+    rc = lib.convrot_linear_forward_noalloc(_ptr(X), M, W.ref(), _ptr(bias), _ptr(out),
+                                            _dtype_tag(out.dtype), _stream(stream))
+    _check("convrot_linear_forward_noalloc", rc)
     return out
 
 

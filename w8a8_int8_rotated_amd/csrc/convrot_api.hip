@@ -403,6 +403,51 @@ int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
     return rc;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free linear forward: the workspace of convrot_linear_forward
+// (the rotated activations' K-tiled codes and row scales) lives in a
+// file-scope device array, one copy per device, held until the process ends.
+// The array's name is a host-side stand-in in host code: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is passed to the kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) int8_t scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
+static int scratch_ptr(void **out)
+{
+    static std::atomic<void *> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= 64) return CONVROT_EUNSUPPORTED;
+    void *p = cached[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p || !aligned16(p)) return hip_status(hipErrorInvalidSymbol);
+        cached[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return CONVROT_OK;
+}
+
+int convrot_linear_forward_noalloc(const void *X, int64_t M, const convrot_weights *W,
+                                   const float *bias, void *Y, int y_dtype, void *stream)
+{
+    int rc = check_weights(W);
+    if (rc == CONVROT_OK) rc = check_rows(M, W->K);
+    if (rc == CONVROT_OK &&
+        convrot_linear_workspace_bytes(M, W->K, W->N, W->block) > CONVROT_NOALLOC_SCRATCH_BYTES)
+        rc = CONVROT_EWORKSPACE;   // beyond the static scratch: the caller must use a workspace
+    void *ws = nullptr;
+    if (rc == CONVROT_OK && M > 0) rc = scratch_ptr(&ws);
+    if (rc == CONVROT_OK)
+        rc = linear_forward_impl(X, M, W, bias, Y, y_dtype, ws, CONVROT_NOALLOC_SCRATCH_BYTES,
+                                 stream);
+    log_call("convrot_linear_forward_noalloc", M, W ? W->N : 0, W ? W->K : 0, rc);
+    return rc;
+}
+
 static int lowrank_forward_impl(const void *X, int64_t M, const convrot_weights *A,
                             const convrot_weights *B, const float *bias, void *Y, int y_dtype,
                             void *ws, size_t ws_bytes, void *stream)
