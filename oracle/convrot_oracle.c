@@ -48,6 +48,14 @@
  *     convrot in ComfyUI": there the low-rank linears stay bf16): each
  *     product is the exact sum over K rounded once to fp32, the bias added in
  *     fp32, then bf16 by round to nearest even; no rotation, no quantisation.
+ * R10 SwiGLU MLP (MiniMax-H3-Rung-Omega README, "Technical Architecture
+ *     Overview", Floor 1: SwiGLU, ConvRot64 and the rowwise INT8 quantise
+ *     fused in front of MLP.fc2).  fc1 is one linear with 2F outputs whose
+ *     bf16 result holds the gate in columns [0, F) and the up projection in
+ *     [F, 2F); g = bf16(s * u) with s = fp32(silu(gate)), silu(z) =
+ *     z / (1 + exp(-z)) evaluated in fp64 on the bf16 gate and rounded once
+ *     to fp32, s * u one fp32 multiply; fc2 rotates g with its own block
+ *     (64 for ConvRot64) and quantises it per token.
  *
  * Precision: every step that decides an INT8 code is evaluated in fp32 (the
  * precision the GPU kernels take those decisions in), with the butterfly order
@@ -520,4 +528,66 @@ int oracle_lowrank_bf16_forward(const uint16_t *X, int64_t M, int64_t K, const u
         memcpy(h_out, h, sizeof(uint16_t) * (size_t)M * (size_t)r);
     free(h);
     return OR_OK;
+}
+
+
+/* ------------------------------------------------------------------ */
+/* R10: SwiGLU MLP                                                     */
+/* ------------------------------------------------------------------ */
+
+/* silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), evaluated in fp64. */
+double oracle_silu_f64(double z) { return z / (1.0 + exp(-z)); }
+
+/* The fp32 activation of one bf16 gate value: the fp64 evaluation rounded
+ * once to fp32. */
+float oracle_silu_f32(uint16_t a) { return (float)oracle_silu_f64((double)oracle_bf16_to_f32(a)); }
+
+/* g [M, F] from the fc1 output gu [M, 2F] (gate = columns [0, F), up =
+ * columns [F, 2F)): g = bf16(silu_f32(gate) * up), one fp32 product. */
+void oracle_swiglu_bf16(const uint16_t *gu, int64_t M, int64_t F, uint16_t *g)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t j = 0; j < F; ++j) {
+            float sg = oracle_silu_f32(gu[m * 2 * F + j]);
+            float up = oracle_bf16_to_f32(gu[m * 2 * F + F + j]);
+            float p = sg * up;
+            g[m * F + j] = oracle_f32_to_bf16(p);
+        }
+    }
+}
+
+/* gu = bf16(linear(X; W_gu, bias_gu)) with W_gu [2F, K] rotated with block
+ * b_up, g = swiglu(gu), y = linear(g; W_down, bias_down) with W_down [N, F]
+ * rotated with block b_down.  gu_out / g_out, when not NULL, receive the
+ * intermediates. */
+int oracle_swiglu_mlp_forward_rot(const uint16_t *X, int64_t M, int64_t K, int b_up,
+                                  int b_down, int rot, const int8_t *qgu, const float *sgu,
+                                  int64_t F, const float *bias_gu, const int8_t *qd,
+                                  const float *sd, int64_t N, const float *bias_down,
+                                  int out_dtype, void *out, uint16_t *gu_out, uint16_t *g_out)
+{
+    if (F <= 0 || F % b_down != 0)
+        return OR_EINVAL;
+    if (M == 0)
+        return OR_OK;
+    size_t n = (size_t)M * (size_t)F;
+    uint16_t *gu = (uint16_t *)malloc(sizeof(uint16_t) * 2 * n);
+    uint16_t *g = (uint16_t *)malloc(sizeof(uint16_t) * n);
+    int rc = OR_EINVAL;
+    if (gu && g) {
+        rc = oracle_linear_forward_rot(X, M, K, b_up, rot, qgu, sgu, 2 * F, bias_gu, OR_BF16, gu);
+        if (rc == OR_OK) {
+            oracle_swiglu_bf16(gu, M, F, g);
+            rc = oracle_linear_forward_rot(g, M, F, b_down, rot, qd, sd, N, bias_down,
+                                           out_dtype, out);
+        }
+        if (rc == OR_OK && gu_out)
+            memcpy(gu_out, gu, sizeof(uint16_t) * 2 * n);
+        if (rc == OR_OK && g_out)
+            memcpy(g_out, g, sizeof(uint16_t) * n);
+    }
+    free(gu);
+    free(g);
+    return rc;
 }

@@ -79,6 +79,12 @@ def open_library(path):
                      _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p]),
         "oracle_lowrank_bf16_forward": (
             _c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p]),
+        "oracle_silu_f64": (ctypes.c_double, [ctypes.c_double]),
+        "oracle_silu_f32": (ctypes.c_float, [ctypes.c_uint16]),
+        "oracle_swiglu_bf16": (None, [_c_p, _c_i64, _c_i64, _c_p]),
+        "oracle_swiglu_mlp_forward_rot": (
+            _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
+                     _c_p, _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_p]),
         "oracle_mlp_forward_rot": (
             _c_int, [_c_p, _c_i64, _c_i64, _c_int, _c_int, _c_p, _c_p, _c_i64, _c_p,
                      _c_p, _c_p, _c_i64, _c_p, _c_int, _c_p, _c_p, _c_p]),
@@ -342,6 +348,62 @@ def mlp_forward(X_bf16, qu, su, qd, sd, b: int, bias_up=None, bias_down=None,
     return (y, u, g) if return_intermediates else y
 
 
+def silu_f64(z: float) -> float:
+    """R10: silu(z) = z / (1 + exp(-z)) in fp64."""
+    return _load().oracle_silu_f64(float(z))
+
+
+def silu_f32(a_bf16) -> np.ndarray:
+    """R10: fp32(silu) of bf16 gate values (raw uint16 bits), element by element."""
+    lib = _load()
+    a = np.asarray(a_bf16, dtype=np.uint16)
+    flat = a.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.float32)
+    f = lib.oracle_silu_f32
+    for i in range(flat.size):
+        out[i] = f(int(flat[i]))
+    return out.reshape(a.shape)
+
+
+def swiglu_bf16(gu_bf16) -> np.ndarray:
+    """R10: g = bf16(silu_f32(gate) * up) for the fc1 output gu [M, 2F]
+    (gate = first F columns, up = last F)."""
+    lib = _load()
+    gu = _c(gu_bf16, np.uint16)
+    M, F2 = gu.shape
+    assert F2 % 2 == 0
+    g = np.empty((M, F2 // 2), dtype=np.uint16)
+    lib.oracle_swiglu_bf16(_ptr(gu), M, F2 // 2, _ptr(g))
+    return g
+
+
+def swiglu_mlp_forward(X_bf16, qgu, sgu, qd, sd, b_up: int, b_down: int, bias_gu=None,
+                       bias_down=None, out: str = "bf16", return_intermediates: bool = False,
+                       rot: str = "sylvester"):
+    """R10: gu = bf16(linear(X; W_gu)) [M, 2F]; g = swiglu(gu); y = linear(g; W_down)."""
+    lib = _load()
+    X = _c(X_bf16, np.uint16)
+    qgu, sgu = _c(qgu, np.int8), _c(sgu, np.float32)
+    qd, sd = _c(qd, np.int8), _c(sd, np.float32)
+    bu = None if bias_gu is None else _c(bias_gu, np.float32)
+    bd = None if bias_down is None else _c(bias_down, np.float32)
+    M, K = X.shape
+    F2 = qgu.shape[0]
+    assert F2 % 2 == 0
+    F = F2 // 2
+    N = qd.shape[0]
+    assert qd.shape[1] == F
+    y = np.empty((M, N), dtype=np.float32 if out == "f32" else np.uint16)
+    gu = np.empty((M, F2), dtype=np.uint16)
+    g = np.empty((M, F), dtype=np.uint16)
+    _check(lib.oracle_swiglu_mlp_forward_rot(_ptr(X), M, K, int(b_up), int(b_down), _rot(rot),
+                                             _ptr(qgu), _ptr(sgu), F, _ptr(bu), _ptr(qd),
+                                             _ptr(sd), N, _ptr(bd),
+                                             F32 if out == "f32" else BF16, _ptr(y), _ptr(gu),
+                                             _ptr(g)), "swiglu_mlp_forward")
+    return (y, gu, g) if return_intermediates else y
+
+
 def lowrank_bf16_forward(X_bf16, A_bf16, B_bf16, bias=None, return_h: bool = False):
     """R9, the bf16 low-rank comparison variant: h = bf16(X . A^T),
     y = bf16(h . B^T + bias), each sum exact then rounded to fp32."""
@@ -364,5 +426,5 @@ __all__ = [
     "num_threads", "bf16_to_f32", "f32_to_bf16", "inv_sqrt_b", "fwht", "rowquant",
     "rotate_quantize", "prepare_weights", "gemm_i32", "dequant",
     "linear_forward", "lowrank_forward", "gelu_f64", "gelu_bf16", "mlp_forward",
-    "lowrank_bf16_forward",
+    "lowrank_bf16_forward", "silu_f64", "silu_f32", "swiglu_bf16", "swiglu_mlp_forward",
 ]

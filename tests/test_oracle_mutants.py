@@ -55,8 +55,20 @@ MUTANTS = [
      ["test_lowrank_is_two_chained_linears_with_bias"]),
     ("mlp_dropped_bias_up", "qu, su, F, bias_up, OR_BF16, u);", "qu, su, F, NULL, OR_BF16, u);",
      ["test_mlp_is_two_biased_linears_around_gelu"]),
-    ("mlp_dropped_bias_down", "qd, sd, N, bias_down,", "qd, sd, N, NULL,",
+    ("mlp_dropped_bias_down", "qd, sd, N, bias_down,\n                                           out_dtype, out);\n        }\n        if (rc == OR_OK && u_out)",
+     "qd, sd, N, NULL,\n                                           out_dtype, out);\n        }\n        if (rc == OR_OK && u_out)",
      ["test_mlp_is_two_biased_linears_around_gelu"]),
+    ("silu_sign", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));",
+     ["test_silu_values", "test_silu_f32_every_bf16_pattern"]),
+    ("swiglu_gate_up_swapped", "float sg = oracle_silu_f32(gu[m * 2 * F + j]);",
+     "float sg = oracle_silu_f32(gu[m * 2 * F + F + j]);",
+     ["test_swiglu_bf16_composition"]),
+    ("swiglu_dropped_bias_gu", "qgu, sgu, 2 * F, bias_gu, OR_BF16, gu);",
+     "qgu, sgu, 2 * F, NULL, OR_BF16, gu);",
+     ["test_swiglu_mlp_is_linear_swiglu_linear"]),
+    ("swiglu_down_block", "rc = oracle_linear_forward_rot(g, M, F, b_down, rot,",
+     "rc = oracle_linear_forward_rot(g, M, F, b_up, rot,",
+     ["test_swiglu_mlp_is_linear_swiglu_linear"]),
 ]
 
 CALL = {
@@ -79,6 +91,11 @@ CALL = {
         lambda: pins.test_lowrank_is_two_chained_linears_with_bias(),
     "test_mlp_is_two_biased_linears_around_gelu":
         lambda: pins.test_mlp_is_two_biased_linears_around_gelu(),
+    "test_silu_values": lambda: pins.test_silu_values(),
+    "test_silu_f32_every_bf16_pattern": lambda: pins.test_silu_f32_every_bf16_pattern(),
+    "test_swiglu_bf16_composition": lambda: pins.test_swiglu_bf16_composition(),
+    "test_swiglu_mlp_is_linear_swiglu_linear":
+        lambda: pins.test_swiglu_mlp_is_linear_swiglu_linear(),
 }
 
 

@@ -577,3 +577,83 @@ def test_mlp_is_two_biased_linears_around_gelu():
     y_ref = oracle.linear_forward(g, qd, sd, b, bias=bd, out="f32")
     assert np.array_equal(y, y_ref)
     assert not np.array_equal(y, oracle.linear_forward(g, qd, sd, b, out="f32"))
+
+
+# ---------------------------------------------------------------- SwiGLU ----
+
+def test_silu_values():
+    """R10's activation against scipy's logistic function: silu(z) =
+    z * expit(z) within two fp64 ulps, silu(0) = 0 with the sign of zero,
+    and the odd-part identity silu(z) - silu(-z) = z."""
+    import scipy.special
+    zs = [-200.0, -40.0, -3.0, -1.0, -0.25, -1e-9, 1e-9, 0.5, 1.0, 2.0, 7.0, 40.0, 200.0]
+    for z in zs:
+        ref = z * scipy.special.expit(z)
+        assert abs(oracle.silu_f64(z) - ref) <= 2 * np.spacing(abs(ref)) + 1e-300, z
+        assert abs((oracle.silu_f64(z) - oracle.silu_f64(-z)) - z) <= 4e-16 * max(1.0, abs(z))
+    assert oracle.silu_f64(0.0) == 0.0 and math.copysign(1.0, oracle.silu_f64(-0.0)) == -1.0
+    assert abs(oracle.silu_f64(1.0) - 0.7310585786300049) < 1e-16
+
+
+def test_silu_f32_every_bf16_pattern():
+    """The fp32 activation of every finite bf16 gate equals fp32(z *
+    expit(z)) from scipy, and the closed forms that bound it: z/2 for
+    |z| < 2^-24, z for z >= 32, -0 for z <= -128."""
+    import scipy.special
+    a = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = oracle.silu_f32(a)
+    z = wl.bf16_bits_to_f32(a)
+    fin = np.isfinite(z)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = (z.astype(np.float64) * scipy.special.expit(z.astype(np.float64))).astype(np.float32)
+    assert np.array_equal(s[fin].view(np.uint32), ref[fin].view(np.uint32))
+    tiny = fin & (np.abs(z) < 2.0 ** -24)
+    assert np.array_equal(s[tiny].view(np.uint32), (z[tiny] * np.float32(0.5)).view(np.uint32))
+    big = fin & (z >= 32)
+    assert np.array_equal(s[big], z[big])
+    neg = fin & (z <= -128)
+    assert np.all(s[neg].view(np.uint32) == 0x80000000)
+
+
+def test_swiglu_bf16_composition():
+    """g = bf16(fp32(silu(gate)) * up) with the gate in the first half of the
+    fc1 output and the up projection in the second, against scipy's logistic,
+    numpy's fp32 product and the input recipe's RNE narrowing."""
+    import scipy.special
+    rng = np.random.default_rng(51)
+    M, F = 7, 96
+    gu = wl.f32_to_bf16_bits((rng.standard_normal((M, 2 * F)) * 3).astype(np.float32))
+    gate = wl.bf16_bits_to_f32(gu[:, :F]).astype(np.float64)
+    up = wl.bf16_bits_to_f32(gu[:, F:])
+    s32 = (gate * scipy.special.expit(gate)).astype(np.float32)
+    ref = wl.f32_to_bf16_bits(s32 * up)
+    g = oracle.swiglu_bf16(gu)
+    assert np.array_equal(g, ref)
+    # up = 1 passes the activation through (rounded to bf16)
+    gu1 = gu.copy()
+    gu1[:, F:] = 0x3F80
+    assert np.array_equal(oracle.swiglu_bf16(gu1), wl.f32_to_bf16_bits(s32))
+
+
+def test_swiglu_mlp_is_linear_swiglu_linear():
+    """R10 as a composition: gu = bf16(linear(X; W_gu) + bias_gu) with the
+    fc1 block, g = swiglu(gu), y = linear(g; W_down) + bias_down with the fc2
+    block (64, ConvRot64), bit for bit."""
+    w = wl.scaled("swiglu_16384", M=9, K=256, N=128, ffn=256)
+    x = w.activations()
+    qgu, sgu = oracle.prepare_weights(w.weight("w"), w.block)
+    qd, sd = oracle.prepare_weights(w.weight("w2"), w.down_block)
+    rng = np.random.default_rng(53)
+    bu = rng.normal(0, 0.5, 2 * w.ffn).astype(np.float32)
+    bd = rng.normal(0, 0.5, w.N).astype(np.float32)
+    y, gu, g = oracle.swiglu_mlp_forward(x, qgu, sgu, qd, sd, w.block, w.down_block,
+                                         bias_gu=bu, bias_down=bd, out="f32",
+                                         return_intermediates=True)
+    gu_ref = oracle.linear_forward(x, qgu, sgu, w.block, bias=bu, out="bf16")
+    assert np.array_equal(gu, gu_ref)
+    assert np.array_equal(g, oracle.swiglu_bf16(gu_ref))
+    y_ref = oracle.linear_forward(g, qd, sd, w.down_block, bias=bd, out="f32")
+    assert np.array_equal(y, y_ref)
+    # the second projection's own block matters: with b = 128 the codes differ
+    qd2, sd2 = oracle.prepare_weights(w.weight("w2"), 128)
+    assert not np.array_equal(y, oracle.linear_forward(g, qd2, sd2, 128, bias=bd, out="f32"))

@@ -46,7 +46,7 @@ def _rngs(seed: int):
 @dataclasses.dataclass
 class Workload:
     name: str
-    kind: str                 # "linear" | "lowrank" | "mlp"
+    kind: str                 # "linear" | "lowrank" | "mlp" | "swiglu"
     M: int
     K: int
     N: int
@@ -60,6 +60,7 @@ class Workload:
     bias_std: float | None = None
     rank: int = 0             # low-rank r
     ffn: int = 0              # MLP hidden width
+    block2: int = 0           # block of the second projection (0: same as block)
     seed: int = 0
     description: str = ""
 
@@ -112,7 +113,14 @@ class Workload:
             return (self.rank, self.K) if which == "w" else (self.N, self.rank)
         if self.kind == "mlp":
             return (self.ffn, self.K) if which == "w" else (self.N, self.ffn)
+        if self.kind == "swiglu":
+            # fc1 holds the gate (first ffn outputs) and the up projection
+            return (2 * self.ffn, self.K) if which == "w" else (self.N, self.ffn)
         raise ValueError(self.kind)
+
+    @property
+    def down_block(self) -> int:
+        return self.block2 or self.block
 
     def bias(self, which: str = "bias", n: int | None = None) -> np.ndarray | None:
         if self.bias_std is None:
@@ -129,6 +137,8 @@ class Workload:
             return 2 * self.M * self.rank * (self.K + self.N)
         if self.kind == "mlp":
             return 2 * self.M * self.ffn * (self.K + self.N)
+        if self.kind == "swiglu":
+            return 2 * self.M * self.ffn * (2 * self.K + self.N)
         raise ValueError(self.kind)
 
 
@@ -151,6 +161,11 @@ WORKLOADS = {
         "mlp_16384", "mlp", M=16384, K=5376, N=5376, ffn=21504, block=128,
         out="bf16", x_dist="normal", w_std=0.02,
         description="MLP pair up M=16384 K=5376 N=21504, GELU, down K=21504 N=5376"),
+    "swiglu_16384": Workload(
+        "swiglu_16384", "swiglu", M=16384, K=5376, N=5376, ffn=21504, block=128, block2=64,
+        out="bf16", x_dist="normal", w_std=0.02,
+        description="SwiGLU MLP: fc1 M=16384 K=5376 N=2x21504 (gate | up) b=128, "
+                    "g = silu(gate) * up, fc2 K=21504 N=5376 with ConvRot64 (b=64)"),
     "qk_38656": Workload(
         "qk_38656", "linear", M=38656, K=128, N=38656, block=128, out="bf16",
         x_dist="normal", w_std=0.02,
