@@ -264,6 +264,43 @@ def setup(w, cr, torch, np, dev):
                   *gemm_cost(M, N, F, ob)),
         ]
         ops = 2.0 * M * F * (K + N)
+    elif w.kind == "swiglu":
+        Wgu, Wd = w.weight("w"), w.weight("w2")
+        host.update(Wgu=Wgu, Wd=Wd)
+        bd = w.down_block
+        pgu = cr.convrot_swiglu_prepare(torch.from_numpy(Wgu).to(dev), b)
+        pd = cr.convrot_linear_prepare_weights(torch.from_numpy(Wd).to(dev), bd)
+        torch.cuda.synchronize()
+        F, N = w.ffn, w.N
+        Y = torch.empty((M, N), dtype=out_dt, device=dev)
+        ws = torch.empty(cr.convrot_swiglu_mlp_workspace_bytes(M, K, F, N, b, bd),
+                         dtype=torch.uint8, device=dev)
+        qx = torch.empty((cr.padded_rows(M), K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        G = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        qg = torch.empty((cr.padded_rows(M), F), dtype=torch.int8, device=dev)
+        sg = torch.empty(M, dtype=torch.float32, device=dev)
+
+        def step():
+            cr.convrot_swiglu_mlp_forward(X, pgu, pd, out=Y, workspace=ws)
+
+        fc1_ops, fc1_bytes = gemm_cost(M, 2 * F, K)
+        fc1_bytes -= 2.0 * M * F          # writes g [M, F], not the [M, 2F] fc1 output
+        stages = [
+            Stage("rotquant X", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(X, b, q=qx, s=sx, stream=stream),
+                  0.0, rq_bytes(M, K), src=X),
+            Stage("gemm_i8 fc1 gate|up + SwiGLU epilogue (K -> 2F, writes g)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qx, sx, pgu, out=G, swiglu=True, stream=stream),
+                  fc1_ops, fc1_bytes),
+            Stage(f"rotquant g (b={bd})", "rotquant",
+                  lambda: cr.convrot_rotate_quantize(G, bd, q=qg, s=sg, stream=stream),
+                  0.0, rq_bytes(M, F)),
+            Stage("gemm_i8 down (F -> N)", "gemm_i8",
+                  lambda: cr.convrot_gemm_dequant(qg, sg, pd, out=Y, stream=stream),
+                  *gemm_cost(M, N, F, ob)),
+        ]
+        ops = 2.0 * M * F * (2 * K + N)
     else:
         raise SystemExit(f"unknown workload kind {w.kind}")
     return step, stages, ops, Y, host
@@ -385,8 +422,10 @@ def main():
            "out": w.out, "bias": w.bias_std is not None, "seed": w.seed}
     if w.kind == "lowrank":
         cfg["rank"] = w.rank
-    if w.kind == "mlp":
+    if w.kind in ("mlp", "swiglu"):
         cfg["ffn"] = w.ffn
+    if w.kind == "swiglu":
+        cfg["block_down"] = w.down_block
     if w.n_outliers():
         cfg["outlier_channels"] = w.n_outliers()
         cfg["outlier_gain"] = w.outlier_gain
@@ -578,6 +617,12 @@ def cpu_baseline(args, w, host, Y):
         qb, sb = oracle.prepare_weights(host["B"], b)
         run = lambda rows: oracle.lowrank_forward(x[rows], qa, sa, qb, sb, b, out=w.out)
         ops_row = 2.0 * w.rank * (w.K + w.N)
+    elif w.kind == "swiglu":
+        qgu, sgu = oracle.prepare_weights(host["Wgu"], b)
+        qd, sd = oracle.prepare_weights(host["Wd"], w.down_block)
+        run = lambda rows: oracle.swiglu_mlp_forward(x[rows], qgu, sgu, qd, sd, b, w.down_block,
+                                                     out=w.out)
+        ops_row = 2.0 * w.ffn * (2 * w.K + w.N)
     else:
         qu, su = oracle.prepare_weights(host["Wu"], b)
         qd, sd = oracle.prepare_weights(host["Wd"], b)
@@ -618,7 +663,8 @@ def cpu_baseline(args, w, host, Y):
         "kind": "oracle",
         "sample": f"{len(rows)} of {M} rows (seeded), every projection over its full width "
                   f"and depth: rotate+quantise of those rows, INT32 contraction and epilogue"
-                  f"{', GELU' if w.kind == 'mlp' else ''}; weight preparation excluded",
+                  f"{', GELU' if w.kind == 'mlp' else ', SwiGLU' if w.kind == 'swiglu' else ''}"
+                  f"; weight preparation excluded",
         "seconds": round(dt, 2),
     }
     parity = {"rows": int(len(rows)), "normwise_err": err, "mismatches": mism,

@@ -126,6 +126,13 @@ typedef enum convrot_layout {
  * index, lowest first; a group (v0..v3) becomes S - 2 v_j with
  * S = (v0 + v1) + (v2 + v3) in fp32.  The scale folds 1/sqrt(b) either way. */
 #define CONVROT_ROT_REGULAR 0x100u
+/* Set by convrot_swiglu_prepare_weights (never by the caller): the 2F rows are
+ * a SwiGLU fc1's gate and up channels, stored interleaved in 32-row blocks
+ * (packed row p holds source row (p/32)*16 + p%32 for p%32 < 16, else
+ * F + (p/32)*16 + p%32 - 16).  Only convrot_swiglu_mlp_forward, the
+ * CONVROT_FLAG_SWIGLU hook and convrot_gemm_i32 accept such a weight; other
+ * entry points return CONVROT_ELAYOUT. */
+#define CONVROT_SWIGLU_PAIRS 0x200u
 #define CONVROT_WEIGHTS_VERSION 2u
 
 /* Prepared (pre-rotated, quantised, packed) weights of one linear layer.
@@ -328,6 +335,71 @@ CONVROT_API int convrot_mlp_forward(const void *X, int64_t M, const convrot_weig
                         size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
+/* SwiGLU MLP                                                          */
+/* ------------------------------------------------------------------ */
+
+/* The SwiGLU MLP of MiniMax-H3-Rung-Omega README, "Technical Architecture
+ * Overview", Floor 1 (SwiGLU, ConvRot64 and the rowwise INT8 quantise fused
+ * in front of MLP.fc2).  fc1 is one ConvRot linear with 2F outputs, the gate
+ * channels [0, F) and the up channels [F, 2F); the activation is
+ *   g = bf16(s * u),  s = fp32(silu(gate)),  silu(z) = z / (1 + exp(-z))
+ * evaluated in fp64 on the bf16 gate and rounded once to fp32, s * u one fp32
+ * multiply on the bf16 up value u, g rounded to nearest even; fc2 is a ConvRot
+ * linear on g with its own block (64 for ConvRot64).  fc1's epilogue forms g,
+ * so the [M, 2F] fc1 output is never written; g [M, F] is, and fc2's
+ * rotate+quantise reads it. */
+
+/* Workspace for convrot_swiglu_prepare_weights: the interleaved copy of the
+ * [2F, K] weight (and of its scales when importing codes). */
+CONVROT_API size_t convrot_swiglu_prepare_workspace_bytes(int64_t F, int64_t K, int block,
+                                                          int w_dtype);
+
+/* Prepare a SwiGLU fc1 weight W [2F, K], output-major, gate rows first:
+ * F32/BF16 float weights (rotated and quantised per output channel as by
+ * convrot_linear_prepare_weights), or I8 codes with src_scale [2F] (import).
+ * The rows are stored interleaved (CONVROT_SWIGLU_PAIRS, set in out->flags
+ * beside the rotation kind, which out->flags selects on entry as for
+ * convrot_linear_prepare_weights).  out->codes / out->scale: caller
+ * allocations of convrot_weights_packed_bytes(2F, K, b) and 8F bytes.
+ * F % 16 == 0; ws of convrot_swiglu_prepare_workspace_bytes(F, K, b, w_dtype)
+ * bytes (required).  Errors as for convrot_linear_prepare_weights. */
+CONVROT_API int convrot_swiglu_prepare_weights(const void *W, int w_dtype,
+                                               const float *src_scale, int64_t F, int64_t K,
+                                               int block, convrot_weights *out, void *ws,
+                                               size_t ws_bytes, void *stream);
+
+/* Workspace for convrot_swiglu_mlp_forward (codes of X, g [M, F] bf16, codes
+ * of g, row scales); block_up and block_down are fc1's and fc2's blocks. */
+CONVROT_API size_t convrot_swiglu_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F,
+                                                      int64_t N, int block_up,
+                                                      int block_down);
+
+/* Y = linear(g; W_down) + bias_down with g = swiglu(linear(X; W_gu) + bias_gu).
+ *   X        device bf16 [M, K].
+ *   W_gu     prepared by convrot_swiglu_prepare_weights (2F x K).
+ *   bias_gu  device F32 [2F] in source order (gate biases, then up), or NULL.
+ *   W_down   a plain prepared weight [N, F]; its block may differ from W_gu's
+ *            (64 for ConvRot64); both must have the same rotation kind.
+ *   bias_down device F32 [N] or NULL; Y device [M, N] (BF16 or F32).
+ * ELAYOUT if W_gu lacks CONVROT_SWIGLU_PAIRS, W_down has it, W_gu->N != 2F or
+ * the rotation kinds differ. */
+CONVROT_API int convrot_swiglu_mlp_forward(const void *X, int64_t M, const convrot_weights *W_gu,
+                                           const float *bias_gu,
+                                           const convrot_weights *W_down,
+                                           const float *bias_down, void *Y, int y_dtype,
+                                           void *ws, size_t ws_bytes, void *stream);
+
+/* The SwiGLU activation on its own (a test hook and the unfused form): g [M, F]
+ * from gu [M, 2F] (gate | up), bf16 device buffers, 16-byte aligned,
+ * F % 8 == 0. */
+CONVROT_API int convrot_swiglu_bf16(const uint16_t *gu, int64_t M, int64_t F, uint16_t *g,
+                                    void *stream);
+
+/* s[i] = fp32(silu(a[i])) for n bf16 values, the s of every SwiGLU path
+ * (test hook: lets a test compare every bf16 pattern at fp32 precision). */
+CONVROT_API int convrot_silu_f32(const uint16_t *a, int64_t n, float *s, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* comparison variant (not the W8A8 path)                              */
 /* ------------------------------------------------------------------ */
 
@@ -381,6 +453,11 @@ CONVROT_API int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_wei
  * bf16(GELU(float(bf16(Y)))), the activation the MLP entry point feeds to its
  * down projection. */
 #define CONVROT_FLAG_GELU 1u
+/* CONVROT_FLAG_SWIGLU (W prepared by convrot_swiglu_prepare_weights, y_dtype
+ * BF16): the epilogue writes g = swiglu of the bf16 fc1 outputs, Y [M, W->N/2],
+ * as convrot_swiglu_mlp_forward feeds its down projection; the bias is [W->N]
+ * in source order. */
+#define CONVROT_FLAG_SWIGLU 2u
 CONVROT_API int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
                          const convrot_weights *W, const float *bias, void *Y,
                          int y_dtype, uint32_t flags, void *stream);

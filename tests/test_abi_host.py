@@ -177,8 +177,20 @@ def test_hook_validation(cr):
     d = _desc(cr)
     assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, cr.F32,
                                     cr.FLAG_GELU, None) == cr.EUNSUPPORTED
-    assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, cr.BF16, 2,
+    assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, cr.BF16, 4,
                                     None) == cr.EUNSUPPORTED
+    # the SwiGLU epilogue needs a weight prepared as SwiGLU pairs, and a plain
+    # forward refuses such a weight
+    assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, cr.BF16,
+                                    cr.FLAG_SWIGLU, None) == cr.ELAYOUT
+    dp = _desc(cr)
+    dp.flags = cr.SWIGLU_PAIRS
+    assert lib.convrot_linear_forward(FAKE, 4, ctypes.byref(dp), None, FAKE, cr.BF16, FAKE,
+                                      1 << 30, None) == cr.ELAYOUT
+    assert lib.convrot_gemm_dequant(FAKE, FAKE, 4, ctypes.byref(dp), None, FAKE, cr.F32,
+                                    cr.FLAG_SWIGLU, None) == cr.EUNSUPPORTED
+    assert lib.convrot_swiglu_mlp_forward(FAKE, 4, ctypes.byref(d), None, ctypes.byref(d), None,
+                                          FAKE, cr.BF16, FAKE, 1 << 30, None) == cr.ELAYOUT
     assert lib.convrot_gemm_i32(FAKE_ODD, 4, ctypes.byref(d), FAKE, None) == cr.EALIGN
     f1 = lambda d, M=4, qx=FAKE, sx=FAKE, qh=FAKE, sh=FAKE: lib.convrot_lowrank_factor1(
         qx, sx, M, ctypes.byref(d), qh, sh, None)

@@ -175,3 +175,32 @@ def test_max_rows_gelu_on_load(cr):
     y_ref = oracle.mlp_forward(bf16_bits(X[rows_d]), qu, su, qd, sd, b, out="bf16")
     assert assert_output_parity(bf16_bits(y[rows_d]), y_ref, "bf16",
                                 f"MLP M={M} F={F} sampled rows") == 0
+
+
+def test_swiglu_16384_fullsize(cr):
+    """SwiGLU MLP M=16384, fc1 K=5376 -> 2 x 21504 (b=128), fc2 21504 -> 5376
+    with ConvRot64: fc1 codes on every row, g and the outputs on sampled rows,
+    in the launch configuration the benchmark times."""
+    w = wl.WORKLOADS["swiglu_16384"]
+    announce(w.description)
+    x, Wgu, Wd = w.activations(), w.weight("w"), w.weight("w2")
+    F = w.ffn
+    pgu = cr.convrot_swiglu_prepare(to_dev(Wgu), w.block)
+    p = np.arange(2 * F)
+    perm = np.where(p % 32 < 16, (p // 32) * 16 + p % 32, F + (p // 32) * 16 + p % 32 - 16)
+    qgu, sgu = oracle.prepare_weights(Wgu, w.block)
+    assert np.array_equal(host(pgu.scale), sgu[perm])
+    pd, qd, sd = _prep(cr, Wd, w.down_block)
+    X = to_dev_bf16(x)
+    y = cr.convrot_swiglu_mlp_forward(X, pgu, pd)
+    qx, sx = cr.convrot_rotate_quantize(X, w.block)
+    g = cr.convrot_gemm_dequant(qx, sx, pgu, swiglu=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.M, 24)
+    y_ref, gu_ref, g_ref = oracle.swiglu_mlp_forward(x[rows], qgu, sgu, qd, sd, w.block,
+                                                     w.down_block, out="bf16",
+                                                     return_intermediates=True)
+    gr = bf16_bits(g[torch.from_numpy(rows).cuda()])
+    assert np.array_equal(gr, g_ref), int(np.count_nonzero(gr != g_ref))
+    yr = bf16_bits(y[torch.from_numpy(rows).cuda()])
+    assert assert_output_parity(yr, y_ref, "bf16", "swiglu_16384 sampled rows") == 0

@@ -910,3 +910,132 @@ def test_nonfinite_rows_stay_local(cr):
     ym_ref = oracle.mlp_forward(x[good], qu, su, qd, sd, w.block, out="bf16")
     assert np.array_equal(ym[good], ym_ref)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- SwiGLU ----
+
+def swiglu_perm(F):
+    """Source row of each packed row of a SwiGLU fc1 weight: 32-row blocks of
+    16 gate rows and their 16 up rows (restated from the header)."""
+    p = np.arange(2 * F)
+    blk, r = p // 32, p % 32
+    return np.where(r < 16, blk * 16 + r, F + blk * 16 + (r - 16))
+
+
+def test_silu_f32_every_pattern(cr):
+    """fp32 silu of every bf16 gate pattern, as every SwiGLU path computes it
+    (the LDS slice and the closed forms outside it), equals the oracle's."""
+    announce("silu fp32, every bf16 pattern")
+    a = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = host(cr.convrot_silu_f32(to_dev_bf16(a)))
+    ref = oracle.silu_f32(a)
+    fin = np.isfinite(wl.bf16_bits_to_f32(a))
+    diff = fin & (s.view(np.uint32) != ref.view(np.uint32))
+    print(f"[parity] silu: {int(diff.sum())} of {int(fin.sum())} finite patterns differ",
+          flush=True)
+    assert not diff.any(), [hex(int(x)) for x in a[diff][:8]]
+
+
+def test_swiglu_hook_matches_oracle(cr):
+    """The elementwise SwiGLU hook on gates and ups of wide dynamic range
+    (tiny, ordinary and huge magnitudes, zeros), ragged M."""
+    announce("swiglu hook")
+    rng = np.random.default_rng(61)
+    M, F = 77, 1024
+    mag = 2.0 ** rng.integers(-40, 12, (M, 2 * F))
+    gu = wl.f32_to_bf16_bits((rng.standard_normal((M, 2 * F)) * mag).astype(np.float32))
+    gu[0, :64] = 0
+    g = bf16_bits(cr.convrot_swiglu_bf16(to_dev_bf16(gu)))
+    assert np.array_equal(g, oracle.swiglu_bf16(gu))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+def test_swiglu_prepare_interleaved(cr, dtype):
+    """convrot_swiglu_prepare_weights stores the codes and scales of row
+    perm(p) at packed row p: float weights are rotated and quantised per row,
+    imported codes and scales are moved unchanged."""
+    announce(f"swiglu prepare {dtype}")
+    F, K, b = 272, 512, 128
+    rng = np.random.default_rng(62)
+    W = (rng.standard_normal((2 * F, K)) * 0.02).astype(np.float32)
+    perm = swiglu_perm(F)
+    if dtype == "i8":
+        q = rng.integers(-127, 128, (2 * F, K)).astype(np.int8)
+        sc = rng.uniform(0.5, 2.0, 2 * F).astype(np.float32)
+        pw = cr.convrot_swiglu_prepare(to_dev(q), b, src_scale=to_dev(sc))
+        q_ref, s_ref = q[perm], sc[perm]
+    elif dtype == "bf16":
+        Wb = wl.f32_to_bf16_bits(W)
+        pw = cr.convrot_swiglu_prepare(to_dev_bf16(Wb), b)
+        q_ref, s_ref = oracle.prepare_weights(Wb[perm], b, dtype="bf16")
+    else:
+        pw = cr.convrot_swiglu_prepare(to_dev(W), b)
+        q_ref, s_ref = oracle.prepare_weights(W[perm], b)
+    assert pw.desc.flags & cr.SWIGLU_PAIRS
+    assert np.array_equal(untile(pw.codes, 2 * F, K), q_ref)
+    assert np.array_equal(host(pw.scale), s_ref)
+
+
+def test_swiglu_epilogue_every_pattern(cr):
+    """Every bf16 gate pattern through the fused SwiGLU epilogue of fc1.
+    Imported codes are one-hot at k = 0 and the activation codes 1 there, so
+    the gate output is bf16((1 * s_x) * s_w) with s_w holding every pattern in
+    a seeded order, the up outputs take seeded scales; rows scale everything
+    by 1, 0, 2^-100, 2^100 and seeded factors.  Expected: the oracle's
+    dequant to bf16, then its SwiGLU (both NaN counts as equal)."""
+    announce("swiglu epilogue, every bf16 gate pattern")
+    M, K, F, b = 300, 128, 65536, 128
+    rng = np.random.default_rng(63)
+    sw = np.empty(2 * F, np.float32)
+    sw[:F] = (rng.permutation(65536).astype(np.uint32) << 16).view(np.float32)
+    sw[F:] = (rng.standard_normal(F) * 2.0 ** rng.integers(-3, 4, F)).astype(np.float32)
+    sx = (2.0 ** rng.integers(-12, 13, M) * rng.uniform(0.5, 1.0, M)).astype(np.float32)
+    sx[:4] = [1.0, 0.0, 2.0 ** -100, 2.0 ** 100]
+    qw = np.zeros((2 * F, K), np.int8)
+    qw[:, 0] = 1
+    qx = np.zeros((M, K), np.int8)
+    qx[:, 0] = 1
+    pw = cr.convrot_swiglu_prepare(to_dev(qw), b, src_scale=to_dev(sw))
+    g = bf16_bits(cr.convrot_gemm_dequant(to_dev(tile(qx)), to_dev(sx), pw, swiglu=True))
+    gu_ref = oracle.dequant(oracle.gemm_i32(qx, qw), sx, sw, out="bf16")
+    g_ref = oracle.swiglu_bf16(gu_ref)
+    nan = lambda a: ((a & 0x7f80) == 0x7f80) & ((a & 0x007f) != 0)
+    diff = (g != g_ref) & ~(nan(g) & nan(g_ref))
+    print(f"[parity] swiglu epilogue: {int(diff.sum())} of {g.size} outputs differ", flush=True)
+    assert not diff.any(), [(hex(int(a)), hex(int(e))) for a, e in zip(g[diff][:6], g_ref[diff][:6])]
+
+
+@pytest.mark.parametrize("M,K,F,N,bu,bd,rot,bias,out", [
+    (300, 1024, 768, 272, 128, 64, "sylvester", True, "bf16"),
+    (257, 512, 6400, 160, 128, 64, "sylvester", False, "f32"),
+    (64, 256, 512, 128, 64, 64, "regular", True, "bf16"),
+    (1, 512, 256, 48, 256, 128, "sylvester", True, "f32"),
+    (513, 5376, 1024, 256, 128, 64, "sylvester", True, "bf16"),
+])
+def test_swiglu_mlp_parity(cr, M, K, F, N, bu, bd, rot, bias, out):
+    """The SwiGLU MLP through its entry point: fc1 codes (interleaved), the
+    intermediate g from the fused epilogue, and every output, bit-exact
+    against the oracle (fc1 block bu, fc2 block bd: ConvRot64 when 64)."""
+    announce(f"swiglu mlp M={M} K={K} F={F} N={N} b={bu}/{bd} {rot} bias={bias} out={out}")
+    w = wl.scaled("swiglu_16384", M=M, K=K, ffn=F, N=N, block=bu, block2=bd,
+                  out=out, bias_std=0.5 if bias else None)
+    x, Wgu, Wd = w.activations(), w.weight("w"), w.weight("w2")
+    bgu = w.bias("bias", 2 * F) if bias else None
+    bdn = w.bias("bias2", N) if bias else None
+    pgu = cr.convrot_swiglu_prepare(to_dev(Wgu), bu, rotation=rot)
+    pd = cr.convrot_linear_prepare_weights(to_dev(Wd), bd, rotation=rot)
+    qgu, sgu = oracle.prepare_weights(Wgu, bu, rot=rot)
+    qd, sd = oracle.prepare_weights(Wd, bd, rot=rot)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    X = to_dev_bf16(x)
+    y = cr.convrot_swiglu_mlp_forward(X, pgu, pd, bias_gu=to_dev(bgu) if bias else None,
+                                      bias_down=to_dev(bdn) if bias else None, out_dtype=od)
+    y_ref, gu_ref, g_ref = oracle.swiglu_mlp_forward(x, qgu, sgu, qd, sd, bu, bd, bias_gu=bgu,
+                                                     bias_down=bdn, out=out, rot=rot,
+                                                     return_intermediates=True)
+    qx, sx = cr.convrot_rotate_quantize(X, bu, rotation=rot)
+    g = bf16_bits(cr.convrot_gemm_dequant(qx, sx, pgu, bias=to_dev(bgu) if bias else None,
+                                          swiglu=True))
+    assert np.array_equal(g, g_ref), f"g: {int(np.count_nonzero(g != g_ref))} differ"
+    yh = bf16_bits(y) if out == "bf16" else host(y)
+    assert assert_output_parity(yh, y_ref, out, "swiglu mlp") == 0

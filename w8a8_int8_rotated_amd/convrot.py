@@ -23,6 +23,8 @@ WEIGHTS_VERSION = 2
 ROT_REGULAR = 0x100          # rotation kind: regular H_4 Kronecker blocks
 ROTATIONS = {"sylvester": 0, "regular": ROT_REGULAR}
 FLAG_GELU = 1
+FLAG_SWIGLU = 2
+SWIGLU_PAIRS = 0x200         # weight flag: interleaved SwiGLU gate/up rows
 
 _c_i64 = ctypes.c_int64
 _c_int = ctypes.c_int
@@ -74,6 +76,15 @@ _SIGNATURES = {
     "convrot_gemm_dequant": (
         _c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_int, ctypes.c_uint32, _c_p]),
     "convrot_lowrank_factor1": (_c_int, [_c_p, _c_p, _c_i64, _W, _c_p, _c_p, _c_p]),
+    "convrot_swiglu_prepare_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_int, _c_int]),
+    "convrot_swiglu_prepare_weights": (
+        _c_int, [_c_p, _c_int, _c_p, _c_i64, _c_i64, _c_int, _W, _c_p, _c_sz, _c_p]),
+    "convrot_swiglu_mlp_workspace_bytes": (
+        _c_sz, [_c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int]),
+    "convrot_swiglu_mlp_forward": (
+        _c_int, [_c_p, _c_i64, _W, _c_p, _W, _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
+    "convrot_swiglu_bf16": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
+    "convrot_silu_f32": (_c_int, [_c_p, _c_i64, _c_p, _c_p]),
     "lowrank_bf16_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "lowrank_bf16_forward": (
         _c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_i64, _c_p, _c_p, _c_p,
@@ -445,6 +456,106 @@ def convrot_mlp_forward(X: torch.Tensor, W_up: PreparedWeights, W_down: Prepared
     return out
 
 
+# ------------------------------------------------------------ SwiGLU ----
+
+def convrot_swiglu_mlp_workspace_bytes(M, K, F, N, block_up, block_down) -> int:
+    return library().convrot_swiglu_mlp_workspace_bytes(M, K, F, N, block_up, block_down)
+
+
+def convrot_swiglu_prepare(W: torch.Tensor, block: int, src_scale: torch.Tensor | None = None,
+                           stream=None, rotation: str = "sylvester") -> PreparedWeights:
+    """Prepare a SwiGLU fc1 weight [2F, K] (gate rows, then up rows): float32 or
+    bfloat16 weights, or int8 codes with src_scale [2F]; stored interleaved
+    (SWIGLU_PAIRS) for the fused SwiGLU epilogue."""
+    lib = library()
+    if not isinstance(W, torch.Tensor) or W.dim() != 2 or W.shape[0] % 2:
+        raise ValueError("W must be a 2-D tensor [2F, K]")
+    N2, K = W.shape
+    if W.dtype not in (torch.float32, torch.bfloat16, torch.int8):
+        raise ValueError(f"W must be float32, bfloat16 or int8 codes, got {W.dtype}")
+    if (W.dtype == torch.int8) != (src_scale is not None):
+        raise ValueError("src_scale is required for int8 codes and only for them")
+    _opt(src_scale, "src_scale", torch.float32, (N2,))
+    if rotation not in ROTATIONS:
+        raise ValueError(f"rotation must be one of {sorted(ROTATIONS)}")
+    W = W.contiguous()
+    _on_device(W.device, W=W, src_scale=src_scale)
+    tag = _dtype_tag(W.dtype)
+    nbytes = lib.convrot_weights_packed_bytes(N2, K, block)
+    wsb = lib.convrot_swiglu_prepare_workspace_bytes(N2 // 2, K, block, tag)
+    if nbytes == 0 or wsb == 0:
+        raise ConvRotError("convrot_swiglu_prepare_weights", EUNSUPPORTED)
+    codes = torch.empty(nbytes, dtype=torch.int8, device=W.device)
+    scale = torch.empty(N2, dtype=torch.float32, device=W.device)
+    desc = convrot_weights()
+    desc.codes, desc.scale, desc.flags = codes.data_ptr(), scale.data_ptr(), ROTATIONS[rotation]
+    ws = _workspace(wsb, W.device, None)
+    rc = lib.convrot_swiglu_prepare_weights(_ptr(W), tag, _ptr(src_scale), N2 // 2, K, block,
+                                            ctypes.byref(desc), _ptr(ws), wsb, _stream(stream))
+    _check("convrot_swiglu_prepare_weights", rc)
+    pw = PreparedWeights(desc, codes, scale)
+    pw._ws = ws
+    return pw
+
+
+def convrot_swiglu_mlp_forward(X: torch.Tensor, W_gu: PreparedWeights, W_down: PreparedWeights,
+                               bias_gu=None, bias_down=None,
+                               out_dtype: torch.dtype = torch.bfloat16, out=None,
+                               workspace=None, stream=None) -> torch.Tensor:
+    """Y = linear(swiglu(linear(X; W_gu) + bias_gu); W_down) + bias_down."""
+    lib = library()
+    dev = _weights(W_gu, "W_gu")
+    if _weights(W_down, "W_down") != dev:
+        raise ValueError("W_gu and W_down must be on the same device")
+    M = _rows(X, "X", W_gu.K)
+    F = W_down.K
+    _opt(bias_gu, "bias_gu", torch.float32, (W_gu.N,))
+    _opt(bias_down, "bias_down", torch.float32, (W_down.N,))
+    _output(out, M, W_down.N, (torch.bfloat16, torch.float32))
+    wsb = lib.convrot_swiglu_mlp_workspace_bytes(M, W_gu.K, F, W_down.N, W_gu.block,
+                                                 W_down.block)
+    _check_workspace(wsb, workspace)
+    _on_device(dev, X=X, bias_gu=bias_gu, bias_down=bias_down, out=out, workspace=workspace)
+    if out is None:
+        out = torch.empty((M, W_down.N), dtype=out_dtype, device=dev)
+    ws = _workspace(wsb, dev, workspace)
+    rc = lib.convrot_swiglu_mlp_forward(_ptr(X), M, W_gu.ref(), _ptr(bias_gu), W_down.ref(),
+                                        _ptr(bias_down), _ptr(out), _dtype_tag(out.dtype),
+                                        _ptr(ws), ws.numel() if ws is not None else 0,
+                                        _stream(stream))
+    _check("convrot_swiglu_mlp_forward", rc)
+    return out
+
+
+def convrot_swiglu_bf16(gu: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """g [M, F] = bf16(fp32(silu(gate)) * up) for gu [M, 2F] = gate | up."""
+    lib = library()
+    if not isinstance(gu, torch.Tensor) or gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be a 2-D tensor [M, 2F]")
+    M, F = gu.shape[0], gu.shape[1] // 2
+    _need(gu, "gu", torch.bfloat16, (M, 2 * F))
+    _opt(out, "out", torch.bfloat16, (M, F))
+    _on_device(gu.device, gu=gu, out=out)
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.bfloat16, device=gu.device)
+    _check("convrot_swiglu_bf16", lib.convrot_swiglu_bf16(_ptr(gu), M, F, _ptr(out),
+                                                          _stream(stream)))
+    return out
+
+
+def convrot_silu_f32(a: torch.Tensor, stream=None) -> torch.Tensor:
+    """fp32(silu(a)) of bf16 values, as every SwiGLU path computes it."""
+    lib = library()
+    if not isinstance(a, torch.Tensor) or a.dtype != torch.bfloat16:
+        raise ValueError("a must be a bf16 tensor")
+    a = a.contiguous()
+    _on_device(a.device, a=a)
+    out = torch.empty(a.shape, dtype=torch.float32, device=a.device)
+    _check("convrot_silu_f32", lib.convrot_silu_f32(_ptr(a), a.numel(), _ptr(out),
+                                                    _stream(stream)))
+    return out
+
+
 def lowrank_bf16_forward(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, bias=None,
                          out=None, workspace=None, stream=None) -> torch.Tensor:
     """Comparison variant: bf16(bf16(X . A^T) . B^T + bias), bf16 factors
@@ -536,8 +647,9 @@ def convrot_gemm_i32(q_x: torch.Tensor, M: int, W: PreparedWeights, out=None, st
 
 def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeights, bias=None,
                          out_dtype: torch.dtype = torch.bfloat16, out=None, gelu: bool = False,
-                         stream=None):
-    """Y [M, N] from K-tiled codes q_x and row scales s_x [M]."""
+                         swiglu: bool = False, stream=None):
+    """Y [M, N] from K-tiled codes q_x and row scales s_x [M] (with swiglu, W a
+    SwiGLU fc1 weight and Y = g [M, N/2])."""
     lib = library()
     dev = _weights(W, "W")
     if not isinstance(s_x, torch.Tensor) or s_x.dim() != 1:
@@ -546,13 +658,14 @@ def convrot_gemm_dequant(q_x: torch.Tensor, s_x: torch.Tensor, W: PreparedWeight
     _need(s_x, "s_x", torch.float32, (M,))
     _codes(q_x, M, W.K, dev)
     _opt(bias, "bias", torch.float32, (W.N,))
-    _output(out, M, W.N, (torch.bfloat16, torch.float32))
+    ncols = W.N // 2 if swiglu else W.N
+    _output(out, M, ncols, (torch.bfloat16, torch.float32))
     _on_device(dev, q_x=q_x, s_x=s_x, bias=bias, out=out)
     if out is None:
-        out = torch.empty((M, W.N), dtype=out_dtype, device=dev)
+        out = torch.empty((M, ncols), dtype=out_dtype, device=dev)
+    flags = (FLAG_GELU if gelu else 0) | (FLAG_SWIGLU if swiglu else 0)
     rc = lib.convrot_gemm_dequant(_ptr(q_x), _ptr(s_x), M, W.ref(), _ptr(bias), _ptr(out),
-                                  _dtype_tag(out.dtype), FLAG_GELU if gelu else 0,
-                                  _stream(stream))
+                                  _dtype_tag(out.dtype), flags, _stream(stream))
     _check("convrot_gemm_dequant", rc)
     return out
 

@@ -57,7 +57,18 @@ enum class InType { F32 = 0, BF16 = 1 };
 int device_cu_count();
 // BF16_MM: not an INT8 path -- bf16 x bf16 operands, row-major, fp32
 // accumulation, y = bf16(acc (+ bias)); used by the bf16 low-rank variant.
-enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3, BF16_MM = 4 };
+// SWIGLU_BF16: the weight rows come in 32-row blocks of 16 gate rows and their
+// 16 up rows (convrot_swiglu_prepare_weights); the epilogue writes
+// g = bf16(fp32(silu(bf16 gate)) * bf16 up) as an [M, N/2] bf16 matrix.
+enum class OutKind { BF16 = 0, F32 = 1, I32 = 2, GELU_BF16 = 3, BF16_MM = 4, SWIGLU_BF16 = 5 };
+
+// Packed row p of a SwiGLU fc1 weight holds source row swiglu_src_row(p, F)
+// of the [2F, K] weight (gate rows 0 .. F-1, up rows F .. 2F-1).
+__host__ __device__ inline int64_t swiglu_src_row(int64_t p, int64_t F)
+{
+    const int64_t blk = p >> 5, r = p & 31;
+    return r < 16 ? blk * 16 + r : F + blk * 16 + (r - 16);
+}
 
 // Rotate (blockwise Sylvester FWHT, or with `regular` the H_4 = J - 2I
 // Kronecker blocks for block 64 or 256) + rowwise INT8 quantise.  src rows
@@ -75,6 +86,16 @@ bool rotquant_fuses_gelu(int64_t K);
 hipError_t launch_rotquant_gelu(const void *src, int64_t M, int64_t K, int64_t ld, int block,
                                 bool regular, float inv_sqrt_b, const uint16_t *gelu_table,
                                 int8_t *q, float *s, hipStream_t stream);
+
+// SwiGLU (fc1 output gu [M, 2F] = gate | up): the elementwise g [M, F] =
+// bf16(fp32(silu(gate)) * up) (F % 8 == 0, 16-byte aligned buffers);
+// fp32(silu(a)) for n bf16 values; and the device address of the silu table
+// (fp32 silu of every bf16 pattern, written once per device like the GELU
+// table), which the fused SwiGLU epilogue of the GEMM reads.
+hipError_t launch_swiglu_bf16(const uint16_t *gu, int64_t M, int64_t F, uint16_t *g,
+                              hipStream_t stream);
+hipError_t launch_silu_f32(const uint16_t *a, int64_t n, float *out, hipStream_t stream);
+hipError_t launch_silu_table(const float **table, hipStream_t stream);
 
 // Factor 1 of the low-rank chain with the requantisation fused in:
 // (qh, sh) = rotate+quantise(bf16(((float)(qx . qa^T) * sx) * sa)) along the R
@@ -108,11 +129,20 @@ hipError_t launch_transpose(const void *src, void *dst, int64_t R, int64_t C,
 
 // acc/Y[M, N] = epilogue(qx[M, K] . qw[N, K]^T), both code matrices K-tiled.
 // For OutKind::BF16_MM, qx and qw are row-major bf16 matrices, K counts
-// their row bytes (2 x elements), and sx, sw are unused.
+// their row bytes (2 x elements), and sx, sw are unused.  For
+// OutKind::SWIGLU_BF16, Y is [M, N/2] and the bias is indexed by source row
+// (swiglu_src_row).
 hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
                           const float *sw, const float *bias, void *Y,
                           OutKind out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream);
+
+// Copy the rows of a [2F, K] SwiGLU fc1 weight (elem_bytes 1, 2 or 4), or of
+// its scales (K = 1, elem_bytes 4), into the interleaved order of
+// swiglu_src_row: dst row p = src row swiglu_src_row(p, F).
+// K * elem_bytes % 4 == 0.
+hipError_t launch_swiglu_interleave(const void *src, void *dst, int64_t F, int64_t K,
+                                    int elem_bytes, hipStream_t stream);
 
 // Measurement probes (probes.hip): INT8 MFMA rounds on changing operands, one
 // workgroup per CU (probe_mfma_i8_ops: the INT8 operations of one launch),

@@ -66,6 +66,11 @@ bool valid_rotation(uint32_t rot, int b)
 }
 
 bool is_regular(const convrot_weights *W) { return (W->flags & CONVROT_ROT_REGULAR) != 0; }
+uint32_t rotation_of(const convrot_weights *W) { return (uint32_t)W->flags & CONVROT_ROT_REGULAR; }
+bool is_swiglu_pairs(const convrot_weights *W)
+{
+    return ((uint32_t)W->flags & CONVROT_SWIGLU_PAIRS) != 0;
+}
 
 // fp32 1/sqrt(b), rounded once from double.
 float inv_sqrt_block(int b) { return (float)(1.0 / std::sqrt((double)b)); }
@@ -89,7 +94,10 @@ int check_linear_shape(int64_t N, int64_t K, int block)
     return CONVROT_OK;
 }
 
-int check_weights(const convrot_weights *W)
+// A prepared descriptor.  `pairs`: whether the weight must (true) or must not
+// (false) hold interleaved SwiGLU gate/up rows; a mismatch is ELAYOUT, since
+// the outputs of such a weight are not the columns of a plain linear.
+int check_weights(const convrot_weights *W, bool pairs = false)
 {
     if (!W) return CONVROT_EINVAL;
     if (W->magic != CONVROT_WEIGHTS_MAGIC || W->version != CONVROT_WEIGHTS_VERSION)
@@ -97,7 +105,11 @@ int check_weights(const convrot_weights *W)
     if (!W->codes || !W->scale) return CONVROT_EINVAL;
     if (!aligned16(W->codes) || !aligned16(W->scale)) return CONVROT_EALIGN;
     int rc = check_linear_shape(W->N, W->K, W->block);
-    if (rc == CONVROT_OK && !valid_rotation((uint32_t)W->flags, W->block)) return CONVROT_ELAYOUT;
+    const uint32_t extra = (uint32_t)W->flags & ~(CONVROT_ROT_REGULAR | CONVROT_SWIGLU_PAIRS);
+    if (rc == CONVROT_OK &&
+        (extra != 0 || !valid_rotation(rotation_of(W), W->block) || is_swiglu_pairs(W) != pairs ||
+         (pairs && W->N % 32 != 0)))
+        return CONVROT_ELAYOUT;
     return rc == CONVROT_EINVAL ? CONVROT_ELAYOUT : rc;
 }
 
@@ -226,7 +238,7 @@ static int prepare_weights_impl(const void *W, int w_dtype, int layout,
     const bool import = (w_dtype == CONVROT_I8);
     if (import != (src_scale != nullptr)) return CONVROT_EINVAL;
     const uint32_t rot = (uint32_t)out->flags;
-    if (!valid_rotation(rot, block)) return CONVROT_EINVAL;
+    if (!valid_rotation(rot, block)) return CONVROT_EINVAL;   // SwiGLU pairs: their own entry
     if (!aligned16(W) || !aligned16(out->codes) || !aligned16(out->scale) ||
         (src_scale && !aligned16(src_scale)))
         return CONVROT_EALIGN;
@@ -401,6 +413,161 @@ int convrot_linear_forward(const void *X, int64_t M, const convrot_weights *W,
     const int rc = linear_forward_impl(X, M, W, bias, Y, y_dtype, ws, ws_bytes, stream);
     log_call("convrot_linear_forward", M, W ? W->N : 0, W ? W->K : 0, rc);
     return rc;
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU MLP (MiniMax-H3-Rung-Omega README, "Technical Architecture
+// Overview", Floor 1: SwiGLU, ConvRot64 and the rowwise INT8 quantise in front
+// of MLP.fc2).  fc1 is one linear with 2F outputs, gate then up; its weight
+// rows are stored interleaved (swiglu_src_row) so that the fc1 epilogue holds
+// each gate next to its up value and writes g = bf16(silu(gate) * up) alone.
+// ---------------------------------------------------------------------------
+
+size_t convrot_swiglu_prepare_workspace_bytes(int64_t F, int64_t K, int block, int w_dtype)
+{
+    if (F <= 0 || F >= kI32Bound || F % 16 != 0 ||
+        check_linear_shape(2 * F, K, block) != CONVROT_OK)
+        return 0;
+    const size_t es = w_dtype == CONVROT_F32 ? 4u : w_dtype == CONVROT_BF16 ? 2u :
+                      w_dtype == CONVROT_I8 ? 1u : 0u;
+    if (es == 0) return 0;
+    return round_up((size_t)2 * F * (size_t)K * es, kAlign) +
+           (w_dtype == CONVROT_I8 ? round_up((size_t)8 * F, kAlign) : 0);
+}
+
+static int swiglu_prepare_impl(const void *W, int w_dtype, const float *src_scale, int64_t F,
+                               int64_t K, int block, convrot_weights *out, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    if (!W || !out || !out->codes || !out->scale || F <= 0) return CONVROT_EINVAL;
+    if (F >= kI32Bound || F % 16 != 0) return CONVROT_EUNSUPPORTED;
+    int rc = check_linear_shape(2 * F, K, block);
+    if (rc != CONVROT_OK) return rc;
+    if (w_dtype != CONVROT_F32 && w_dtype != CONVROT_BF16 && w_dtype != CONVROT_I8)
+        return CONVROT_EUNSUPPORTED;
+    const bool import = w_dtype == CONVROT_I8;
+    if (import != (src_scale != nullptr)) return CONVROT_EINVAL;
+    if (!valid_rotation((uint32_t)out->flags, block)) return CONVROT_EINVAL;
+    if (!aligned16(W) || !aligned16(out->codes) || !aligned16(out->scale) ||
+        (src_scale && !aligned16(src_scale)) || (ws && !aligned16(ws)))
+        return CONVROT_EALIGN;
+    const size_t need = convrot_swiglu_prepare_workspace_bytes(F, K, block, w_dtype);
+    if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
+    const int es = w_dtype == CONVROT_F32 ? 4 : w_dtype == CONVROT_BF16 ? 2 : 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carve c(ws);
+    void *rows = c.take((size_t)2 * F * (size_t)K * es);
+    hipError_t e = convrot::launch_swiglu_interleave(W, rows, F, K, es, s);
+    const float *scales = nullptr;
+    if (import && e == hipSuccess) {
+        // the per-output scales follow their rows (rows of one 4-byte scale)
+        void *sc = c.take((size_t)8 * F);
+        e = convrot::launch_swiglu_interleave(src_scale, sc, F, 1, 4, s);
+        scales = static_cast<const float *>(sc);
+    }
+    rc = hip_status(e);
+    if (rc != CONVROT_OK) return rc;
+    rc = prepare_weights_impl(rows, w_dtype, CONVROT_OUT_MAJOR, scales, 2 * F, K, block, out,
+                              nullptr, 0, stream);
+    if (rc == CONVROT_OK) out->flags |= (int32_t)CONVROT_SWIGLU_PAIRS;
+    return rc;
+}
+
+int convrot_swiglu_prepare_weights(const void *W, int w_dtype, const float *src_scale, int64_t F,
+                                   int64_t K, int block, convrot_weights *out, void *ws,
+                                   size_t ws_bytes, void *stream)
+{
+    const int rc = swiglu_prepare_impl(W, w_dtype, src_scale, F, K, block, out, ws, ws_bytes,
+                                       stream);
+    log_call("convrot_swiglu_prepare_weights", 0, 2 * F, K, rc);
+    return rc;
+}
+
+size_t convrot_swiglu_mlp_workspace_bytes(int64_t M, int64_t K, int64_t F, int64_t N,
+                                          int block_up, int block_down)
+{
+    if (F <= 0 || F >= kI32Bound || F % 16 != 0 ||
+        check_linear_shape(2 * F, K, block_up) != CONVROT_OK ||
+        check_linear_shape(N, F, block_down) != CONVROT_OK || check_rows(M, K) != CONVROT_OK ||
+        check_rows(M, F) != CONVROT_OK)
+        return 0;
+    return codes_bytes(M, K) + scales_bytes(M) + round_up((size_t)M * (size_t)F * 2u, kAlign) +
+           codes_bytes(M, F) + scales_bytes(M);
+}
+
+static int swiglu_forward_impl(const void *X, int64_t M, const convrot_weights *W_gu,
+                               const float *bias_gu, const convrot_weights *W_down,
+                               const float *bias_down, void *Y, int y_dtype, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    int rc = check_weights(W_gu, true);
+    if (rc != CONVROT_OK) return rc;
+    if ((rc = check_weights(W_down)) != CONVROT_OK) return rc;
+    if (W_gu->N != 2 * W_down->K || rotation_of(W_gu) != rotation_of(W_down))
+        return CONVROT_ELAYOUT;
+    const int64_t F = W_down->K;
+    if ((rc = check_rows(M, W_gu->K)) != CONVROT_OK) return rc;
+    if ((rc = check_rows(M, F)) != CONVROT_OK) return rc;
+    if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
+    if (M == 0) return CONVROT_OK;
+    if (!X || !Y) return CONVROT_EINVAL;
+    if (!aligned16(X) || !aligned16(Y) || (bias_gu && !aligned16(bias_gu)) ||
+        (bias_down && !aligned16(bias_down)) || (ws && !aligned16(ws)))
+        return CONVROT_EALIGN;
+    const size_t need = convrot_swiglu_mlp_workspace_bytes(M, W_gu->K, F, W_down->N,
+                                                           W_gu->block, W_down->block);
+    if (!ws || ws_bytes < need) return CONVROT_EWORKSPACE;
+
+    Carve c(ws);
+    int8_t *qx = static_cast<int8_t *>(c.take(codes_bytes(M, W_gu->K)));
+    float *sx = static_cast<float *>(c.take((size_t)M * 4u));
+    void *g = c.take((size_t)M * (size_t)F * 2u);
+    int8_t *qg = static_cast<int8_t *>(c.take(codes_bytes(M, F)));
+    float *sg = static_cast<float *>(c.take((size_t)M * 4u));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = convrot::launch_rotquant(X, convrot::InType::BF16, M, W_gu->K, W_gu->K,
+                                            W_gu->block, is_regular(W_gu),
+                                            inv_sqrt_block(W_gu->block), qx, sx, s);
+    // fc1 with the SwiGLU epilogue: g [M, F] is the only intermediate written
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qx, W_gu->codes, sx, W_gu->scale, bias_gu, g,
+                                    convrot::OutKind::SWIGLU_BF16, M, W_gu->N, W_gu->K, s);
+    if (e == hipSuccess)
+        e = convrot::launch_rotquant(g, convrot::InType::BF16, M, F, F, W_down->block,
+                                     is_regular(W_down), inv_sqrt_block(W_down->block), qg, sg, s);
+    if (e == hipSuccess)
+        e = convrot::launch_gemm_i8(qg, W_down->codes, sg, W_down->scale, bias_down, Y,
+                                    out_kind(y_dtype), M, W_down->N, F, s);
+    return hip_status(e);
+}
+
+int convrot_swiglu_mlp_forward(const void *X, int64_t M, const convrot_weights *W_gu,
+                               const float *bias_gu, const convrot_weights *W_down,
+                               const float *bias_down, void *Y, int y_dtype, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    const int rc = swiglu_forward_impl(X, M, W_gu, bias_gu, W_down, bias_down, Y, y_dtype, ws,
+                                       ws_bytes, stream);
+    log_call("convrot_swiglu_mlp_forward", M, W_down ? W_down->N : 0, W_gu ? W_gu->K : 0, rc);
+    return rc;
+}
+
+int convrot_swiglu_bf16(const uint16_t *gu, int64_t M, int64_t F, uint16_t *g, void *stream)
+{
+    if (M < 0 || F <= 0) return CONVROT_EINVAL;
+    if (F % 8 != 0 || M >= kI32Bound || F >= kI32Bound) return CONVROT_EUNSUPPORTED;
+    if (M == 0) return CONVROT_OK;
+    if (!gu || !g) return CONVROT_EINVAL;
+    if (!aligned16(gu) || !aligned16(g)) return CONVROT_EALIGN;
+    return hip_status(convrot::launch_swiglu_bf16(gu, M, F, g, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_silu_f32(const uint16_t *a, int64_t n, float *s_out, void *stream)
+{
+    if (n < 0) return CONVROT_EINVAL;
+    if (n == 0) return CONVROT_OK;
+    if (!a || !s_out) return CONVROT_EINVAL;
+    return hip_status(convrot::launch_silu_f32(a, n, s_out, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------
@@ -641,7 +808,8 @@ int convrot_rotate_quantize(const void *X, int x_dtype, int64_t M, int64_t K, in
 int convrot_gemm_i32(const int8_t *q_x, int64_t M, const convrot_weights *W, int32_t *acc,
                      void *stream)
 {
-    int rc = check_weights(W);
+    // any prepared weight, SwiGLU pairs included (columns in packed row order)
+    int rc = check_weights(W, W && is_swiglu_pairs(W));
     if (rc != CONVROT_OK) return rc;
     if ((rc = check_rows(M, W->K)) != CONVROT_OK) return rc;
     if (M == 0) return CONVROT_OK;
@@ -656,21 +824,25 @@ int convrot_gemm_dequant(const int8_t *q_x, const float *s_x, int64_t M,
                          const convrot_weights *W, const float *bias, void *Y, int y_dtype,
                          uint32_t flags, void *stream)
 {
-    int rc = check_weights(W);
+    if ((flags & ~(CONVROT_FLAG_GELU | CONVROT_FLAG_SWIGLU)) != 0 ||
+        flags == (CONVROT_FLAG_GELU | CONVROT_FLAG_SWIGLU))
+        return CONVROT_EUNSUPPORTED;
+    const bool gelu = (flags & CONVROT_FLAG_GELU) != 0;
+    const bool swiglu = (flags & CONVROT_FLAG_SWIGLU) != 0;
+    int rc = check_weights(W, swiglu);
     if (rc != CONVROT_OK) return rc;
     if ((rc = check_rows(M, W->K)) != CONVROT_OK) return rc;
     if ((rc = check_out_dtype(y_dtype)) != CONVROT_OK) return rc;
-    if ((flags & ~CONVROT_FLAG_GELU) != 0) return CONVROT_EUNSUPPORTED;
-    const bool gelu = (flags & CONVROT_FLAG_GELU) != 0;
-    if (gelu && y_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
+    if ((gelu || swiglu) && y_dtype != CONVROT_BF16) return CONVROT_EUNSUPPORTED;
     if (M == 0) return CONVROT_OK;
     if (!q_x || !s_x || !Y) return CONVROT_EINVAL;
     if (!aligned16(q_x) || !aligned16(s_x) || !aligned16(Y) || (bias && !aligned16(bias)))
         return CONVROT_EALIGN;
     return hip_status(convrot::launch_gemm_i8(
         q_x, W->codes, s_x, W->scale, bias, Y,
-        gelu ? convrot::OutKind::GELU_BF16 : out_kind(y_dtype), M, W->N, W->K,
-        static_cast<hipStream_t>(stream)));
+        swiglu ? convrot::OutKind::SWIGLU_BF16
+               : gelu ? convrot::OutKind::GELU_BF16 : out_kind(y_dtype),
+        M, W->N, W->K, static_cast<hipStream_t>(stream)));
 }
 
 int convrot_lowrank_factor1(const int8_t *q_x, const float *s_x, int64_t M,

@@ -355,6 +355,103 @@ __device__ __forceinline__ void gelu_store(void *Y, const uint32_t (&gv)[4][2][2
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// SwiGLU epilogue (MiniMax-H3-Rung-Omega README, "Technical Architecture
+// Overview", Floor 1: SwiGLU in front of the rotated, rowwise quantised fc2),
+// fused into fc1: the fc1 weight rows come in 32-row blocks of 16 gate rows
+// followed by their 16 up rows (swiglu_src_row), so in each 32-row fragment
+// lane (l32, g) holds, for token m, gate rows 8q + 4g + r and the matching up
+// rows 16 + 8q + 4g + r (q = 0, 1; r = 0..3).  Both are dequantised and
+// rounded to bf16 (the fc1 output), then g = bf16(fp32(silu(gate)) * up) is
+// formed and only g [M, N/2] is written: 16 columns per fragment, after a
+// v_permlane32_swap 8 consecutive ones (16 bytes) per lane.
+//
+// fp32(silu) comes from the LDS slice of the silu table with |gate| in
+// [2^-15, 2^8) (biased exponents 112..134, 11.5 KiB per sign, beside the 128
+// KiB of stages); a gate outside it (rare: tiny or huge, zero, inf, NaN) is
+// looked up in the full table in memory.
+constexpr int kSiluLoE = 112 << 7;     // first |gate| pattern of the slice
+constexpr int kSiluSpanE = 23 << 7;    // patterns per sign
+__shared__ float g_silu_lds[2 * kSiluSpanE];
+
+template <bool HAS_BIAS, int TJ, bool FULL>
+__device__ __forceinline__ void swiglu_epilogue(void *Y, const v16i (&acc)[4][TJ],
+                                                const float (&sscale)[3][kTile],
+                                                const float *__restrict__ silu_tab, int M,
+                                                int N, int m0, int n0, int wm, int wn, int l32,
+                                                int g)
+{
+    const int F = N >> 1;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int ml = wm * 32 * TJ + 32 * j + l32;
+        const int m = m0 + ml;
+        if (!FULL && m >= M) continue;
+        const float sxm = sscale[0][ml];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int nf = n0 + wn * 128 + 32 * i;       // first packed row of the fragment
+            if (!FULL && nf >= N) continue;
+            const v16i av = acc_frag(acc[i][j]);
+            // the fc1 outputs of this lane as packed bf16: [q][dword]
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * 128 + 32 * i + 8 * q + 4 * g;
+                const float4 swv = *reinterpret_cast<const float4 *>(&sscale[1][nl]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&sscale[2][nl]);
+                pk[q][0] = cvt_pk_bf16(
+                    dequant1<int(OutKind::BF16), HAS_BIAS>(av[4 * q + 0], sxm, swv.x, bv.x),
+                    dequant1<int(OutKind::BF16), HAS_BIAS>(av[4 * q + 1], sxm, swv.y, bv.y));
+                pk[q][1] = cvt_pk_bf16(
+                    dequant1<int(OutKind::BF16), HAS_BIAS>(av[4 * q + 2], sxm, swv.z, bv.z),
+                    dequant1<int(OutKind::BF16), HAS_BIAS>(av[4 * q + 3], sxm, swv.w, bv.w));
+            }
+            // fp32 silu of the 8 gates (q = 0, 1), from the LDS slice
+            float sv[2][4];
+            bool outside = false;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t a = (pk[h][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    const uint32_t off = (a & 0x7fffu) - (uint32_t)kSiluLoE;
+                    outside |= off >= (uint32_t)kSiluSpanE;
+                    sv[h][e] = g_silu_lds[(a >> 15) * kSiluSpanE +
+                                          min(off, (uint32_t)kSiluSpanE - 1u)];
+                }
+            if (__builtin_amdgcn_ballot_w64(outside)) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t a = (pk[h][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                        if ((a & 0x7fffu) - (uint32_t)kSiluLoE >= (uint32_t)kSiluSpanE)
+                            sv[h][e] = silu_tab[a];
+                    }
+            }
+            // g = bf16(s * up), up rows 16 + (the gate's row): q + 2
+            uint32_t d[2][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t u0 = pk[h + 2][0], u1 = pk[h + 2][1];
+                d[h][0] = cvt_pk_bf16(__fmul_rn(sv[h][0], __uint_as_float(u0 << 16)),
+                                      __fmul_rn(sv[h][1], __uint_as_float(u0 & 0xffff0000u)));
+                d[h][1] = cvt_pk_bf16(__fmul_rn(sv[h][2], __uint_as_float(u1 << 16)),
+                                      __fmul_rn(sv[h][3], __uint_as_float(u1 & 0xffff0000u)));
+            }
+            // lower lanes' q = 1 half <-> upper lanes' q = 0 half: lane g then
+            // holds columns 8 g .. 8 g + 7 of the fragment's 16
+            const auto s0 = __builtin_amdgcn_permlane32_swap(d[0][0], d[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(d[0][1], d[1][1], false, false);
+            uint4 o;
+            o.x = s0[0]; o.y = s1[0]; o.z = s0[1]; o.w = s1[1];
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(Y) + (int64_t)m * F +
+                                       (nf >> 1) + 8 * g) = o;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 template <int OUT, bool HAS_BIAS, int TJ, bool FULL>
 __device__ __forceinline__ void epilogue(void *Y, const v16i (&acc)[4][TJ],
                                          const float (&sscale)[3][kTile], int M, int N,
@@ -712,20 +809,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
     const int8_t *__restrict__ qx, const int8_t *__restrict__ qw,
     const float *__restrict__ sx, const float *__restrict__ sw,
     const float *__restrict__ bias, void *__restrict__ Y, int M, int N, int K,
-    int tiles_m, int tiles_n, int tiles_per_xcd, int wgs_per_xcd)
+    int tiles_m, int tiles_n, int tiles_per_xcd, int wgs_per_xcd,
+    const float *__restrict__ silu_tab)
 {
     constexpr int TM = 64 * TJ;            // tile edge in m
     constexpr int STGW = kTile * kBK;      // 16 KiB of weights per stage
     constexpr int STGX = TM * kBK;         // 16 or 8 KiB of activations per stage
     constexpr bool MM = OUT == int(OutKind::BF16_MM);   // bf16 operands, row-major
+    constexpr bool SWIGLU = OUT == int(OutKind::SWIGLU_BF16);
     constexpr bool BF16_OUT =
         OUT == int(OutKind::BF16) || OUT == int(OutKind::GELU_BF16) || MM;
     constexpr int NSCALE = OUT == int(OutKind::I32) ? 0 : MM ? (HAS_BIAS ? 1 : 0)
                                                              : (HAS_BIAS ? 3 : 2);
     // memory operations per wave between a tile's K-tile S-2 copies and its
-    // K-tile S-1 copies: the previous tile's stores (bf16: 4 x TJ x 2 of 16 B)
-    // and this tile's scale loads; other outputs drain at the tile boundary
-    constexpr int EPI = (BF16_OUT ? 8 * TJ : 0) + NSCALE;
+    // K-tile S-1 copies: the previous tile's stores (bf16: 4 x TJ x 2 of 16 B;
+    // SwiGLU: 4 x TJ) and this tile's scale loads; other outputs drain at the
+    // tile boundary
+    constexpr int EPI = (BF16_OUT ? 8 * TJ : SWIGLU ? 4 * TJ : 0) + NSCALE;
     __shared__ __attribute__((aligned(1024))) int8_t sw0[STGW], sw1[STGW],
         sw2[S == 4 ? STGW : 16], sw3[S == 4 ? STGW : 16];
     __shared__ __attribute__((aligned(1024))) int8_t sx0[STGX], sx1[STGX],
@@ -755,6 +855,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 
     int m0, n0;
     if (!tile_at(0, m0, n0)) return;
+    if constexpr (SWIGLU) {
+        // the LDS slice of the silu table (written once per device before any
+        // launch that reads it)
+        for (int i = threadIdx.x; i < 2 * kSiluSpanE; i += kThreads) {
+            const int neg = i >= kSiluSpanE;
+            g_silu_lds[i] = silu_tab[(neg << 15) | (i - neg * kSiluSpanE + kSiluLoE)];
+        }
+        __syncthreads();
+    }
     if constexpr (OUT == int(OutKind::GELU_BF16)) {
         // the LDS slice of the GELU table (written by the launch before this
         // one on the same stream)
@@ -776,7 +885,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
             a = sx[min(m0_ + tid, M - 1)];
             b = sw[min(n0_ + tid, N - 1)];
         }
-        if constexpr (OUT != int(OutKind::I32) && HAS_BIAS) c = bias[min(n0_ + tid, N - 1)];
+        if constexpr (OUT != int(OutKind::I32) && HAS_BIAS) {
+            const int n = min(n0_ + tid, N - 1);
+            // SwiGLU: the bias of the interleaved row's source channel
+            c = bias[SWIGLU ? (int)swiglu_src_row(n, N >> 1) : n];
+        }
     };
 
     float sc_x = 0.f, sc_w = 0.f, sc_b = 0.f;
@@ -821,16 +934,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
             issue_half<4, TJ, 1, MM>(cur, nxt, voffw, voffx, nk + S - 1, nk, wave, wl, xl);
         }
         const bool full = m0 + TM <= M && n0 + kTile <= N;
-        if (full)
-            epilogue<OUT, HAS_BIAS, TJ, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
-        else
-            epilogue<OUT, HAS_BIAS, TJ, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+        if constexpr (SWIGLU) {
+            if (full)
+                swiglu_epilogue<HAS_BIAS, TJ, true>(Y, acc, sscale, silu_tab, M, N, m0, n0, wm,
+                                                    wn, l32, g);
+            else
+                swiglu_epilogue<HAS_BIAS, TJ, false>(Y, acc, sscale, silu_tab, M, N, m0, n0, wm,
+                                                     wn, l32, g);
+        } else {
+            if (full)
+                epilogue<OUT, HAS_BIAS, TJ, true>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+            else
+                epilogue<OUT, HAS_BIAS, TJ, false>(Y, acc, sscale, M, N, m0, n0, wm, wn, l32, g);
+        }
 
         if (!more) break;
         // The next tile's waits count exactly EPI operations issued after its
         // first copies.  A partial tile issues fewer stores (and other outputs
         // more), so drain them: every copy issued so far has then landed.
-        if (!BF16_OUT || !full) wait_vmcnt<0>();
+        if (!(BF16_OUT || SWIGLU) || !full) wait_vmcnt<0>();
         m0 = nm0;
         n0 = nn0;
         cur = nxt;
@@ -846,7 +968,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
 template <int OUT, bool HAS_BIAS, int TJ>
 hipError_t launch_tj(const int8_t *qx, const int8_t *qw, const float *sx, const float *sw,
                      const float *bias, void *Y, int64_t M, int64_t N, int64_t K, int cus,
-                     hipStream_t stream)
+                     hipStream_t stream, const float *silu_tab)
 {
     constexpr int TM = 64 * TJ;
     const int tiles_m = (int)((M + TM - 1) / TM);
@@ -859,11 +981,11 @@ hipError_t launch_tj(const int8_t *qx, const int8_t *qw, const float *sx, const 
     if (nk % 4 == 0)
         hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, TJ, 4>), grid, block, 0, stream, qx, qw,
                            sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
-                           wgs_per_xcd);
+                           wgs_per_xcd, silu_tab);
     else
         hipLaunchKernelGGL((gemm_i8_kernel<OUT, HAS_BIAS, TJ, 2>), grid, block, 0, stream, qx, qw,
                            sx, sw, bias, Y, (int)M, (int)N, (int)K, tiles_m, tiles_n, per_xcd,
-                           wgs_per_xcd);
+                           wgs_per_xcd, silu_tab);
     return hipGetLastError();
 }
 
@@ -1179,6 +1301,11 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
         const hipError_t e = launch_gelu_table(&table, stream);
         if (e != hipSuccess) return e;
     }
+    const float *silu_tab = nullptr;
+    if constexpr (OUT == int(OutKind::SWIGLU_BF16)) {
+        const hipError_t e = launch_silu_table(&silu_tab, stream);
+        if (e != hipSuccess) return e;
+    }
     const int cus = device_cu_count();
     const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
     auto rounds = [&](int64_t tiles) { return (double)((tiles + cus - 1) / cus); };
@@ -1194,13 +1321,15 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
     const int64_t m1 = std::min<int64_t>(M, best_a * kTile);
     if (m1 > 0) {
         const hipError_t e =
-            launch_tj<OUT, HAS_BIAS, 4>(qx, qw, sx, sw, bias, Y, m1, N, K, cus, stream);
+            launch_tj<OUT, HAS_BIAS, 4>(qx, qw, sx, sw, bias, Y, m1, N, K, cus, stream, silu_tab);
         if (e != hipSuccess || m1 == M) return e;
     }
     constexpr size_t ysize = OUT == int(OutKind::F32) || OUT == int(OutKind::I32) ? 4 : 2;
+    // row stride of Y in elements (SwiGLU writes N/2 columns)
+    const int64_t ycols = OUT == int(OutKind::SWIGLU_BF16) ? N / 2 : N;
     return launch_tj<OUT, HAS_BIAS, 2>(qx + m1 * K, qw, sx ? sx + m1 : nullptr, sw, bias,
-                                       static_cast<char *>(Y) + (size_t)(m1 * N) * ysize,
-                                       M - m1, N, K, cus, stream);
+                                       static_cast<char *>(Y) + (size_t)(m1 * ycols) * ysize,
+                                       M - m1, N, K, cus, stream, silu_tab);
 }
 
 } // namespace
@@ -1227,6 +1356,9 @@ hipError_t launch_gemm_i8(const int8_t *qx, const int8_t *qw, const float *sx,
     case OutKind::BF16_MM:
         return hb ? launch_t<int(OutKind::BF16_MM), true>(qx, qw, sx, sw, bias, Y, M, N, K, stream)
                   : launch_t<int(OutKind::BF16_MM), false>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
+    case OutKind::SWIGLU_BF16:
+        return hb ? launch_t<int(OutKind::SWIGLU_BF16), true>(qx, qw, sx, sw, bias, Y, M, N, K, stream)
+                  : launch_t<int(OutKind::SWIGLU_BF16), false>(qx, qw, sx, sw, bias, Y, M, N, K, stream);
     }
     return hipErrorInvalidValue;
 }

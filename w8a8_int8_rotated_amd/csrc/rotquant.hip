@@ -41,6 +41,9 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
 
 namespace convrot {
 namespace {
@@ -540,6 +543,105 @@ hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------- SwiGLU ----
+// The activation of the SwiGLU MLP (MiniMax-H3-Rung-Omega README, "Technical
+// Architecture Overview", Floor 1: SwiGLU in front of the rotated, rowwise
+// quantised fc2): fc1 writes [gate | up] as one bf16 row of 2F values and
+// g = bf16(s * up) with s = fp32(silu(gate)), silu(z) = z / (1 + exp(-z))
+// evaluated in fp64 on the bf16 gate and rounded once to fp32, s * up one
+// fp32 multiply.
+//
+// g_silu_f32 holds s for every bf16 gate pattern, written once per device
+// (launch_silu_table).  Kernels read a slice of it from LDS: for each sign the
+// patterns with |z| in [2^-24, 2^8) (biased exponents 103..134, 4096 entries,
+// 16 KiB per sign).  Outside the slice s has a closed form, which the
+// exhaustive test of every pattern checks: z/2 for |z| < 2^-24 (the next term
+// z^2/4 is below half an ulp of z/2), z for z >= 2^8 and -0 for z <= -2^8
+// (exp(-|z|) is far below an ulp there; both hold from |z| >= 128 on).
+// Non-finite gates give unspecified values.
+__device__ __align__(16) float g_silu_f32[65536];
+
+constexpr int kSiluLo = 103 << 7;     // first |z| pattern of the slice
+constexpr int kSiluSpan = 32 << 7;    // patterns per sign
+
+__global__ __launch_bounds__(256) void silu_table_kernel()
+{
+    const uint32_t a = blockIdx.x * 256u + threadIdx.x;
+    const double z = (double)__uint_as_float(a << 16);
+    g_silu_f32[a] = (float)(z / (1.0 + exp(-z)));
+}
+
+// Copy the slice of the table into LDS (every thread of the workgroup takes
+// part; the caller synchronises).
+__device__ __forceinline__ void load_silu_slice(float *sl, const float *__restrict__ tab,
+                                                int nthreads)
+{
+    for (int i = threadIdx.x; i < 2 * kSiluSpan; i += nthreads) {
+        const int neg = i >= kSiluSpan;
+        sl[i] = tab[(neg << 15) | (i - neg * kSiluSpan + kSiluLo)];
+    }
+}
+
+// s = fp32(silu(z)) of the bf16 pattern a (low 16 bits), from the LDS slice or
+// the closed forms outside it; branch-free (the index is clamped into the
+// slice either way).
+__device__ __forceinline__ float silu_of(uint32_t a, const float *sl)
+{
+    const uint32_t mag = a & 0x7fffu, neg = (a >> 15) & 1u;
+    const float z = __uint_as_float(a << 16);
+    const uint32_t off = mag - (uint32_t)kSiluLo;      // wraps below the slice
+    const float t = sl[neg * kSiluSpan + min(off, (uint32_t)kSiluSpan - 1u)];
+    const float out = mag < (uint32_t)kSiluLo ? __fmul_rn(z, 0.5f) : (neg ? -0.0f : z);
+    return off < (uint32_t)kSiluSpan ? t : out;
+}
+
+typedef __bf16 rq_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float rq_f32x2 __attribute__((ext_vector_type(2)));
+
+// Two bf16 gate/up pairs (packed dwords) -> the packed bf16 pair of g.
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t gate2, uint32_t up2, const float *sl)
+{
+    const float g0 = __fmul_rn(silu_of(gate2 & 0xffffu, sl), bf16_lo(up2));
+    const float g1 = __fmul_rn(silu_of(gate2 >> 16, sl), bf16_hi(up2));
+    // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((rq_f32x2){g0, g1}, rq_bf16x2));
+}
+
+// g [M, F] = swiglu of gu [M, 2F], 8 values per thread (16-byte loads of the
+// gate and the up halves, one 16-byte store); grid-stride over M * F / 8.
+__global__ __launch_bounds__(256) void swiglu_apply8_kernel(const uint4 *__restrict__ gu,
+                                                            uint4 *__restrict__ g, int64_t M,
+                                                            int64_t F8)
+{
+    __shared__ float sl[2 * kSiluSpan];
+    load_silu_slice(sl, g_silu_f32, 256);
+    __syncthreads();
+    const int64_t n = M * F8, stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const int64_t m = i / F8, j = i % F8;
+        const uint4 a = gu[m * 2 * F8 + j], u = gu[m * 2 * F8 + F8 + j];
+        uint4 o;
+        o.x = swiglu_pair(a.x, u.x, sl);
+        o.y = swiglu_pair(a.y, u.y, sl);
+        o.z = swiglu_pair(a.z, u.z, sl);
+        o.w = swiglu_pair(a.w, u.w, sl);
+        g[i] = o;
+    }
+}
+
+// s[i] = fp32(silu(a[i])) for n bf16 values, through the same slice and
+// closed forms as every SwiGLU kernel.
+__global__ __launch_bounds__(256) void silu_f32_kernel(const uint16_t *__restrict__ a,
+                                                       float *__restrict__ out, int64_t n)
+{
+    __shared__ float sl[2 * kSiluSpan];
+    load_silu_slice(sl, g_silu_f32, 256);
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride)
+        out[i] = silu_of(a[i], sl);
+}
+
 // Streaming variant for long rows (6144 < K <= 24576): rows are taken in
 // pairs, one per half-wave.  A wave step covers 256 elements of each row of
 // the pair (32 lanes x 8 elements; a Hadamard block of b <= 256 lies inside
@@ -551,16 +653,20 @@ hipError_t launch_stream(const void *src, int64_t M, int64_t K, int64_t ld,
 // persistent workgroup per CU walks pair groups, and each wave loads the raw
 // input of its next group before rotating the current one, so memory and the
 // rotation overlap inside the wave as well as across waves.
-// GELU (bf16 input only): each loaded value u is replaced by bf16(GELU(u))
-// from the 65,536-entry table gtab (one entry per bf16 pattern) before the
-// rotation, so the MLP's intermediate is read once, as u, and g is never
-// written.  The table is copied into LDS (128 KiB) when the workgroup starts.
-template <int IN, int B, int ROT, int SPR, int WPR, int NW, bool GELU = false>
+// ACT = kActGelu (bf16 input only): each loaded value u is replaced by
+// bf16(GELU(u)) from the 65,536-entry table gtab (one entry per bf16 pattern)
+// before the rotation, so the MLP's intermediate is read once, as u, and g is
+// never written.  The table is copied into LDS (128 KiB) when the workgroup
+// starts.
+constexpr int kActNone = 0, kActGelu = 1;
+
+template <int IN, int B, int ROT, int SPR, int WPR, int NW, int ACT = kActNone>
 __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
     const void *__restrict__ src, int64_t M, int K, int64_t ld, float inv_sqrt_b,
-    int8_t *__restrict__ q, float *__restrict__ s, const uint16_t *__restrict__ gtab)
+    int8_t *__restrict__ q, float *__restrict__ s, const void *__restrict__ gtab)
 {
-    static_assert(!GELU || IN == int(InType::BF16), "GELU applies to bf16 input");
+    static_assert(ACT == kActNone || IN == int(InType::BF16), "activations take bf16 input");
+    constexpr bool GELU = ACT == kActGelu;
     __shared__ uint16_t tab[GELU ? 65536 : 2];
     if constexpr (GELU) {
         const uint4 *gt = reinterpret_cast<const uint4 *>(gtab);
@@ -598,23 +704,39 @@ __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
     // the Sylvester sign trick leaves the upper lanes' values negated
     const bool negated = ROT == 0 && (__builtin_popcount(chunk) & 1) != 0;
 
-    // Every memory instruction is unconditional (steps past the row end fall
-    // outside the buffer range: loads read zero, stores are dropped), so the
-    // compiler can count them and wait for the prefetched loads only.
+    // Every memory instruction is unconditional, so the compiler can count
+    // them and wait for the prefetched loads only.  The buffer resources are
+    // wave-uniform (a resource that differs between the half-waves costs a
+    // loop per instruction): loads go through the pair's rows inside M, the
+    // lane's own row reached by its offset, and an element at or past K gets
+    // an offset outside every range, so it reads zero; stores go through the
+    // pair's 16-row block of codes, and a lane whose row is past M stores
+    // outside it (dropped).
+    constexpr uint32_t kOut = 0x7f000000u;       // beyond every range used here
+    const uint32_t lane_row = (uint32_t)(half * ld * ESIZE);
+    auto pair_rsrc = [&](int64_t gi) {
+        const int64_t row0 = (gi * PAIRS + grp) * 2;
+        const int64_t rows = row0 < M ? (M - row0 < 2 ? M - row0 : 2) : 0;
+        return row_rsrc(reinterpret_cast<const char *>(src) + (rows ? row0 : 0) * ld * ESIZE,
+                        (int)(rows * ld * ESIZE));
+    };
+    // byte offset of step t of this lane's row, `skip` elements into the row
+    auto step_off = [&](int t, int skip) -> uint32_t {
+        const int e = (part + WPR * t) * HS + lane_off;
+        return e < K ? lane_row + (uint32_t)((skip + e) * ESIZE) : kOut;
+    };
+
     int raw[SPR][DW];
     auto issue = [&](int64_t gi) {
-        const int64_t row = (gi * PAIRS + grp) * 2 + half;
-        const bool in = row < M;
-        const __amdgpu_buffer_rsrc_t r = row_rsrc(
-            reinterpret_cast<const char *>(src) + (in ? row : 0) * ld * ESIZE, in ? K * ESIZE : 0);
+        const __amdgpu_buffer_rsrc_t r = pair_rsrc(gi);
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
-            const int e = (part + WPR * t) * HS + lane_off;
-            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE, 0, kStreamLoad);
+            const uint32_t o = step_off(t, 0);
+            const v4i a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, kStreamLoad);
 #pragma unroll
             for (int j = 0; j < 4; ++j) raw[t][j] = a[j];
             if constexpr (DW == 8) {
-                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, e * ESIZE + 16, 0, kStreamLoad);
+                const v4i c = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o + 16, 0, kStreamLoad);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) raw[t][4 + j] = c[j];
             }
@@ -687,28 +809,30 @@ __global__ __launch_bounds__(NW * 64) void rotquant_pair_kernel(
         __builtin_amdgcn_raw_buffer_store_b32(
             __float_as_int(__fmul_rn(__fdiv_rn(mx, 127.0f), inv_sqrt_b)), srs,
             (part == 0 && hl == 0 && in) ? (int)(row * 4) : 0x7ffffff0, 0, 0);
+        const int64_t row0 = row - half;
         const __amdgpu_buffer_rsrc_t qb =
-            row_rsrc(q + (in ? (row & ~int64_t(15)) : 0) * (int64_t)K, in ? 16 * K : 0);
-        const int q_off = (int)tiled_offset(row & 15, lane_off, K);
+            row_rsrc(q + (row0 < M ? (row0 & ~int64_t(15)) : 0) * (int64_t)K,
+                     row0 < M ? 16 * K : 0);
+        const uint32_t q_off = in ? (uint32_t)tiled_offset(row & 15, lane_off, K) : kOut;
 #pragma unroll
         for (int t = 0; t < SPR; ++t) {
             const uint2 c = quantise_chunk(v[t], invs);
             // step t spans 4 K-tiles of the row block: 4 KiB
             __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)c.x, (int)c.y}, qb,
-                                                  (part + WPR * t) * 4096 + q_off, 0, 0);
+                                                  (int)((part + WPR * t) * 4096 + q_off), 0, 0);
         }
     }
 }
 
-template <int IN, int B, int ROT, int SPR, int WPR, int NW, bool GELU = false>
+template <int IN, int B, int ROT, int SPR, int WPR, int NW, int ACT = kActNone>
 hipError_t launch_pair(const void *src, int64_t M, int64_t K, int64_t ld,
                          float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream,
-                         const uint16_t *gtab = nullptr)
+                         const void *gtab = nullptr)
 {
     constexpr int rows_per_wg = 2 * (NW / WPR);
     const int64_t groups = (M + rows_per_wg - 1) / rows_per_wg;
     const int64_t grid = std::min<int64_t>(groups, device_cu_count());
-    hipLaunchKernelGGL((rotquant_pair_kernel<IN, B, ROT, SPR, WPR, NW, GELU>),
+    hipLaunchKernelGGL((rotquant_pair_kernel<IN, B, ROT, SPR, WPR, NW, ACT>),
                        dim3((unsigned)grid), dim3(NW * 64), 0, stream, src, M, (int)K, ld,
                        inv_sqrt_b, q, s, gtab);
     return hipGetLastError();
@@ -756,16 +880,37 @@ hipError_t launch_in(const void *src, int64_t M, int64_t K, int64_t ld, int bloc
     }
 }
 
-// The pair kernel's range, with GELU on load (bf16 rows, 6144 < K <= 24576).
-template <int B, int ROT>
-hipError_t launch_gelu_b(const void *src, int64_t M, int64_t K, int64_t ld, float inv_sqrt_b,
-                         int8_t *q, float *s, const uint16_t *gtab, hipStream_t stream)
+// The pair kernel's range, with an activation on load (bf16 rows,
+// 6144 < K <= 24576).
+template <int B, int ROT, int ACT>
+hipError_t launch_act_b(const void *src, int64_t M, int64_t K, int64_t ld, float inv_sqrt_b,
+                        int8_t *q, float *s, const void *gtab, hipStream_t stream)
 {
     constexpr int BF = int(InType::BF16);
     const int64_t hsteps = (K + 255) / 256;
     if (hsteps <= 48)
-        return launch_pair<BF, B, ROT, 6, 8, 16, true>(src, M, K, ld, inv_sqrt_b, q, s, stream, gtab);
-    return launch_pair<BF, B, ROT, 6, 16, 16, true>(src, M, K, ld, inv_sqrt_b, q, s, stream, gtab);
+        return launch_pair<BF, B, ROT, 6, 8, 16, ACT>(src, M, K, ld, inv_sqrt_b, q, s, stream, gtab);
+    return launch_pair<BF, B, ROT, 6, 16, 16, ACT>(src, M, K, ld, inv_sqrt_b, q, s, stream, gtab);
+}
+
+template <int ACT>
+hipError_t launch_act(const void *src, int64_t M, int64_t K, int64_t ld, int block, bool regular,
+                      float inv_sqrt_b, const void *gtab, int8_t *q, float *s,
+                      hipStream_t stream)
+{
+    if (regular) {
+        switch (block) {
+        case 64: return launch_act_b<64, 1, ACT>(src, M, K, ld, inv_sqrt_b, q, s, gtab, stream);
+        case 256: return launch_act_b<256, 1, ACT>(src, M, K, ld, inv_sqrt_b, q, s, gtab, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (block) {
+    case 64: return launch_act_b<64, 0, ACT>(src, M, K, ld, inv_sqrt_b, q, s, gtab, stream);
+    case 128: return launch_act_b<128, 0, ACT>(src, M, K, ld, inv_sqrt_b, q, s, gtab, stream);
+    case 256: return launch_act_b<256, 0, ACT>(src, M, K, ld, inv_sqrt_b, q, s, gtab, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // ---------------------------------------------------------- tile codes ----
@@ -837,6 +982,22 @@ __global__ __launch_bounds__(256) void pad_copy_kernel(const T *__restrict__ src
     }
 }
 
+// --------------------------------------------------- SwiGLU interleave ----
+
+// dst row p of a [2F, rows of ru units U] SwiGLU fc1 weight (or of its
+// per-row scales, one 4-byte unit per row) = src row swiglu_src_row(p, F).
+template <typename U>
+__global__ __launch_bounds__(256) void swiglu_interleave_kernel(const U *__restrict__ src,
+                                                                U *__restrict__ dst, int64_t F,
+                                                                int64_t ru)
+{
+    const int64_t n = 2 * F * ru, stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
+        const int64_t p = i / ru, c = i % ru;
+        dst[i] = src[swiglu_src_row(p, F) * ru + c];
+    }
+}
+
 } // namespace
 
 hipError_t launch_rotquant(const void *src, InType in, int64_t M, int64_t K,
@@ -861,19 +1022,72 @@ hipError_t launch_rotquant_gelu(const void *src, int64_t M, int64_t K, int64_t l
 {
     if (!rotquant_fuses_gelu(K) || !gelu_table) return hipErrorInvalidValue;
     if (M == 0) return hipSuccess;
-    if (regular) {
-        switch (block) {
-        case 64: return launch_gelu_b<64, 1>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
-        case 256: return launch_gelu_b<256, 1>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
-        default: return hipErrorInvalidValue;
-        }
+    return launch_act<kActGelu>(src, M, K, ld, block, regular, inv_sqrt_b, gelu_table, q, s,
+                                stream);
+}
+
+hipError_t launch_silu_table(const float **table, hipStream_t stream)
+{
+    // per device ordinal: the table's address, and whether it has been
+    // written (the scheme of the GELU table: the first call outside a graph
+    // capture fills it and waits once)
+    static std::atomic<const float *> cached[64];
+    static std::atomic<int> filled[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool known = dev >= 0 && dev < 64;
+    const float *p = known ? cached[dev].load(std::memory_order_relaxed) : nullptr;
+    if (!p) {
+        void *a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(g_silu_f32));
+        if (e != hipSuccess) return e;
+        p = static_cast<const float *>(a);
+        if (reinterpret_cast<uintptr_t>(p) & 15) return hipErrorInvalidValue;
+        if (known) cached[dev].store(p, std::memory_order_relaxed);
     }
-    switch (block) {
-    case 64: return launch_gelu_b<64, 0>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
-    case 128: return launch_gelu_b<128, 0>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
-    case 256: return launch_gelu_b<256, 0>(src, M, K, ld, inv_sqrt_b, q, s, gelu_table, stream);
-    default: return hipErrorInvalidValue;
-    }
+    *table = p;
+    if (known && filled[dev].load(std::memory_order_acquire)) return hipSuccess;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(silu_table_kernel, dim3(256), dim3(256), 0, stream);
+    e = hipGetLastError();
+    if (e != hipSuccess || cap != hipStreamCaptureStatusNone || !known) return e;
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return e;
+    filled[dev].store(1, std::memory_order_release);
+    if (std::getenv("CONVROT_LOG") && std::getenv("CONVROT_LOG")[0] == '1')
+        std::fprintf(stderr, "[convrot] silu table written on device %d\n", dev);
+    return hipSuccess;
+}
+
+hipError_t launch_swiglu_bf16(const uint16_t *gu, int64_t M, int64_t F, uint16_t *g,
+                              hipStream_t stream)
+{
+    if (M == 0 || F == 0) return hipSuccess;
+    if (F % 8 != 0 || ((reinterpret_cast<uintptr_t>(gu) | reinterpret_cast<uintptr_t>(g)) & 15))
+        return hipErrorInvalidValue;
+    const float *table = nullptr;
+    const hipError_t e = launch_silu_table(&table, stream);
+    if (e != hipSuccess) return e;
+    const int64_t n = M * (F / 8);
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, (int64_t)device_cu_count() * 4);
+    hipLaunchKernelGGL(swiglu_apply8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4 *>(gu), reinterpret_cast<uint4 *>(g), M,
+                       F / 8);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_f32(const uint16_t *a, int64_t n, float *out, hipStream_t stream)
+{
+    if (n == 0) return hipSuccess;
+    const float *table = nullptr;
+    const hipError_t e = launch_silu_table(&table, stream);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, (int64_t)device_cu_count() * 4);
+    hipLaunchKernelGGL(silu_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, out, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_tile_codes(const int8_t *src, bool transposed, int8_t *dst, int64_t R,
@@ -928,6 +1142,25 @@ hipError_t launch_pad_copy(const void *src, int64_t R, int64_t C, void *dst, int
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_interleave(const void *src, void *dst, int64_t F, int64_t K,
+                                    int elem_bytes, hipStream_t stream)
+{
+    const int64_t rb = K * elem_bytes;
+    if (F == 0) return hipSuccess;
+    if (rb % 4 != 0) return hipErrorInvalidValue;
+    // rows move in 16-byte units, or 4-byte ones (a row of one scale)
+    const int64_t unit = rb % 16 == 0 ? 16 : 4, ru = rb / unit, n = 2 * F * ru;
+    const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 8 * device_cu_count());
+    if (unit == 16)
+        hipLaunchKernelGGL(swiglu_interleave_kernel<uint4>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), F, ru);
+    else
+        hipLaunchKernelGGL(swiglu_interleave_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint32_t *>(src), static_cast<uint32_t *>(dst), F,
+                           ru);
     return hipGetLastError();
 }
 
