@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective INT8 TOPS & % INT8 MFMA peak, ConvRot linear M=38656 K=5376"
-PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_INT8_TOPS = 5033.2      # MI355X dense INT8 MFMA: 256 CUs x 8192 ops/clk x 2.4 GHz (5.0 POP/s)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 RIDGE = PEAK_INT8_TOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # ops per byte
 CSRC = os.path.join(ROOT, "w8a8_int8_rotated_amd", "csrc")
@@ -456,6 +456,19 @@ def main():
         "cpu_baseline": None,
     }
 
+    clk = loaded_clock(dominant, torch, stream)
+    result["loaded_clock"] = clk
+    if clk and dominant.bound == "mfma":
+        # MFMA utilisation at the clock actually held: the INT8 rate of the
+        # launch over what every CU's matrix cores deliver at that clock
+        # (8,192 INT8 ops per clock per CU, the spec peak's rate at 2.4 GHz)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        cap = cus * 8192.0 * clk["gfx_mhz"] * 1e6 / 1e12
+        result["roofline"]["mfma_util_at_loaded_clock"] = round(
+            result["roofline"]["achieved"] / cap, 4)
+        log(f"loaded clock {clk['gfx_mhz']:.0f} MHz during {dominant.name}: "
+            f"{result['roofline']['achieved']:.0f} of {cap:.0f} TOPS at that clock")
+
     if not args.no_ceilings:
         ceil = ceilings(cr, torch, dev, stream, stages, first_rq)
         result["ceilings"] = ceil
@@ -467,13 +480,59 @@ def main():
             r["frac_of_measured_ceiling"] = round(r["achieved"] / ceil[key]["value"], 4)
 
     if w.kind == "lowrank":
-        result["comparison"] = bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream,
-                                                       ms_per_step)
+        result["comparison"] = {
+            "dense_w8a8": dense_comparison(args, w, host, cr, torch, dev, stream, ms_per_step, Y),
+            "bf16_lowrank": bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream,
+                                                    ms_per_step),
+        }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(args, w, host, Y)
 
     print(json.dumps(result), flush=True)
+
+
+def loaded_clock(stage, torch, stream, seconds=0.6):
+    """The shader clock while `stage` runs back to back for about `seconds`:
+    the host enqueues the launches, then reads the current level of the
+    driver's sclk table (pp_dpm_sclk, the entry marked '*') every few
+    milliseconds until they finish; the median of the middle 80% of the
+    readings.  None when the table is not readable."""
+    import glob
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+
+    def read_mhz():
+        try:
+            with open(paths[0]) as f:
+                for ln in f:
+                    if ln.strip().endswith("*"):
+                        return float(re.search(r"(\d+)\s*Mhz", ln, re.I).group(1))
+        except (OSError, AttributeError):
+            return None
+        return None
+
+    n = max(8, int(seconds / max(stage.ms * 1e-3, 1e-5)))
+    done = torch.cuda.Event()
+    torch.cuda.synchronize()
+    for _ in range(n):
+        stage.fn()
+    done.record(stream)
+    samples = []
+    while not done.query():
+        v = read_mhz()
+        if v is not None:
+            samples.append(v)
+        time.sleep(0.003)
+    torch.cuda.synchronize()
+    if len(samples) < 5:
+        return None
+    k = len(samples) // 10
+    mid = sorted(samples[k:len(samples) - k])
+    return {"gfx_mhz": mid[len(mid) // 2], "samples": len(samples), "launches": n,
+            "kernel": stage.name, "source": "pp_dpm_sclk current level, median while the "
+            "kernel runs back to back"}
 
 
 def environment(torch):
@@ -569,6 +628,52 @@ def ceilings(cr, torch, dev, stream, stages, first_rq):
     }
 
 
+def dense_comparison(args, w, host, cr, torch, dev, stream, lowrank_ms, Y_lowrank):
+    """The dense W8A8 linear the low-rank layer approximates: W = B A formed in
+    fp64, stored fp32 and prepared like any weight, run on the same
+    activations and timed the same way outside the step.  Reports its TOPS,
+    the low-rank step's dense-equivalent TOPS (2 M N K over the low-rank
+    time), and both outputs' normwise error against the fp64 product W x on
+    sampled rows."""
+    import numpy as np
+    A64, B64 = host["A"].astype(np.float64), host["B"].astype(np.float64)
+    W64 = B64 @ A64
+    W = W64.astype(np.float32)
+    pw = cr.convrot_linear_prepare_weights(torch.from_numpy(W).to(dev), w.block)
+    X = torch.from_numpy(host["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    Y = torch.empty((w.M, w.N), dtype=Y_lowrank.dtype, device=dev)
+    ws = torch.empty(cr.convrot_linear_workspace_bytes(w.M, w.K, w.N, w.block),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: cr.convrot_linear_forward(X, pw, out=Y, workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        run()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    dense_ops = 2.0 * w.M * w.N * w.K
+    rows = np.sort(np.random.default_rng(99).choice(w.M, 64, replace=False))
+    xf = ((host["x"][rows].astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+    y64 = xf @ W64.T
+    idx = torch.from_numpy(rows).to(dev)
+    to64 = lambda t: t[idx].float().cpu().numpy().astype(np.float64)
+    err = lambda y: float(np.linalg.norm(y - y64) / np.linalg.norm(y64))
+    e_dense, e_lr = err(to64(Y)), err(to64(Y_lowrank))
+    log(f"dense W8A8 comparison (W = B A): {ms:.4f} ms, {dense_ops / ms / 1e9:.1f} TOPS; "
+        f"low-rank step {lowrank_ms:.4f} ms = {dense_ops / lowrank_ms / 1e9:.1f} dense-equivalent "
+        f"TOPS; normwise error vs fp64 W x: dense {e_dense:.4f}, low-rank {e_lr:.4f}")
+    return {"variant": "dense W8A8 linear, W = B A (fp64 product stored fp32), same X",
+            "ms_per_step": round(ms, 5), "tops": round(dense_ops / ms / 1e9, 2),
+            "lowrank_dense_equivalent_tops": round(dense_ops / lowrank_ms / 1e9, 2),
+            "lowrank_speedup": round(ms / lowrank_ms, 3),
+            "normwise_err_vs_fp64": {"dense": round(e_dense, 5), "lowrank": round(e_lr, 5),
+                                     "rows": 64}}
+
+
 def bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream, int8_ms):
     """The same low-rank layer with bf16 factors and no rotation or
     quantisation (the variant where the low-rank linears stay bf16), timed
@@ -601,12 +706,17 @@ def bf16_lowrank_comparison(args, w, host, cr, torch, dev, stream, int8_ms):
 
 
 def cpu_baseline(args, w, host, Y):
-    """The oracle (as it stands) on a bounded, seeded sample of the same rows;
-    its outputs are also compared with the benchmarked GPU outputs."""
+    """The oracle (as it stands) on the host cores, stage by stage: weight
+    preparation (every weight, in full), rotate+quantise of every row, and the
+    whole forward (rotate+quantise, INT32 contraction, epilogue) on a bounded,
+    seeded sample of rows, which also checks the benchmarked GPU outputs on
+    those rows.  For the two small linear workloads the whole forward runs on
+    every row, on all threads and on one."""
     import numpy as np
     import oracle
 
     M, b, x = w.M, w.block, host["x"]
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     if w.kind == "linear":
         qw, sw = oracle.prepare_weights(host["W"], b)
@@ -629,21 +739,43 @@ def cpu_baseline(args, w, host, Y):
         run = lambda rows: oracle.mlp_forward(x[rows], qu, su, qd, sd, b, out=w.out)
         ops_row = 2.0 * w.ffn * (w.K + w.N)
     prep_s = time.perf_counter() - t0
-    rng = np.random.default_rng(1234)
-    probe = np.sort(rng.choice(M, min(M, 16), replace=False))
+    # rotate + quantise of every row of X (the first stage of the forward)
     t0 = time.perf_counter()
-    run(probe)
-    per_row = (time.perf_counter() - t0) / len(probe)
-    n = int(min(M, max(64, args.cpu_seconds / max(per_row, 1e-9))))
-    rows = np.sort(rng.choice(M, n, replace=False))
-    rows[0], rows[-1] = 0, M - 1
-    rows = np.unique(rows)
+    oracle.rotate_quantize(x, b, "bf16")
+    rq_s = time.perf_counter() - t0
+    rq_gbs = (3.0 * M * w.K + 4.0 * M) / rq_s / 1e9
+
+    rng = np.random.default_rng(1234)
+    full = w.name in ("tiny", "linear_4096")
+    if full:
+        rows = np.arange(M)
+    else:
+        probe = np.sort(rng.choice(M, min(M, 16), replace=False))
+        t0 = time.perf_counter()
+        run(probe)
+        per_row = (time.perf_counter() - t0) / len(probe)
+        n = int(min(M, max(64, args.cpu_seconds / max(per_row, 1e-9))))
+        rows = np.sort(rng.choice(M, n, replace=False))
+        rows[0], rows[-1] = 0, M - 1
+        rows = np.unique(rows)
     t0 = time.perf_counter()
     y_ref = run(rows)
     dt = time.perf_counter() - t0
     cpu_tops = ops_row * len(rows) / dt / 1e12
-    log(f"oracle: {len(rows)} rows in {dt:.2f}s = {cpu_tops:.4f} TOPS on "
-        f"{oracle.num_threads()} threads (weight prep {prep_s:.1f}s, not timed)")
+    one = None
+    if full:
+        oracle.set_num_threads(1)
+        try:
+            t0 = time.perf_counter()
+            run(rows)
+            dt1 = time.perf_counter() - t0
+        finally:
+            oracle.set_num_threads(threads)
+        one = {"seconds": round(dt1, 2), "value": round(ops_row * len(rows) / dt1 / 1e12, 5),
+               "unit": "TOPS", "cores": 1}
+    log(f"oracle: weight prep {prep_s:.1f}s; rotate+quantise of all {M} rows {rq_s:.2f}s "
+        f"({rq_gbs:.2f} GB/s); forward on {len(rows)} rows {dt:.2f}s = {cpu_tops:.4f} TOPS on "
+        f"{threads} threads" + (f", {one['value']:.4f} TOPS on 1 thread" if one else ""))
 
     import torch
     yg = Y[torch.from_numpy(rows).to(Y.device)].cpu()
@@ -656,17 +788,27 @@ def cpu_baseline(args, w, host, Y):
         a, r = yg.astype(np.float64), y_ref.astype(np.float64)
     err = float(np.max(np.abs(a - r)) / max(np.max(np.abs(r)), 1e-30))
     mism = int(np.count_nonzero(yg != y_ref))
+    what = {"linear": "", "lowrank": ", both factors and the requantised h",
+            "mlp": ", GELU", "swiglu": ", SwiGLU"}[w.kind]
     base = {
         "value": round(cpu_tops, 5),
         "unit": "TOPS",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(rows)} of {M} rows (seeded), every projection over its full width "
-                  f"and depth: rotate+quantise of those rows, INT32 contraction and epilogue"
-                  f"{', GELU' if w.kind == 'mlp' else ', SwiGLU' if w.kind == 'swiglu' else ''}"
-                  f"; weight preparation excluded",
+        "sample": (f"{'all' if full else len(rows)} of {M} rows"
+                   f"{'' if full else ' (seeded)'}, every projection over its full width and "
+                   f"depth: rotate+quantise of those rows, INT32 contraction and epilogue{what}"),
         "seconds": round(dt, 2),
+        "stages": {
+            "prepare_weights": {"seconds": round(prep_s, 2), "rows": "every weight row"},
+            "rotate_quantize": {"seconds": round(rq_s, 2), "rows": M,
+                                "value": round(rq_gbs, 3), "unit": "GB/s"},
+            "forward": {"seconds": round(dt, 2), "rows": int(len(rows)),
+                        "value": round(cpu_tops, 5), "unit": "TOPS"},
+        },
     }
+    if one:
+        base["single_thread"] = one
     parity = {"rows": int(len(rows)), "normwise_err": err, "mismatches": mism,
               "tolerance": 1e-3 if w.out == "bf16" else 1e-5}
     return base, parity

@@ -78,6 +78,13 @@
 /* Threads an OpenMP region of this library uses (for reporting). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Set the threads of later OpenMP regions (n >= 1; for timing on one core). */
+void oracle_set_num_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
 /* ------------------------------------------------------------------ */
 /* bf16 <-> fp32                                                       */
 /* ------------------------------------------------------------------ */

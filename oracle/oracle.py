@@ -42,6 +42,7 @@ def open_library(path):
     lib = ctypes.CDLL(path)
     sig = {
         "oracle_num_threads": (_c_int, []),
+        "oracle_set_num_threads": (None, [_c_int]),
         "oracle_bf16_to_f32": (ctypes.c_float, [ctypes.c_uint16]),
         "oracle_f32_to_bf16": (ctypes.c_uint16, [ctypes.c_float]),
         "oracle_fwht_f32": (_c_int, [_c_p, _c_i64, _c_int]),
@@ -152,6 +153,11 @@ def f32_to_bf16(x) -> np.ndarray:
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel regions use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later parallel regions (timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def inv_sqrt_b(b: int) -> np.float32:
@@ -423,7 +429,7 @@ def lowrank_bf16_forward(X_bf16, A_bf16, B_bf16, bias=None, return_h: bool = Fal
 
 
 __all__ = [
-    "num_threads", "bf16_to_f32", "f32_to_bf16", "inv_sqrt_b", "fwht", "rowquant",
+    "num_threads", "set_num_threads", "bf16_to_f32", "f32_to_bf16", "inv_sqrt_b", "fwht", "rowquant",
     "rotate_quantize", "prepare_weights", "gemm_i32", "dequant",
     "linear_forward", "lowrank_forward", "gelu_f64", "gelu_bf16", "mlp_forward",
     "lowrank_bf16_forward", "silu_f64", "silu_f32", "swiglu_bf16", "swiglu_mlp_forward",

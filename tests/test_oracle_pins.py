@@ -497,6 +497,36 @@ def test_lowrank_is_two_chained_linears_with_bias():
         assert not np.array_equal(y, y_nb)
 
 
+def test_lowrank_vs_dense_error_report():
+    """The comparison the low-rank workload names: the W8A8 low-rank chain
+    (A [r, K], B [N, r]) against the dense W8A8 linear with W = B A (formed in
+    fp64, stored fp32, prepared like any weight), both against the fp64
+    product W x on the same rows.  The dense path stays inside its
+    closed-form bound; both normwise errors are reported and stay at the
+    scale of INT8 quantisation (a few percent), the chain's larger by the
+    requantisation of h."""
+    b = 128
+    w = wl.scaled("lowrank_38656", M=24, K=1024, N=384, rank=256)
+    x = w.activations()
+    A, B = w.weight("w"), w.weight("w2")
+    W = (B.astype(np.float64) @ A.astype(np.float64)).astype(np.float32)
+    qa, sa = oracle.prepare_weights(A, b)
+    qb, sb = oracle.prepare_weights(B, b)
+    qw, sw = oracle.prepare_weights(W, b)
+    y_lr = oracle.lowrank_forward(x, qa, sa, qb, sb, b, out="f32").astype(np.float64)
+    y_d = oracle.linear_forward(x, qw, sw, b, out="f32").astype(np.float64)
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    y64 = xf @ W.astype(np.float64).T
+    _, sx = oracle.rotate_quantize(x, b, "bf16")
+    bound = _bound_linear(xf, W.astype(np.float64), b, sx, sw)
+    assert np.all(np.abs(y_d - y64) <= bound + np.abs(y64) * 2.0 ** -22)
+    norm = lambda e: float(np.linalg.norm(e) / np.linalg.norm(y64))
+    e_d, e_lr, e_between = norm(y_d - y64), norm(y_lr - y64), norm(y_lr - y_d)
+    print(f"[report] normwise error vs fp64 W x: dense {e_d:.4f}, low-rank {e_lr:.4f}; "
+          f"low-rank vs dense {e_between:.4f}")
+    assert e_d < 0.03 and e_lr < 0.05 and e_d < e_lr
+
+
 def test_lowrank_rejects_bad_rank():
     q = np.zeros((100, 128), np.int8)
     s = np.ones(100, np.float32)
