@@ -31,7 +31,7 @@ def _x(M, K, seed=0, outliers=0, gain=1.0, dist="normal"):
 @pytest.mark.parametrize("b", [64, 128, 256])
 @pytest.mark.parametrize("M,K", [(1, 512), (37, 512), (300, 5376), (5, 21504), (9, 1024),
                                  (3, 2560), (2, 65536), (130, 768), (4, 30720), (33, 24576),
-                                 (7, 8192)])
+                                 (7, 8192), (5, 3328), (17, 4096), (3, 5504), (11, 6144)])
 def test_rotquant_codes_bitexact(cr, b, M, K):
     if K % b:
         pytest.skip("K not a multiple of b")

@@ -839,13 +839,15 @@ hipError_t launch_pair(const void *src, int64_t M, int64_t K, int64_t ld,
 }
 
 // Rows of up to 4 steps (2048 elements) are held by one wave, several rows
-// per wave when they are short.  Rows of up to 12 steps go to the streaming
-// kernel, one row over 2 waves of 6 steps, 16 waves per CU (at K = 5376 its
-// K-tiled stores cost nothing: 0.117 ms, as row-major codes).  Rows up to
-// 24576 elements go in pairs to the pair kernel: 4..16 waves per pair of at
-// most 6 steps of 256 elements (at K = 21504 it takes 0.200 ms where one row
-// per wave took 0.244 ms).  Longer rows go to the one-shot kernel with 16
-// waves of up to 8 steps of 512 elements (K <= 65536).
+// per wave when they are short.  Rows of up to 6 steps go to the streaming
+// kernel, one row over 2 waves of up to 6 steps, 16 waves per CU.  Longer
+// rows up to 24576 elements go in pairs to the pair kernel: rows of at most
+// 21 steps of 256 elements over 3 waves of 7 steps (12 waves per CU; at
+// K = 5376 rotate+quantise of 38656 rows takes 99.7 us where the streaming
+// kernel took 107.4 us, back to back on one box), up to 24 steps over 4
+// waves of 6, then 8 or 16 waves of 6 (at K = 21504 it takes 0.200 ms where
+// one row per wave took 0.244 ms).  Longer rows go to the one-shot kernel
+// with 16 waves of up to 8 steps of 512 elements (K <= 65536).
 template <int IN, int B, int ROT>
 hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
                     float inv_sqrt_b, int8_t *q, float *s, hipStream_t stream)
@@ -855,7 +857,9 @@ hipError_t launch_b(const void *src, int64_t M, int64_t K, int64_t ld,
     if (steps <= 1) return launch_cfg<IN, B, ROT, 1, 8, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 2) return launch_cfg<IN, B, ROT, 2, 4, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (steps <= 4) return launch_cfg<IN, B, ROT, 4, 2, 1, 4>(src, M, K, ld, inv_sqrt_b, q, s, stream);
-    if (steps <= 12) return launch_stream<IN, B, ROT, 6, 2, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (steps <= 6) return launch_stream<IN, B, ROT, 6, 2, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (hsteps <= 21) return launch_pair<IN, B, ROT, 7, 3, 12>(src, M, K, ld, inv_sqrt_b, q, s, stream);
+    if (hsteps <= 24) return launch_pair<IN, B, ROT, 6, 4, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (hsteps <= 48) return launch_pair<IN, B, ROT, 6, 8, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     if (hsteps <= 96) return launch_pair<IN, B, ROT, 6, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
     return launch_cfg<IN, B, ROT, 8, 1, 16, 16>(src, M, K, ld, inv_sqrt_b, q, s, stream);
