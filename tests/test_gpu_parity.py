@@ -273,6 +273,44 @@ def test_linear_4096_config_full(cr):
                           oracle.linear_forward(x[rows], qw, sw, w.block, bias=bias, out="bf16"))
 
 
+@pytest.mark.parametrize("M,K,N,with_bias", [(4000, 1536, 9008, True), (5000, 2048, 4112, False),
+                                              (3000, 6144, 7168, True)])
+def test_linear_many_tiles_per_workgroup(cr, M, K, N, with_bias):
+    """More output tiles than workgroups, full and partial tiles mixed, K of at
+    least 24 K-tiles: a full tile that is not its workgroup's last is stored
+    while the next tile computes.  Every column of rows sampled at every
+    32-row position of every m-tile against the oracle, the whole output
+    against the forward of row chunks too small to give a workgroup two tiles,
+    and a canary band around Y."""
+    announce(f"many tiles per workgroup M={M} K={K} N={N} bias={with_bias}")
+    w = wl.Workload("mt", "linear", M=M, K=K, N=N, block=128, out="bf16", x_dist="student_t4",
+                    outlier_frac=0.01, outlier_gain=20, bias_std=0.05 if with_bias else None,
+                    seed=M + K + N)
+    x, W, bias = w.activations(), w.weight(), w.bias()
+    pw, qw, sw = _prepare_pair(cr, W, 128)
+    X = to_dev_bf16(x)
+    pad = 8192
+    buf = torch.full((pad + M * N + pad,), -7, dtype=torch.int16, device="cuda")
+    y = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    cr.convrot_linear_forward(X, pw, bias=None if bias is None else to_dev(bias), out=y)
+    torch.cuda.synchronize()
+    b = host(buf)
+    assert (b[:pad] == -7).all() and (b[pad + M * N:] == -7).all()
+    yb = bf16_bits(y)
+    rows = sorted({min(M - 1, t + o) for t in range(0, M, 256)
+                   for o in (3, 45, 70, 101, 140, 166, 203, 255)} | {M - 1})
+    rows = np.array(rows, dtype=np.int64)
+    y_ref = oracle.linear_forward(x[rows], qw, sw, 128, bias=bias, out="bf16")
+    assert assert_output_parity(yb[rows], y_ref, "bf16", "many tiles, sampled rows") == 0
+    # rows are independent: chunks of 512 rows make at most 2 x ceil(N/256)
+    # tiles, fewer than the workgroups, so each workgroup stores at once
+    for a in range(0, M, 512):
+        e = min(M, a + 512)
+        yc = cr.convrot_linear_forward(X[a:e].contiguous(), pw,
+                                       bias=None if bias is None else to_dev(bias))
+        assert np.array_equal(bf16_bits(yc), yb[a:e]), f"rows {a}:{e}"
+
+
 def test_row_chunk_invariance(cr):
     """forward(X[a:b]) equals forward(X)[a:b] bit for bit (rows independent)."""
     announce("row chunk invariance")
