@@ -1,12 +1,12 @@
 """Summarise rocprofv3 CSV output into the short text files kept in profiles/.
 
-    python -m w8a8_int8_rotated_amd.rocprof_summary stats <run_kernel_stats.csv> \\
+    python rocprof_summary.py stats <run_kernel_stats.csv> \\
         --command "<rocprofv3 command>" --workload qkv_38656 -o profiles/X.md
-    python -m w8a8_int8_rotated_amd.rocprof_summary traffic \\
+    python rocprof_summary.py traffic \\
         --fetch <fetch run_counter_collection.csv> --write <write ...csv> \\
         --copy-bytes 536870912 --kernel gemm_i8_kernel --source <kernel .hip> \\
         --command-fetch "..." --command-write "..." -o profiles/Y.md
-    python -m w8a8_int8_rotated_amd.rocprof_summary counters <run_counter_collection.csv> ... \\
+    python rocprof_summary.py counters <run_counter_collection.csv> ... \\
         --kernel gemm_i8_kernel --command "..." --command "..." -o profiles/Z.md
 
 `traffic` scales each counter by what it reads for the plain device copy of

@@ -30,7 +30,7 @@ def _summary(tmp_path, fetch_rows, write_rows, copy_bytes=512 << 20):
     fetch, write, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.md"
     _csv(fetch, "FETCH_SIZE", fetch_rows)
     _csv(write, "WRITE_SIZE", write_rows)
-    r = subprocess.run([sys.executable, "-m", "w8a8_int8_rotated_amd.rocprof_summary", "traffic",
+    r = subprocess.run([sys.executable, "rocprof_summary.py", "traffic",
                         "--fetch", str(fetch), "--write", str(write),
                         "--copy-bytes", str(copy_bytes), "--kernel", "gemm_i8_kernel",
                         "--source", str(src), "--workload", "test",
@@ -73,7 +73,7 @@ def test_traffic_without_a_matching_kernel_fails(tmp_path):
     src.write_text("x")
     _csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
     _csv(tmp_path / "w.csv", "WRITE_SIZE", write)
-    r = subprocess.run([sys.executable, "-m", "w8a8_int8_rotated_amd.rocprof_summary", "traffic",
+    r = subprocess.run([sys.executable, "rocprof_summary.py", "traffic",
                         "--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
                         "--copy-bytes", "1", "--kernel", "gemm_i8_kernel", "--source", str(src),
                         "--workload", "t", "--command-fetch", "a", "--command-write", "b"],
