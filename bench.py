@@ -750,10 +750,18 @@ def cpu_baseline(args, w, host, Y):
     if full:
         rows = np.arange(M)
     else:
-        probe = np.sort(rng.choice(M, min(M, 16), replace=False))
-        t0 = time.perf_counter()
-        run(probe)
-        per_row = (time.perf_counter() - t0) / len(probe)
+        # the time per row, from probes large enough that a call's fixed cost
+        # (threads, intermediates) does not dominate
+        k = 16
+        while True:
+            probe = np.sort(rng.choice(M, min(M, k), replace=False))
+            t0 = time.perf_counter()
+            run(probe)
+            dt_probe = time.perf_counter() - t0
+            if dt_probe >= 0.25 or k >= M:
+                break
+            k *= 4
+        per_row = dt_probe / len(probe)
         n = int(min(M, max(64, args.cpu_seconds / max(per_row, 1e-9))))
         rows = np.sort(rng.choice(M, n, replace=False))
         rows[0], rows[-1] = 0, M - 1

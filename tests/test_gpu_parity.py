@@ -448,6 +448,11 @@ def test_lowrank_rank_padding(cr, r, block):
     (1000, 640, 512, 64),       # b = 64: two rotation blocks per wave, S = 2 stages
     (256, 512, 128, 128),       # one wave active
     (1, 256, 384, 128),         # a single token
+    (520, 768, 256, 128),       # 12, 24 and 36 K-tiles
+    (1000, 1536, 512, 64),
+    (300, 2304, 128, 128),
+    (1, 768, 384, 128),
+    (200, 384, 512, 128),       # 6 K-tiles, 2 stages
 ])
 def test_lowrank_factor1_fused(cr, M, K, r, block):
     """The fused factor-1 kernel's codes and row scales equal the oracle's
@@ -459,13 +464,17 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-@pytest.mark.parametrize("shape", ["one_round", "split_tail"])
-def test_lowrank_factor1_tile_plans(cr, shape):
-    """128-token tiles only (the last round fills more than half the CUs), and
-    whole rounds of 128-token tiles followed by a launch of 64-token tiles."""
+@pytest.mark.parametrize("K", [256, 768])
+@pytest.mark.parametrize("shape", ["one_round", "split_tail", "three_rounds"])
+def test_lowrank_factor1_tile_plans(cr, shape, K):
+    """128-token tiles only (the last round fills more than half the CUs),
+    whole rounds of 128-token tiles followed by a launch of 64-token tiles,
+    and three rounds (every workgroup walks three tiles, so the copies of a
+    tile's first K-tiles are issued during the one before) plus the tail."""
     cus = _cus()
-    M = cus * 64 + 100 if shape == "one_round" else cus * 128 + 300
-    _check_factor1(cr, M, 256, 512, 128)
+    M = {"one_round": cus * 64 + 100, "split_tail": cus * 128 + 300,
+         "three_rounds": 3 * cus * 128 + 300}[shape]
+    _check_factor1(cr, M, K, 512, 128)
 
 
 def _check_factor1(cr, M, K, r, block):
