@@ -22,7 +22,7 @@ which also checks the benchmarked outputs on those rows; and ``ceilings``,
 the INT8 MFMA rate and the streaming HBM rate measured with the library's
 probes, against which ``frac_of_measured_ceiling`` is given.
 
-    python bench.py [--steps 20] [--warmup 5] [--workload qkv_38656]
+    python bench.py [--steps 20] [--warmup W] [--workload qkv_38656]
 """
 from __future__ import annotations
 
@@ -54,7 +54,12 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps before the timed ones (default: as many as take "
+                        "--warmup-seconds, at least 5)")
+    p.add_argument("--warmup-seconds", type=float, default=0.5,
+                   help="GPU time of the default warm-up: the shader clock settles over the "
+                        "first tenths of a second of sustained load")
     p.add_argument("--workload", default="qkv_38656")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
@@ -68,6 +73,26 @@ def parse():
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run a plain device copy of this size first (counter calibration)")
     return p.parse_args()
+
+
+def warmup_steps(args, step, torch):
+    """The untimed steps: --warmup of them, or by default as many as take
+    --warmup-seconds of GPU time (at least 5); the count is what the JSON
+    line reports as warmup."""
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(5):
+            step()
+        n += 5
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= args.warmup_seconds:
+            break
+    args.warmup = n
 
 
 def source_sha(path):
@@ -341,9 +366,7 @@ def main():
     stream = torch.cuda.current_stream()
     log(f"{w.name}: inputs generated and weights prepared in {time.time() - t0:.1f}s")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup_steps(args, step, torch)
     if args.graph:
         # the step recorded once into a HIP graph and replayed: one launch per
         # step instead of one per kernel (the calls allocate, synchronise and
@@ -362,7 +385,7 @@ def main():
             step()
         torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` forward calls, an event after each ----
+    # ---- timed region: exactly `steps` forward calls between two events ----
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     scratch = (torch.empty(args.evict_mib << 20, dtype=torch.uint8, device=dev)
                if args.evict_mib else None)
@@ -372,9 +395,20 @@ def main():
         evs[0].record(stream)
         for i in range(args.steps):
             step()
-            evs[i + 1].record(stream)
+        evs[-1].record(stream)
         torch.cuda.synchronize()
-        per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+        total_ms = evs[0].elapsed_time(evs[-1])
+        wall = time.perf_counter() - wall0
+        # per-step spread from a second pass with an event after each step (an
+        # event between steps leaves the GPU idle for a few microseconds, so
+        # the figure above has none inside it)
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        pe[0].record(stream)
+        for i in range(args.steps):
+            step()
+            pe[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = [pe[i].elapsed_time(pe[i + 1]) for i in range(args.steps)]
     else:
         # cold caches: a scratch write evicts the last-level cache before
         # each step, outside that step's events
@@ -386,12 +420,15 @@ def main():
             ends[i].record(stream)
         torch.cuda.synchronize()
         per_step = [evs[i].elapsed_time(ends[i]) for i in range(args.steps)]
-    wall = time.perf_counter() - wall0
-    ms_per_step = sum(per_step) / args.steps
+        total_ms = sum(per_step)
+        wall = time.perf_counter() - wall0
+    ms_per_step = total_ms / args.steps
     srt = sorted(per_step)
     step_stats = {"median": round(srt[len(srt) // 2], 5), "min": round(srt[0], 5),
                   "p90": round(srt[min(len(srt) - 1, int(0.9 * len(srt)))], 5),
-                  "cold_caches": scratch is not None}
+                  "cold_caches": scratch is not None,
+                  "source": ("an event around each step, scratch write outside" if scratch is not None
+                             else "a second pass of the same steps, an event after each")}
     tops = ops / (ms_per_step * 1e-3) / 1e12
     log(f"forward: {ms_per_step:.4f} ms/step, {tops:.1f} TOPS (wall {wall:.3f}s)")
 
