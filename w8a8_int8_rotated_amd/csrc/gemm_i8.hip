@@ -55,7 +55,9 @@
 //  - the low-rank factor 1 with the rotation and requantisation of its
 //    output in the epilogue (lowrank_f1_kernel);
 //  - the bf16 GELU table of the MLP's up projection, whose epilogue reads the
-//    slice with |u| in [2^-31, 2^9) from LDS (20 KiB beside the stages).
+//    slice with |u| in [2^-31, 2^9) from LDS (20 KiB beside the stages);
+//  - the SwiGLU fc1 epilogue (OutKind::SWIGLU_BF16), reading the fp32 silu
+//    table's slice with |gate| in [2^-15, 2^8) from LDS (23 KiB).
 #include "common.hpp"
 
 #include <algorithm>
@@ -865,8 +867,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(
         __syncthreads();
     }
     if constexpr (OUT == int(OutKind::GELU_BF16)) {
-        // the LDS slice of the GELU table (written by the launch before this
-        // one on the same stream)
+        // the LDS slice of the GELU table (written once per device before
+        // any launch that reads it)
         for (int i = threadIdx.x; i < 2 * kGeluSpan; i += kThreads) {
             const int neg = i >= kGeluSpan;
             g_gelu_lds[i] = g_gelu_bf16[(neg << 15) | (i - neg * kGeluSpan + kGeluLo)];
