@@ -453,6 +453,21 @@ def main():
         log(f"{st.name}: {st.ms:.4f} ms, {r['achieved']} {r['unit']} ({100 * r['frac']:.1f}%)")
     dominant = max(stages, key=lambda s: s.ms)
     first_rq = next(s for s in stages if s.kernel == "rotquant")
+    # the same rotquant launched back to back on its own: in the step it runs
+    # right after a GEMM whose output's dirty lines are still being written
+    # back from the last-level cache, which takes HBM bandwidth from it
+    for _ in range(3):
+        first_rq.fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        first_rq.fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rq_alone_ms = e0.elapsed_time(e1) / args.steps
+    log(f"{first_rq.name} back to back on its own: {rq_alone_ms:.4f} ms, "
+        f"{first_rq.bytes / (rq_alone_ms * 1e-3) / 1e9:.1f} GB/s")
 
     cfg = {"workload": w.name, "M": w.M, "K": w.K, "N": w.N, "block": w.block,
            "activations": "bf16 Student-t(4)" if w.x_dist == "student_t4" else "bf16 normal",
@@ -488,7 +503,11 @@ def main():
         "step_ms": step_stats,
         "launch": "hipGraph replay" if args.graph else "eager",
         "roofline": dominant.roofline(w.name),
-        "roofline_rotquant": first_rq.roofline(w.name),
+        "roofline_rotquant": dict(first_rq.roofline(w.name), back_to_back_alone={
+            "avg_launch_ms": round(rq_alone_ms, 5),
+            "achieved": round(first_rq.bytes / (rq_alone_ms * 1e-3) / 1e9, 2),
+            "frac": round(first_rq.bytes / (rq_alone_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "note": "not after a GEMM: no write-back of its output competes for HBM"}),
         "kernels": [s.roofline(w.name) for s in stages],
         "cpu_baseline": None,
     }
