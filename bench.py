@@ -66,13 +66,28 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="time replays of the step captured in a HIP graph")
-    p.add_argument("--evict-mib", type=int, default=0,
-                   help="write this many MiB of scratch before each timed step (cold caches)")
+    p.add_argument("--evict-mib", type=int, default=None,
+                   help="write this many MiB of scratch before each timed step (cold caches; "
+                        "default 512 when the step's working set is under 512 MiB, so the 256 MB "
+                        "last-level cache cannot hold it from one step to the next, else 0)")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the measured MFMA and HBM ceilings")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run a plain device copy of this size first (counter calibration)")
     return p.parse_args()
+
+
+def working_set_bytes(w):
+    """Bytes a step touches: the bf16 input, every code matrix and weight,
+    every intermediate and the output."""
+    ob = 4 if w.out == "f32" else 2
+    lin = lambda M, K, N, o: 2 * M * K + M * K + N * K + o * M * N
+    if w.kind == "lowrank":
+        return lin(w.M, w.K, w.rank, 2) + lin(w.M, w.rank, w.N, ob) - 2 * w.M * w.rank
+    if w.kind in ("mlp", "swiglu"):
+        up = 2 * w.ffn if w.kind == "swiglu" else w.ffn
+        return lin(w.M, w.K, up, 2) + lin(w.M, w.ffn, w.N, ob)
+    return lin(w.M, w.K, w.N, ob)
 
 
 def warmup_steps(args, step, torch):
@@ -366,6 +381,8 @@ def main():
     stream = torch.cuda.current_stream()
     log(f"{w.name}: inputs generated and weights prepared in {time.time() - t0:.1f}s")
 
+    if args.evict_mib is None:
+        args.evict_mib = 512 if working_set_bytes(w) < (512 << 20) else 0
     warmup_steps(args, step, torch)
     if args.graph:
         # the step recorded once into a HIP graph and replayed: one launch per
