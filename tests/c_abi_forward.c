@@ -7,7 +7,10 @@
  * before anything is launched.  Then it prepares low-rank pairs whose rank
  * needs padding (lowrank_convrot_prepare_weights) and runs the low-rank
  * forward with bias: outputs bit for bit against the oracle's chain on the
- * unpadded factors when b divides r, on zero-padded factors otherwise.
+ * unpadded factors when b divides r, on zero-padded factors otherwise.  Last,
+ * the SwiGLU MLP (fc1 prepared interleaved, fc2 with its own block, biases on
+ * both), bit for bit against the oracle's chain, after checking that a plain
+ * forward refuses the interleaved fc1 weight.
  *
  * Test infrastructure: tests/test_c_abi.py builds it with gcc and runs it.
  * Exit status 0 = every check passed.
@@ -31,6 +34,11 @@ int oracle_lowrank_forward(const uint16_t *X, int64_t M, int64_t K, int b, const
                            const float *sa, int64_t r, const int8_t *qb, const float *sb,
                            int64_t N, const float *bias, int out_dtype, void *out,
                            uint16_t *h_out);
+int oracle_swiglu_mlp_forward_rot(const uint16_t *X, int64_t M, int64_t K, int b_up,
+                                  int b_down, int rot, const int8_t *qgu, const float *sgu,
+                                  int64_t F, const float *bias_gu, const int8_t *qd,
+                                  const float *sd, int64_t N, const float *bias_down,
+                                  int out_dtype, void *out, uint16_t *gu_out, uint16_t *g_out);
 
 #define HIP_OK(x)                                                                  \
     do {                                                                           \
@@ -139,6 +147,82 @@ static int64_t lowrank_case(const uint16_t *X, const void *dX, int64_t M, int64_
     return bad;
 }
 
+/* The SwiGLU MLP: fc1 W_gu [2F, K] (gate rows, then up rows) prepared by
+ * convrot_swiglu_prepare_weights with block b_up, fc2 W_down [N, F] with its
+ * own block b_down, biases on both; returns the number of fp32 outputs that
+ * differ from the oracle (or a negative code on a failed call). */
+static int64_t swiglu_case(const uint16_t *X, const void *dX, int64_t M, int64_t K, int64_t F,
+                           int64_t N, int b_up, int b_down, uint64_t *seed)
+{
+    float *Wgu = malloc(sizeof(float) * 2 * F * K), *Wd = malloc(sizeof(float) * N * F);
+    float *bgu = malloc(sizeof(float) * 2 * F), *bd = malloc(sizeof(float) * N);
+    float *Y = malloc(sizeof(float) * M * N), *Yref = malloc(sizeof(float) * M * N);
+    float *sgu = malloc(sizeof(float) * 2 * F), *sd = malloc(sizeof(float) * N);
+    int8_t *qgu = malloc((size_t)(2 * F * K)), *qd = malloc((size_t)(N * F));
+    if (!Wgu || !Wd || !bgu || !bd || !Y || !Yref || !sgu || !sd || !qgu || !qd) return -4;
+    for (int64_t i = 0; i < 2 * F * K; ++i) Wgu[i] = 0.05f * uniform(seed);
+    for (int64_t i = 0; i < N * F; ++i) Wd[i] = 0.05f * uniform(seed);
+    for (int64_t i = 0; i < 2 * F; ++i) bgu[i] = 0.5f * uniform(seed);
+    for (int64_t i = 0; i < N; ++i) bd[i] = 0.5f * uniform(seed);
+
+    void *dWgu, *dWd, *dcgu, *dsgu, *dcd, *dsd, *dbgu, *dbd, *dY, *dwp, *dwd = NULL, *dws;
+    const size_t cgu = convrot_weights_packed_bytes(2 * F, K, b_up);
+    const size_t cd = convrot_weights_packed_bytes(N, F, b_down);
+    const size_t wp = convrot_swiglu_prepare_workspace_bytes(F, K, b_up, CONVROT_F32);
+    const size_t wd = convrot_prepare_workspace_bytes(N, F, b_down, CONVROT_F32, CONVROT_OUT_MAJOR);
+    const size_t wf = convrot_swiglu_mlp_workspace_bytes(M, K, F, N, b_up, b_down);
+    if (!cgu || !cd || !wp || !wf) return -5;
+    if (hipMalloc(&dWgu, sizeof(float) * 2 * F * K) || hipMalloc(&dWd, sizeof(float) * N * F) ||
+        hipMalloc(&dcgu, cgu) || hipMalloc(&dsgu, 8 * F) || hipMalloc(&dcd, cd) ||
+        hipMalloc(&dsd, 4 * N) || hipMalloc(&dbgu, 8 * F) || hipMalloc(&dbd, 4 * N) ||
+        hipMalloc(&dY, 4 * M * N) || hipMalloc(&dwp, wp) || (wd && hipMalloc(&dwd, wd)) ||
+        hipMalloc(&dws, wf))
+        return -2;
+    if (hipMemcpy(dWgu, Wgu, sizeof(float) * 2 * F * K, hipMemcpyHostToDevice) ||
+        hipMemcpy(dWd, Wd, sizeof(float) * N * F, hipMemcpyHostToDevice) ||
+        hipMemcpy(dbgu, bgu, 8 * F, hipMemcpyHostToDevice) ||
+        hipMemcpy(dbd, bd, 4 * N, hipMemcpyHostToDevice))
+        return -2;
+    convrot_weights wgu, wdn;
+    memset(&wgu, 0, sizeof wgu);
+    memset(&wdn, 0, sizeof wdn);
+    wgu.codes = (int8_t *)dcgu; wgu.scale = (float *)dsgu;
+    wdn.codes = (int8_t *)dcd; wdn.scale = (float *)dsd;
+    int rc = convrot_swiglu_prepare_weights(dWgu, CONVROT_F32, NULL, F, K, b_up, &wgu, dwp, wp,
+                                            NULL);
+    if (rc == CONVROT_OK)
+        rc = convrot_linear_prepare_weights(dWd, CONVROT_F32, CONVROT_OUT_MAJOR, NULL, N, F,
+                                            b_down, &wdn, dwd, wd, NULL);
+    /* the interleaved fc1 weight is not a plain linear weight */
+    if (rc == CONVROT_OK &&
+        convrot_linear_forward(dX, M, &wgu, NULL, dY, CONVROT_F32, dws, wf, NULL) != CONVROT_ELAYOUT)
+        rc = -7;
+    if (rc == CONVROT_OK)
+        rc = convrot_swiglu_mlp_forward(dX, M, &wgu, (const float *)dbgu, &wdn, (const float *)dbd,
+                                        dY, CONVROT_F32, dws, wf, NULL);
+    if (rc != CONVROT_OK) {
+        fprintf(stderr, "swiglu F=%lld: %s\n", (long long)F,
+                rc < -6 ? "a plain forward accepted the fc1 weight" : convrot_status_string(rc));
+        return -3;
+    }
+    if (hipDeviceSynchronize() || hipMemcpy(Y, dY, 4 * M * N, hipMemcpyDeviceToHost)) return -2;
+    if (oracle_rotate_quantize_rows_rot(Wgu, 0, 2 * F, K, K, b_up, 0, qgu, sgu) != 0 ||
+        oracle_rotate_quantize_rows_rot(Wd, 0, N, F, F, b_down, 0, qd, sd) != 0 ||
+        oracle_swiglu_mlp_forward_rot(X, M, K, b_up, b_down, 0, qgu, sgu, F, bgu, qd, sd, N, bd,
+                                      0, Yref, NULL, NULL) != 0)
+        return -6;
+    int64_t bad = 0;
+    for (int64_t i = 0; i < M * N; ++i) bad += memcmp(&Y[i], &Yref[i], 4) != 0;
+    printf("c-abi swiglu M=%lld K=%lld F=%lld N=%lld b=%d/%d: %lld outputs differ from the "
+           "oracle\n", (long long)M, (long long)K, (long long)F, (long long)N, b_up, b_down,
+           (long long)bad);
+    hipFree(dWgu); hipFree(dWd); hipFree(dcgu); hipFree(dsgu); hipFree(dcd); hipFree(dsd);
+    hipFree(dbgu); hipFree(dbd); hipFree(dY); hipFree(dwp); hipFree(dwd); hipFree(dws);
+    free(Wgu); free(Wd); free(bgu); free(bd); free(Y); free(Yref); free(sgu); free(sd);
+    free(qgu); free(qd);
+    return bad;
+}
+
 int main(void)
 {
     const int64_t M = 300, K = 1024, N = 512;
@@ -209,6 +293,9 @@ int main(void)
     const int64_t lr1 = lowrank_case(X, dX, M, K, 192, 272, 64, &seed);
     const int64_t lr2 = lowrank_case(X, dX, M, K, 320, 272, 128, &seed);
     if (lr1 != 0 || lr2 != 0) return lr1 < 0 || lr2 < 0 ? 7 : 1;
+    /* the SwiGLU MLP: fc1 b = 128, fc2 ConvRot64 */
+    const int64_t sg = swiglu_case(X, dX, M, K, 256, 272, 128, 64, &seed);
+    if (sg != 0) return sg < 0 ? 8 : 1;
     hipFree(dX); hipFree(dW); hipFree(dcodes); hipFree(dscale); hipFree(dbias); hipFree(dY);
     hipFree(dwsp); hipFree(dwsf);
     free(X); free(W); free(bias); free(Y); free(Yref); free(sw); free(sw_ref); free(qw_ref);

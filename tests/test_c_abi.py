@@ -32,10 +32,11 @@ def test_c_program_builds(tmp_path):
 @pytest.mark.gpu
 def test_c_program_forward_matches_oracle(tmp_path):
     exe = _build(tmp_path / "c_abi_forward")
-    print("[case] C program: prepare + linear forward, padded low-rank pairs through the C ABI",
+    print("[case] C program: prepare + linear forward, padded low-rank pairs and the SwiGLU MLP "
+          "through the C ABI",
           flush=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     print(r.stdout.strip(), r.stderr.strip(), flush=True)
     assert r.returncode == 0, f"exit {r.returncode}: {r.stdout}{r.stderr}"
     assert "0 codes, 0 scales, 0 outputs differ" in r.stdout
-    assert r.stdout.count("0 outputs differ from the oracle") == 3
+    assert r.stdout.count("0 outputs differ from the oracle") == 4
