@@ -75,6 +75,10 @@ int main(void)
                 acc += lowrank_convrot_prepare_workspace_bytes(dims[i], dims[j], dims[j],
                                                                blocks[k], CONVROT_F32);
                 acc += (size_t)lowrank_convrot_padded_rank(dims[i], blocks[k]);
+                acc += convrot_swiglu_prepare_workspace_bytes(dims[i], dims[j], blocks[k],
+                                                              CONVROT_I8);
+                acc += convrot_swiglu_mlp_workspace_bytes(dims[i], dims[j], dims[j], 512,
+                                                          blocks[k], 64);
             }
     EXPECT(convrot_weights_packed_bytes(16, 65536 + 128, 128) == 0, 1);
     EXPECT(convrot_weights_packed_bytes(512, 5376, 128) == (size_t)512 * 5376, 1);
@@ -219,6 +223,71 @@ int main(void)
                                            FAKE, 1 << 20, NULL),
            CONVROT_EINVAL);
     EXPECT(pa.magic == 0 && pb.magic == 0, 1);
+    /* SwiGLU: preparation, forward, the fused flag and the hooks */
+    EXPECT(convrot_swiglu_prepare_workspace_bytes(256, 512, 128, CONVROT_F32) ==
+               (size_t)512 * 512 * 4, 1);
+    EXPECT(convrot_swiglu_prepare_workspace_bytes(256, 512, 128, CONVROT_I8) ==
+               (size_t)512 * 512 + 2048, 1);
+    EXPECT(convrot_swiglu_prepare_workspace_bytes(100, 512, 128, CONVROT_F32) == 0, 1);
+    EXPECT(convrot_swiglu_mlp_workspace_bytes(8, 512, 256, 272, 128, 100) == 0, 1);
+    EXPECT(convrot_swiglu_prepare_weights(FAKE, CONVROT_F32, NULL, 100, 512, 128, &pa, FAKE,
+                                          1 << 20, NULL),
+           CONVROT_EUNSUPPORTED);
+    EXPECT(convrot_swiglu_prepare_weights(FAKE, CONVROT_I8, NULL, 256, 512, 128, &pa, FAKE,
+                                          1 << 20, NULL),
+           CONVROT_EINVAL);
+    EXPECT(convrot_swiglu_prepare_weights(FAKE, CONVROT_F32, NULL, 256, 512, 128, &pa, NULL, 0,
+                                          NULL),
+           CONVROT_EWORKSPACE);
+    EXPECT(convrot_swiglu_prepare_weights(FAKE_ODD, CONVROT_F32, NULL, 256, 512, 128, &pa, FAKE,
+                                          1 << 20, NULL),
+           CONVROT_EALIGN);
+    EXPECT(pa.magic == 0, 1);
+    convrot_weights gu = desc(512, 512, 128), dn = desc(272, 256, 64), gu_bad = gu;
+    gu.flags = (int32_t)CONVROT_SWIGLU_PAIRS;
+    EXPECT(convrot_swiglu_mlp_forward(FAKE, 8, &gu_bad, NULL, &dn, NULL, FAKE, CONVROT_BF16, FAKE,
+                                      big_ws, NULL),
+           CONVROT_ELAYOUT);                                  /* fc1 not interleaved */
+    EXPECT(convrot_swiglu_mlp_forward(FAKE, 8, &gu, NULL, &gu, NULL, FAKE, CONVROT_BF16, FAKE,
+                                      big_ws, NULL),
+           CONVROT_ELAYOUT);                                  /* fc2 interleaved */
+    convrot_weights dn_wide = desc(272, 384, 64);
+    EXPECT(convrot_swiglu_mlp_forward(FAKE, 8, &gu, NULL, &dn_wide, NULL, FAKE, CONVROT_BF16,
+                                      FAKE, big_ws, NULL),
+           CONVROT_ELAYOUT);                                  /* 2F != fc1 outputs */
+    EXPECT(convrot_swiglu_mlp_forward(FAKE, INT64_MAX, &gu, NULL, &dn, NULL, FAKE, CONVROT_BF16,
+                                      FAKE, big_ws, NULL),
+           CONVROT_EUNSUPPORTED);
+    EXPECT(convrot_swiglu_mlp_forward(FAKE, 8, &gu, NULL, &dn, NULL, FAKE, CONVROT_BF16, FAKE, 64,
+                                      NULL),
+           CONVROT_EWORKSPACE);
+    EXPECT(convrot_swiglu_mlp_forward(FAKE, 0, &gu, NULL, &dn, NULL, FAKE, CONVROT_BF16, FAKE,
+                                      big_ws, NULL),
+           CONVROT_OK);
+    EXPECT(convrot_linear_forward(FAKE, 4, &gu, NULL, FAKE, CONVROT_BF16, FAKE, big_ws, NULL),
+           CONVROT_ELAYOUT);                                  /* interleaved in a plain forward */
+    EXPECT(convrot_gemm_dequant((const int8_t *)FAKE, (const float *)FAKE, 4, &d, NULL, FAKE,
+                                CONVROT_BF16, CONVROT_FLAG_SWIGLU, NULL),
+           CONVROT_ELAYOUT);                                  /* the flag on a plain weight */
+    EXPECT(convrot_gemm_dequant((const int8_t *)FAKE, (const float *)FAKE, 4, &gu, NULL, FAKE,
+                                CONVROT_F32, CONVROT_FLAG_SWIGLU, NULL),
+           CONVROT_EUNSUPPORTED);                             /* bf16 only */
+    EXPECT(convrot_swiglu_bf16((const uint16_t *)FAKE, -1, 16, (uint16_t *)FAKE, NULL),
+           CONVROT_EINVAL);
+    EXPECT(convrot_swiglu_bf16((const uint16_t *)FAKE, 4, 12, (uint16_t *)FAKE, NULL),
+           CONVROT_EUNSUPPORTED);
+    EXPECT(convrot_swiglu_bf16((const uint16_t *)FAKE_ODD, 4, 16, (uint16_t *)FAKE, NULL),
+           CONVROT_EALIGN);
+    EXPECT(convrot_swiglu_bf16(NULL, 0, 16, NULL, NULL), CONVROT_OK);
+    EXPECT(convrot_silu_f32((const uint16_t *)FAKE, -1, (float *)FAKE, NULL), CONVROT_EINVAL);
+    EXPECT(convrot_silu_f32(NULL, 0, NULL, NULL), CONVROT_OK);
+    /* the allocation-free forward: a workspace beyond its static array, bad M */
+    EXPECT(convrot_linear_forward_noalloc(FAKE, 1 << 20, &d, NULL, FAKE, CONVROT_BF16, NULL),
+           CONVROT_EWORKSPACE);
+    EXPECT(convrot_linear_forward_noalloc(FAKE, -1, &d, NULL, FAKE, CONVROT_BF16, NULL),
+           CONVROT_EINVAL);
+    EXPECT(convrot_linear_forward_noalloc(FAKE, 0, &d, NULL, FAKE, CONVROT_BF16, NULL), CONVROT_OK);
+
     int64_t ops = 0;
     EXPECT(convrot_probe_mfma_i8(0, FAKE, FAKE, &ops, NULL), CONVROT_EINVAL);
     EXPECT(convrot_probe_stream(FAKE, FAKE, 64, 3, NULL), CONVROT_EINVAL);
