@@ -992,6 +992,53 @@ def test_chain_random_sweep(cr, case):
     assert assert_output_parity(yh, y_ref, c["out"], f"{c['kind']} sweep") == 0
 
 
+def _swiglu_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rot = "regular" if rng.random() < 0.3 else "sylvester"
+        blocks = [64, 256] if rot == "regular" else [64, 128, 256]
+        bu, bd = int(rng.choice(blocks)), int(rng.choice(blocks))
+        # hidden widths up to 49 x 128: rows of g long enough for the pair
+        # rotquant kernel as well as the short-row kernels
+        f = int(rng.choice([1, 2, 3, 5, 8, 25, 49]))
+        cases.append(dict(M=int(rng.integers(1, 700)), K=int(rng.integers(1, 25)) * max(bu, 128),
+                          F=f * max(bd, 128), N=int(rng.integers(1, 65)) * 16, bu=bu, bd=bd,
+                          rot=rot, out=str(rng.choice(["bf16", "f32"])),
+                          bias=bool(rng.random() < 0.5), seed=3000 + 17 * i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _swiglu_cases(8, 79),
+                         ids=lambda c: "M{M}_K{K}_F{F}_N{N}_b{bu}-{bd}_{rot}_{out}".format(**c))
+def test_swiglu_random_sweep(cr, case):
+    """Seeded random SwiGLU MLPs: fc1 and fc2 blocks drawn independently,
+    both rotation kinds, both outputs, biases on both projections or none,
+    against the oracle's chain, every output bit-exact."""
+    c = case
+    announce(f"swiglu sweep {c}")
+    rng = np.random.default_rng(c["seed"])
+    M, K, F, N = c["M"], c["K"], c["F"], c["N"]
+    x = wl.f32_to_bf16_bits(rng.standard_t(4, (M, K)).astype(np.float32))
+    Wgu = rng.normal(0, 0.02, (2 * F, K)).astype(np.float32)
+    Wd = rng.normal(0, 0.02, (N, F)).astype(np.float32)
+    bgu = rng.normal(0, 0.05, 2 * F).astype(np.float32) if c["bias"] else None
+    bdn = rng.normal(0, 0.05, N).astype(np.float32) if c["bias"] else None
+    pgu = cr.convrot_swiglu_prepare(to_dev(Wgu), c["bu"], rotation=c["rot"])
+    pd = cr.convrot_linear_prepare_weights(to_dev(Wd), c["bd"], rotation=c["rot"])
+    qgu, sgu = oracle.prepare_weights(Wgu, c["bu"], rot=c["rot"])
+    qd, sd = oracle.prepare_weights(Wd, c["bd"], rot=c["rot"])
+    od = torch.bfloat16 if c["out"] == "bf16" else torch.float32
+    y = cr.convrot_swiglu_mlp_forward(to_dev_bf16(x), pgu, pd,
+                                      bias_gu=None if bgu is None else to_dev(bgu),
+                                      bias_down=None if bdn is None else to_dev(bdn),
+                                      out_dtype=od)
+    y_ref = oracle.swiglu_mlp_forward(x, qgu, sgu, qd, sd, c["bu"], c["bd"], bias_gu=bgu,
+                                      bias_down=bdn, out=c["out"], rot=c["rot"])
+    yh = bf16_bits(y) if c["out"] == "bf16" else host(y)
+    assert assert_output_parity(yh, y_ref, c["out"], "swiglu sweep") == 0
+
+
 def test_nonfinite_rows_stay_local(cr):
     """Non-finite inputs give unspecified values but stay in their own rows:
     rows holding NaN or inf change nothing else, through the linear forward
