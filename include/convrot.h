@@ -36,17 +36,23 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates nothing and keeps no per-call state.  It is re-entrant: calls
- *     on different streams may overlap if they use separate workspaces.  Its
- *     one piece of device state is a read-only 65,536-entry bf16 GELU table
- *     (one copy per device, in the library's code object), written once per
- *     device by the first call of a GELU path (convrot_mlp_forward,
- *     CONVROT_FLAG_GELU, convrot_gelu_bf16).
+ *     on different streams may overlap if they use separate workspaces (the
+ *     allocation-free forward below shares one scratch array per device and
+ *     is the exception).  Its device state is fixed in size, one copy per
+ *     device in the library's code object: two read-only tables, each written
+ *     once per device by the first call of a path that reads it -- the
+ *     65,536-entry bf16 GELU table (convrot_mlp_forward, CONVROT_FLAG_GELU,
+ *     convrot_gelu_bf16) and the 65,536-entry fp32 silu table (the SwiGLU
+ *     paths: convrot_swiglu_mlp_forward, CONVROT_FLAG_SWIGLU,
+ *     convrot_swiglu_bf16, convrot_silu_f32) -- and the scratch array of
+ *     convrot_linear_forward_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls are asynchronous on that stream.  The host waits only once per
- *     device: the first GELU-path call that is not being recorded into a graph
- *     waits for its table fill, so that launches on any stream may read the
- *     table from then on.  A GELU-path call recorded into a graph before that
- *     records the fill too (each replay rewrites the same values).
+ *     device and table: the first call of a GELU or SwiGLU path that is not
+ *     being recorded into a graph waits for its table fill, so that launches
+ *     on any stream may read the table from then on.  Such a call recorded
+ *     into a graph before that records the fill too (each replay rewrites the
+ *     same values).
  *   - Float matrices (X, Y, weights, intermediates in bf16) are row-major and
  *     dense; bf16 tensors hold raw bfloat16 bits.  INT8 code matrices (the
  *     test hooks' q_x and q_h, prepared weight codes) use the K-tiled layout
