@@ -467,14 +467,17 @@ def _cus():
 
 
 @pytest.mark.parametrize("K", [256, 768])
-@pytest.mark.parametrize("shape", ["one_round", "split_tail", "three_rounds"])
+@pytest.mark.parametrize("shape", ["one_round", "split_tail", "split_tail_64", "three_rounds"])
 def test_lowrank_factor1_tile_plans(cr, shape, K):
-    """128-token tiles only (the last round fills more than half the CUs),
-    whole rounds of 128-token tiles followed by a launch of 64-token tiles,
-    and three rounds (every workgroup walks three tiles, so the copies of a
-    tile's first K-tiles are issued during the one before) plus the tail."""
+    """128-token tiles only (the last round fills more than half the CUs);
+    whole rounds of 128-token tiles followed by a launch of 32-token tiles
+    (the last round would fill at most a quarter of the CUs; its last tile
+    ragged) or of 64-token tiles (between a quarter and a half); and three
+    rounds (every workgroup walks three tiles, so the copies of a tile's
+    first K-tiles are issued during the one before) plus the tail."""
     cus = _cus()
     M = {"one_round": cus * 64 + 100, "split_tail": cus * 128 + 300,
+         "split_tail_64": cus * 128 + cus * 40 + 5,
          "three_rounds": 3 * cus * 128 + 300}[shape]
     _check_factor1(cr, M, K, 512, 128)
 
