@@ -180,11 +180,12 @@ def test_prepare_import_int8_unchanged(cr, layout):
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (300, 272, 384), (1, 16, 512),
                                    (513, 528, 1024), (64, 784, 5376), (257, 1040, 256),
                                    (2048, 8192, 256), (2000, 8000, 384), (4100, 5376, 1024),
-                                   (17, 48, 65536)])
+                                   (1200, 16128, 1024), (17, 48, 65536)])
 def test_gemm_i32_bitexact(cr, M, N, K):
     """One tile to a full round of 256 tiles, ragged tails in M, N and K,
     (M = 4100) whole rounds of 256 x 256 tiles followed by a 256 x 128 tail,
-    and (K = 65536) the largest K with the extreme accumulator -127^2 K."""
+    (M = 1200, N = 16128) one round followed by a ragged 256 x 64 tail, and
+    (K = 65536) the largest K with the extreme accumulator -127^2 K."""
     announce(f"gemm_i32 M={M} N={N} K={K}")
     rng = np.random.default_rng(M * 7 + N)
     qx = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
@@ -311,6 +312,27 @@ def test_linear_many_tiles_per_workgroup(cr, M, K, N, with_bias):
         yc = cr.convrot_linear_forward(X[a:e].contiguous(), pw,
                                        bias=None if bias is None else to_dev(bias))
         assert np.array_equal(bf16_bits(yc), yb[a:e]), f"rows {a}:{e}"
+
+
+@pytest.mark.parametrize("out,with_bias", [("bf16", True), ("f32", False)])
+def test_linear_quarter_tail(cr, out, with_bias):
+    """The last tile-row as 256 x 64 tiles: at M = 1200, N = 16128 (315 tiles
+    of 256 x 256 for 256 CUs) the plan runs 252 tiles in one round and the
+    last 176 rows as 189 tiles of 64 rows, the last of them ragged.  Every
+    output against the oracle."""
+    announce(f"quarter tail M=1200 K=1024 N=16128 out={out} bias={with_bias}")
+    M, K, N = 1200, 1024, 16128
+    w = wl.Workload("qt", "linear", M=M, K=K, N=N, block=128, out=out, x_dist="student_t4",
+                    outlier_frac=0.01, outlier_gain=20, bias_std=0.05 if with_bias else None,
+                    seed=1200 + (out == "f32"))
+    x, W, bias = w.activations(), w.weight(), w.bias()
+    pw, qw, sw = _prepare_pair(cr, W, 128)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = cr.convrot_linear_forward(to_dev_bf16(x), pw,
+                                  bias=None if bias is None else to_dev(bias), out_dtype=od)
+    y_ref = oracle.linear_forward(x, qw, sw, 128, bias=bias, out=out)
+    yh = host(y) if out == "f32" else bf16_bits(y)
+    assert assert_output_parity(yh, y_ref, out, "quarter tail") == 0
 
 
 def test_row_chunk_invariance(cr):

@@ -1298,11 +1298,15 @@ hipError_t launch_f1_blk(const int8_t *qx, const int8_t *qa, const float *sx, co
 // leave CUs idle, the last tile-rows can go to a second launch of 256 (n) x
 // 128 (m) tiles (TJ = 2), which take about 0.6 of a 256 x 256 tile each (they
 // move more bytes per MFMA, so a whole launch of them runs at 0.8 of the
-// rate).  The split is chosen from that estimate when K >= 1024; it pays
-// when tiles are few (M = 4096: 336 tiles for 256 CUs, 10% faster).  With
-// short K (the low-rank factor 2, K = 512) the launch is bound by its output
-// stores and the split measured slower.
+// rate), or, for the plain outputs, of 256 x 64 tiles (TJ = 1, about 0.35).
+// The split is chosen from these estimates when K >= 1024; it pays when
+// tiles are few (M = 4096: 336 tiles for 256 CUs, 10% faster), and at
+// M = 38656, N = 16128 the last tile-row as one round of 256 x 64 tiles
+// takes about 7 us less than as 256 x 128 ones.  With short K (the low-rank
+// factor 2, K = 512) the launch is bound by its output stores and the split
+// measured slower.
 constexpr double kHalfTileCost = 0.625;   // TJ = 2 tile time / TJ = 4 tile time
+constexpr double kQuarterTileCost = 0.35; // TJ = 1 tile time / TJ = 4 tile time
 constexpr double kLaunchCost = 0.05;      // a second launch, in tile times
 
 template <int OUT, bool HAS_BIAS>
@@ -1323,13 +1327,22 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
     const int cus = device_cu_count();
     const int64_t tm = (M + kTile - 1) / kTile, tn = (N + kTile - 1) / kTile;
     auto rounds = [&](int64_t tiles) { return (double)((tiles + cus - 1) / cus); };
+    // quarter tiles (256 (n) x 64 (m), TJ = 1) for the plain outputs
+    constexpr bool QUARTER = OUT == int(OutKind::BF16) || OUT == int(OutKind::F32) ||
+                             OUT == int(OutKind::I32);
     int64_t best_a = tm;
+    bool best_q = false;
     double best = rounds(tm * tn);
     for (int64_t a = tm - 1; K >= 1024 && a >= 0 && a >= tm - 16; --a) {
-        const double t = rounds(a * tn) + kHalfTileCost * rounds(2 * (tm - a) * tn) + kLaunchCost;
+        const double th = rounds(a * tn) + kHalfTileCost * rounds(2 * (tm - a) * tn) + kLaunchCost;
+        const double tq = QUARTER ? rounds(a * tn) + kQuarterTileCost * rounds(4 * (tm - a) * tn) +
+                                        kLaunchCost
+                                  : 1e30;
+        const double t = std::min(th, tq);
         if (t < best - 0.1) {
             best = t;
             best_a = a;
+            best_q = tq < th;
         }
     }
     const int64_t m1 = std::min<int64_t>(M, best_a * kTile);
@@ -1341,6 +1354,12 @@ hipError_t launch_t(const int8_t *qx, const int8_t *qw, const float *sx, const f
     constexpr size_t ysize = OUT == int(OutKind::F32) || OUT == int(OutKind::I32) ? 4 : 2;
     // row stride of Y in elements (SwiGLU writes N/2 columns)
     const int64_t ycols = OUT == int(OutKind::SWIGLU_BF16) ? N / 2 : N;
+    if constexpr (QUARTER) {
+        if (best_q)
+            return launch_tj<OUT, HAS_BIAS, 1>(qx + m1 * K, qw, sx ? sx + m1 : nullptr, sw, bias,
+                                               static_cast<char *>(Y) + (size_t)(m1 * ycols) * ysize,
+                                               M - m1, N, K, cus, stream, silu_tab);
+    }
     return launch_tj<OUT, HAS_BIAS, 2>(qx + m1 * K, qw, sx ? sx + m1 : nullptr, sw, bias,
                                        static_cast<char *>(Y) + (size_t)(m1 * ycols) * ysize,
                                        M - m1, N, K, cus, stream, silu_tab);
